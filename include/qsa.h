@@ -1,0 +1,199 @@
+/*
+ * qsa.h -- C ABI of the paged block-scoring indexer (QSA-style sparse
+ * attention indexer) for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes.  Each query row r (one token of a prefill chunk
+ * or of a decode step) belongs to a request and sits at absolute position
+ * pos[r].  The request owns a paged side cache of compressed index keys: one
+ * fp16 key of head_dim values per block of compress_ratio (cr) tokens, shared
+ * by all index heads (MQA with a single key head).  Key j covers tokens
+ * cr*j .. cr*j+cr-1 and becomes visible to row r once its last token exists,
+ * i.e. for j < V_r = (pos[r]+1) / cr.  Every visible key is scored against the
+ * row's index-head queries; the per-head dot products (fp16 inputs, fp32
+ * accumulation) are summed over heads into one fp32 score per (row, key).
+ * The row keeps its exact top k/cr blocks under the lexicographic rule
+ * "higher score first, lower index on ties", and each block expands to its cr
+ * raw token positions; unused output slots hold -1.
+ *
+ * Sources (cited by page title and section):
+ *  [thor]   "qwen4_exp QSA cooperative_topk cannot launch on NVIDIA Thor
+ *           (sm_110): cluster misconfiguration", section "What happens" (the
+ *           indexer's forward calls qsa_select_paged_tokens, which runs a
+ *           top-k op over (logits, visible_blocks, blocks, workspace,
+ *           block_topk, columns); a failed launch surfaces as an error that
+ *           names the source location and the launch error).
+ *  [turing] "[Perf][Qwen4Exp] Admit the cuBLAS QSA indexer and exact top-k on
+ *           Turing", sections "Purpose" (FP16 scorer with FP32 accumulation;
+ *           exact lexicographic top-k with a deterministic tie rule), "Test
+ *           Plan" (4 index heads, head dim 128, compress ratio 4, top-k 2,048
+ *           tokens), "Path coverage" (block top-k 512, int32 indices).
+ *  [spec]   "spec(MODEL-MM-QWEN4-EXP): Qwen3.8-Flash-Next is a new
+ *           architecture vLLM does not implement, so the port splits its
+ *           oracle", section "The component deep-dives, and two corrections to
+ *           the above" (one key head of dim 128 shared by the index heads,
+ *           relu(q.k) summed over heads and scaled by 1/sqrt(head_dim), no
+ *           head axis in the result, the (position+1) % ratio boundary, one
+ *           stored state per ratio tokens, raw tokens selected at ratio
+ *           granularity, every candidate selected below the budget).
+ *
+ * Conventions for every entry point.
+ *  - Pointers named as device data must point to device memory (HIP
+ *    allocations) of the current device; host scalars are passed by value.
+ *  - All work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *    void*; NULL means the default stream).  Nothing is synchronised.
+ *  - The caller owns every buffer.  The library never allocates, frees or
+ *    retains a pointer after returning; buffers must stay alive until the
+ *    enqueued work completes.  Scratch memory is a caller-provided workspace
+ *    sized by the matching *_workspace_size query ([thor]: the top-k op takes
+ *    a caller workspace).
+ *  - Argument errors are detected on the host before anything is enqueued
+ *    and return a non-zero qsa_status; qsa_last_error() then describes the
+ *    failure as "file:line: message".  Launch failures return QSA_ERR_DEVICE
+ *    with the HIP error text.  Faults of already-enqueued work surface at the
+ *    caller's next synchronisation.
+ *  - Supported geometry: heads == 4 and head_dim == 128 ([turing] "Test
+ *    Plan"); anything else returns QSA_ERR_UNSUPPORTED.  page_size must be a
+ *    positive multiple of compress_ratio.
+ *  - Device-side data outside its contract (a page-table entry outside
+ *    [0, num_pages), a row_req entry outside [0, num_reqs), a row with
+ *    V_r > max_visible) never causes an out-of-bounds access: page ids are
+ *    clamped into range, rows with an invalid request select nothing, and V_r
+ *    is clamped to max_visible.  The results for such rows are unspecified.
+ *  - Inputs must be finite; NaN scores are outside the contract.
+ *  - Calls are thread-safe.  Library state is a per-device properties cache
+ *    and a thread-local error string.
+ *  - Indices are logical positions within the request (key j, token t); the
+ *    mapping to physical cache slots is the consumer's.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qsa_status {
+    QSA_OK = 0,
+    QSA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad stride, k not a multiple of cr, unknown flag */
+    QSA_ERR_UNSUPPORTED = 2,        /* heads != 4, head_dim != 128, k beyond the selector's limit, device not gfx950 */
+    QSA_ERR_WORKSPACE_TOO_SMALL = 3,
+    QSA_ERR_DEVICE = 4              /* a HIP call or kernel launch failed */
+} qsa_status;
+
+/* flags */
+#define QSA_SCORE_RELU 0x1u  /* [spec] form: sum_h relu(q_h . k) times the fp32 value nearest 1/sqrt(head_dim);
+                                default is the plain sum_h q_h . k */
+#define QSA_OUT_KEYS   0x2u  /* k counts keys and the output holds key indices (no expansion to tokens) */
+
+/* Largest number of selected entries per row (blocks, or keys with
+ * QSA_OUT_KEYS) that the selector supports. */
+#define QSA_MAX_SELECT 4096
+
+/*
+ * qsa_score_paged -- the scorer alone ([turing] "Purpose": FP16 inputs, FP32
+ * accumulation; [spec]: one score per (row, key), summed over index heads).
+ *
+ *  q            device fp16 [rows][heads][head_dim], row-major, contiguous.
+ *  kcache       device fp16 [num_pages][page_size/compress_ratio][head_dim]:
+ *               page p holds keys slot 0.. page_size/cr-1 contiguously.
+ *  page_table   device int32 [num_reqs][pt_stride]: logical page i of
+ *               request q is physical page page_table[q*pt_stride + i]; key j
+ *               of request q is slot j % (page_size/cr) of logical page
+ *               j / (page_size/cr).  Entries for logical pages at or beyond
+ *               ceil(V/(page_size/cr)) of a request's longest row are never read.
+ *  pt_stride    row stride of page_table in entries; must be >=
+ *               ceil(max_visible / (page_size/cr)).
+ *  num_pages    number of physical pages in kcache (>= 1).
+ *  num_reqs     number of page-table rows (>= 1).
+ *  row_req      device int32 [rows]: request of each row; NULL means every
+ *               row belongs to request 0.
+ *  pos          device int32 [rows]: absolute token position of each row.
+ *               V_r = (pos[r]+1)/compress_ratio keys are visible (0 if pos<0).
+ *  rows         number of query rows (0 is a no-op).
+ *  max_visible  host upper bound on every V_r (the top-k op's `columns` in
+ *               [thor]); sizes the launch.
+ *  flags        0 or QSA_SCORE_RELU.
+ *  scores       device fp32 [rows][ld_scores]: entry (r, j) is written for
+ *               j < V_r only; every other entry is left untouched.
+ *  ld_scores    row stride of scores in floats, >= max_visible.
+ */
+qsa_status qsa_score_paged(const void* q, const void* kcache, const int32_t* page_table,
+                           int64_t pt_stride, int32_t num_pages, int32_t num_reqs,
+                           const int32_t* row_req, const int32_t* pos, int32_t rows,
+                           int32_t heads, int32_t head_dim, int32_t page_size,
+                           int32_t compress_ratio, int32_t max_visible, uint32_t flags,
+                           float* scores, int64_t ld_scores, void* stream);
+
+/*
+ * qsa_topk_rows -- the exact selector alone ([thor] "What happens": the top-k
+ * op over the score matrix, the per-row visible count, k and the column
+ * count; [turing] "Purpose": exact, lexicographic, deterministic on ties).
+ *
+ *  scores       device fp32 [rows][ld_scores]; only entries j < visible[r]
+ *               are read.  -0 and +0 are equal (a tie broken by index).
+ *  visible      device int32 [rows] or NULL (then every row has max_visible
+ *               candidates); values are clamped to [0, max_visible].
+ *  rows         number of rows (0 is a no-op).
+ *  max_visible  host upper bound on visible[r]; ld_scores >= max_visible.
+ *  k            entries to select per row, 1 <= k <= QSA_MAX_SELECT.
+ *  out          device int32 [rows][k]: out[r][i] is the key index of rank i
+ *               (higher score first, lower index on ties), -1 for
+ *               i >= min(k, visible[r]).
+ *  workspace    device scratch of at least qsa_topk_rows_workspace_size(...)
+ *               bytes (may be NULL when that size is 0); its contents on entry
+ *               and exit are unspecified.
+ */
+qsa_status qsa_topk_rows(const float* scores, int64_t ld_scores, const int32_t* visible,
+                         int32_t rows, int32_t max_visible, int32_t k, int32_t* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+size_t qsa_topk_rows_workspace_size(int32_t rows, int32_t max_visible, int32_t k);
+
+/*
+ * qsa_select_paged_tokens -- the whole indexer ([thor] "What happens": the
+ * indexer forward's entry point; [turing] "Test Plan": 4 heads, head dim 128,
+ * compress ratio 4, top-k 2,048 tokens; [spec]: raw tokens at ratio
+ * granularity, every candidate selected below the budget).
+ *
+ *  q .. max_visible   as for qsa_score_paged.
+ *  k            output entries per row.  Default: tokens; k must be a
+ *               multiple of compress_ratio and k/cr blocks are selected
+ *               (1 <= k/cr <= QSA_MAX_SELECT).  With QSA_OUT_KEYS: keys,
+ *               1 <= k <= QSA_MAX_SELECT.
+ *  flags        QSA_SCORE_RELU and/or QSA_OUT_KEYS.
+ *  out          device int32 [rows][k]: rank-ordered blocks, each expanded to
+ *               tokens cr*j .. cr*j+cr-1 ascending (or key j with
+ *               QSA_OUT_KEYS); -1 after the min(k/cr, V_r) selected blocks.
+ *  workspace    device scratch of at least
+ *               qsa_select_paged_tokens_workspace_size(...) bytes.
+ */
+qsa_status qsa_select_paged_tokens(const void* q, const void* kcache, const int32_t* page_table,
+                                   int64_t pt_stride, int32_t num_pages, int32_t num_reqs,
+                                   const int32_t* row_req, const int32_t* pos, int32_t rows,
+                                   int32_t heads, int32_t head_dim, int32_t page_size,
+                                   int32_t compress_ratio, int32_t max_visible, int32_t k,
+                                   uint32_t flags, int32_t* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+size_t qsa_select_paged_tokens_workspace_size(int32_t rows, int32_t num_reqs, int32_t max_visible,
+                                              int32_t compress_ratio, int32_t k, uint32_t flags);
+
+/* Description of the last failure on the calling thread, "file:line: message"
+ * ("" if none).  The pointer stays valid until the thread's next library call. */
+const char* qsa_last_error(void);
+
+/* Name of the execution arm the calling thread's last successful
+ * qsa_select_paged_tokens call used (e.g. "two_pass"); "" before any call. */
+const char* qsa_last_path(void);
+
+/* Library version string. */
+const char* qsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

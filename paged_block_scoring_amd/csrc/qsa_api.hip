@@ -1,0 +1,272 @@
+// qsa_api.hip -- the C ABI declared in include/qsa.h: argument validation,
+// device check, workspace carving and kernel launches.
+//
+// Error behaviour follows "qwen4_exp QSA cooperative_topk cannot launch on
+// NVIDIA Thor (sm_110): cluster misconfiguration", section "What happens": a
+// failure is reported with the source location and the launch error text.
+// Here every argument is checked on the host before anything is enqueued, and
+// the device is identified by its real architecture name and limits rather
+// than a capability proxy (the same page, section "What the source says").
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/qsa.h"
+#include "qsa_internal.hpp"
+
+#define QSA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[1024] = "";
+thread_local const char* g_path = "";
+
+qsa_status fail_at(const char* file, int line, qsa_status code, const char* fmt, ...) {
+    const char* base = strrchr(file, '/');
+    base = base ? base + 1 : file;
+    int n = snprintf(g_err, sizeof g_err, "%s:%d: ", base, line);
+    if (n < 0 || n >= (int)sizeof g_err) n = 0;
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err + n, sizeof g_err - (size_t)n, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+#define FAIL(code, ...) return fail_at(__FILE__, __LINE__, (code), __VA_ARGS__)
+#define REQUIRE(cond, code, ...) \
+    do {                         \
+        if (!(cond)) FAIL((code), __VA_ARGS__); \
+    } while (0)
+#define HIP_CHECK(expr)                                                                         \
+    do {                                                                                        \
+        hipError_t e_ = (expr);                                                                 \
+        if (e_ != hipSuccess) FAIL(QSA_ERR_DEVICE, "%s failed: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+    bool probed = false;
+    bool supported = false;
+    int cus = 0;
+    size_t lds = 0;
+    char arch[64] = "";
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+// Identify the current device once: the kernels are written for gfx950
+// (CDNA4) and its 64-wide wavefronts, 16x16x32 f16 MFMA and 160 KB LDS.
+qsa_status check_device(const DeviceInfo** out) {
+    int dev = -1;
+    HIP_CHECK(hipGetDevice(&dev));
+    REQUIRE(dev >= 0 && dev < kMaxDevices, QSA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    DeviceInfo& d = g_dev[dev];
+    if (!d.probed) {
+        hipDeviceProp_t p;
+        HIP_CHECK(hipGetDeviceProperties(&p, dev));
+        snprintf(d.arch, sizeof d.arch, "%s", p.gcnArchName);
+        d.cus = p.multiProcessorCount;
+        d.lds = p.sharedMemPerBlock;
+        d.supported = strncmp(d.arch, "gfx950", 6) == 0 && p.warpSize == 64 && d.lds >= 64 * 1024;
+        d.probed = true;
+    }
+    REQUIRE(d.supported, QSA_ERR_UNSUPPORTED,
+            "device %d is %s; this library is built for gfx950 (MI355X)", dev, d.arch);
+    *out = &d;
+    return QSA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Common checks of the paged inputs (everything qsa_score_paged and
+// qsa_select_paged_tokens share).
+qsa_status check_paged(const void* q, const void* kcache, const int32_t* page_table, int64_t pt_stride,
+                       int32_t num_pages, int32_t num_reqs, const int32_t* pos, int32_t rows,
+                       int32_t heads, int32_t head_dim, int32_t page_size, int32_t compress_ratio,
+                       int32_t max_visible) {
+    REQUIRE(rows >= 0, QSA_ERR_INVALID_ARGUMENT, "rows must be >= 0 (got %d)", rows);
+    REQUIRE(heads == 4, QSA_ERR_UNSUPPORTED, "heads must be 4 (got %d)", heads);
+    REQUIRE(head_dim == 128, QSA_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+    REQUIRE(compress_ratio >= 1, QSA_ERR_INVALID_ARGUMENT, "compress_ratio must be >= 1 (got %d)",
+            compress_ratio);
+    REQUIRE(page_size >= 1 && page_size % compress_ratio == 0, QSA_ERR_INVALID_ARGUMENT,
+            "page_size (%d) must be a positive multiple of compress_ratio (%d)", page_size, compress_ratio);
+    REQUIRE(max_visible >= 0, QSA_ERR_INVALID_ARGUMENT, "max_visible must be >= 0 (got %d)", max_visible);
+    REQUIRE(num_pages >= 1, QSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1 (got %d)", num_pages);
+    REQUIRE(num_reqs >= 1, QSA_ERR_INVALID_ARGUMENT, "num_reqs must be >= 1 (got %d)", num_reqs);
+    const int64_t kpp = page_size / compress_ratio;
+    REQUIRE(pt_stride >= ceil_div(max_visible, kpp) && pt_stride >= 1, QSA_ERR_INVALID_ARGUMENT,
+            "pt_stride (%lld) must be >= ceil(max_visible / keys_per_page) = %lld", (long long)pt_stride,
+            (long long)ceil_div(max_visible, kpp));
+    if (rows == 0) return QSA_OK;
+    REQUIRE(q && kcache && page_table && pos, QSA_ERR_INVALID_ARGUMENT,
+            "null pointer: q=%p kcache=%p page_table=%p pos=%p", q, kcache, (const void*)page_table,
+            (const void*)pos);
+    REQUIRE(aligned16(q) && aligned16(kcache), QSA_ERR_INVALID_ARGUMENT,
+            "q and kcache must be 16-byte aligned");
+    return QSA_OK;
+}
+
+qsa::PagedArgs make_paged(const void* q, const void* kcache, const int32_t* page_table, int64_t pt_stride,
+                          int32_t num_pages, int32_t num_reqs, const int32_t* row_req, const int32_t* pos,
+                          int32_t rows, int32_t page_size, int32_t compress_ratio, int32_t max_visible,
+                          uint32_t flags) {
+    qsa::PagedArgs a;
+    a.q = static_cast<const _Float16*>(q);
+    a.kcache = static_cast<const _Float16*>(kcache);
+    a.page_table = page_table;
+    a.pt_stride = pt_stride;
+    a.num_pages = num_pages;
+    a.num_reqs = num_reqs;
+    a.row_req = row_req;
+    a.pos = pos;
+    a.rows = rows;
+    a.kpp = page_size / compress_ratio;
+    a.cr = compress_ratio;
+    a.max_visible = max_visible;
+    a.relu = (flags & QSA_SCORE_RELU) != 0;
+    return a;
+}
+
+// Two-pass arm: fp32 scores [rows][ld] in the workspace, then the selector.
+int64_t two_pass_ld(int32_t max_visible) { return ceil_div(max_visible > 0 ? max_visible : 1, 64) * 64; }
+
+size_t two_pass_bytes(int32_t rows, int32_t max_visible) {
+    return (size_t)rows * (size_t)two_pass_ld(max_visible) * sizeof(float);
+}
+
+}  // namespace
+
+QSA_EXPORT const char* qsa_last_error(void) { return g_err; }
+QSA_EXPORT const char* qsa_last_path(void) { return g_path; }
+QSA_EXPORT const char* qsa_version(void) { return "qsa-mi355x 0.1.0 (gfx950)"; }
+
+QSA_EXPORT qsa_status qsa_score_paged(const void* q, const void* kcache, const int32_t* page_table,
+                                      int64_t pt_stride, int32_t num_pages, int32_t num_reqs,
+                                      const int32_t* row_req, const int32_t* pos, int32_t rows, int32_t heads,
+                                      int32_t head_dim, int32_t page_size, int32_t compress_ratio,
+                                      int32_t max_visible, uint32_t flags, float* scores, int64_t ld_scores,
+                                      void* stream) {
+    g_err[0] = 0;
+    qsa_status st = check_paged(q, kcache, page_table, pt_stride, num_pages, num_reqs, pos, rows, heads,
+                                head_dim, page_size, compress_ratio, max_visible);
+    if (st != QSA_OK) return st;
+    REQUIRE((flags & ~QSA_SCORE_RELU) == 0, QSA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x for the scorer",
+            flags);
+    REQUIRE(ld_scores >= max_visible && ld_scores >= 1, QSA_ERR_INVALID_ARGUMENT,
+            "ld_scores (%lld) must be >= max_visible (%d)", (long long)ld_scores, max_visible);
+    if (rows == 0 || max_visible == 0) return QSA_OK;
+    REQUIRE(scores != nullptr, QSA_ERR_INVALID_ARGUMENT, "null pointer: scores");
+    const DeviceInfo* dev = nullptr;
+    if ((st = check_device(&dev)) != QSA_OK) return st;
+    qsa::PagedArgs a = make_paged(q, kcache, page_table, pt_stride, num_pages, num_reqs, row_req, pos, rows,
+                                  page_size, compress_ratio, max_visible, flags);
+    HIP_CHECK(qsa::launch_score_paged(a, scores, ld_scores, static_cast<hipStream_t>(stream)));
+    return QSA_OK;
+}
+
+QSA_EXPORT size_t qsa_topk_rows_workspace_size(int32_t rows, int32_t max_visible, int32_t k) {
+    (void)rows;
+    (void)max_visible;
+    (void)k;
+    return 0;
+}
+
+QSA_EXPORT qsa_status qsa_topk_rows(const float* scores, int64_t ld_scores, const int32_t* visible, int32_t rows,
+                                    int32_t max_visible, int32_t k, int32_t* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    REQUIRE(rows >= 0, QSA_ERR_INVALID_ARGUMENT, "rows must be >= 0 (got %d)", rows);
+    REQUIRE(max_visible >= 0, QSA_ERR_INVALID_ARGUMENT, "max_visible must be >= 0 (got %d)", max_visible);
+    REQUIRE(k >= 1, QSA_ERR_INVALID_ARGUMENT, "k must be >= 1 (got %d)", k);
+    REQUIRE(k <= QSA_MAX_SELECT, QSA_ERR_UNSUPPORTED, "k (%d) exceeds the selector limit %d", k,
+            QSA_MAX_SELECT);
+    REQUIRE(ld_scores >= max_visible && ld_scores >= 1, QSA_ERR_INVALID_ARGUMENT,
+            "ld_scores (%lld) must be >= max_visible (%d)", (long long)ld_scores, max_visible);
+    const size_t need = qsa_topk_rows_workspace_size(rows, max_visible, k);
+    REQUIRE(workspace_bytes >= need, QSA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < required %zu",
+            workspace_bytes, need);
+    (void)workspace;
+    if (rows == 0) return QSA_OK;
+    REQUIRE(out != nullptr, QSA_ERR_INVALID_ARGUMENT, "null pointer: out");
+    REQUIRE(scores != nullptr || max_visible == 0, QSA_ERR_INVALID_ARGUMENT, "null pointer: scores");
+    const DeviceInfo* dev = nullptr;
+    qsa_status st = check_device(&dev);
+    if (st != QSA_OK) return st;
+    qsa::VisibleSource vs;
+    vs.visible = visible;
+    vs.pos = nullptr;
+    vs.row_req = nullptr;
+    vs.num_reqs = 1;
+    vs.cr = 1;
+    vs.max_visible = max_visible;
+    HIP_CHECK(qsa::launch_topk_rows(scores, ld_scores, vs, rows, k, 1, k, out,
+                                    static_cast<hipStream_t>(stream)));
+    return QSA_OK;
+}
+
+QSA_EXPORT size_t qsa_select_paged_tokens_workspace_size(int32_t rows, int32_t num_reqs, int32_t max_visible,
+                                                         int32_t compress_ratio, int32_t k, uint32_t flags) {
+    (void)num_reqs;
+    (void)compress_ratio;
+    (void)k;
+    (void)flags;
+    if (rows <= 0 || max_visible <= 0) return 0;
+    return two_pass_bytes(rows, max_visible);
+}
+
+QSA_EXPORT qsa_status qsa_select_paged_tokens(const void* q, const void* kcache, const int32_t* page_table,
+                                              int64_t pt_stride, int32_t num_pages, int32_t num_reqs,
+                                              const int32_t* row_req, const int32_t* pos, int32_t rows,
+                                              int32_t heads, int32_t head_dim, int32_t page_size,
+                                              int32_t compress_ratio, int32_t max_visible, int32_t k,
+                                              uint32_t flags, int32_t* out, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    qsa_status st = check_paged(q, kcache, page_table, pt_stride, num_pages, num_reqs, pos, rows, heads,
+                                head_dim, page_size, compress_ratio, max_visible);
+    if (st != QSA_OK) return st;
+    REQUIRE((flags & ~(QSA_SCORE_RELU | QSA_OUT_KEYS)) == 0, QSA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x",
+            flags);
+    REQUIRE(k >= 1, QSA_ERR_INVALID_ARGUMENT, "k must be >= 1 (got %d)", k);
+    const bool out_keys = (flags & QSA_OUT_KEYS) != 0;
+    REQUIRE(out_keys || k % compress_ratio == 0, QSA_ERR_INVALID_ARGUMENT,
+            "k (%d) must be a multiple of compress_ratio (%d) unless QSA_OUT_KEYS is set", k, compress_ratio);
+    const int32_t kb = out_keys ? k : k / compress_ratio;
+    REQUIRE(kb <= QSA_MAX_SELECT, QSA_ERR_UNSUPPORTED, "%d selected entries per row exceed the limit %d", kb,
+            QSA_MAX_SELECT);
+    const size_t need = qsa_select_paged_tokens_workspace_size(rows, num_reqs, max_visible, compress_ratio, k,
+                                                               flags);
+    REQUIRE(workspace_bytes >= need, QSA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < required %zu",
+            workspace_bytes, need);
+    if (rows == 0) return QSA_OK;
+    REQUIRE(out != nullptr, QSA_ERR_INVALID_ARGUMENT, "null pointer: out");
+    REQUIRE(need == 0 || workspace != nullptr, QSA_ERR_INVALID_ARGUMENT, "null pointer: workspace");
+    const DeviceInfo* dev = nullptr;
+    if ((st = check_device(&dev)) != QSA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    qsa::PagedArgs a = make_paged(q, kcache, page_table, pt_stride, num_pages, num_reqs, row_req, pos, rows,
+                                  page_size, compress_ratio, max_visible, flags);
+    float* scores = static_cast<float*>(workspace);
+    const int64_t ld = two_pass_ld(max_visible);
+    if (max_visible > 0) HIP_CHECK(qsa::launch_score_paged(a, scores, ld, s));
+    qsa::VisibleSource vs;
+    vs.visible = nullptr;
+    vs.pos = pos;
+    vs.row_req = row_req;
+    vs.num_reqs = num_reqs;
+    vs.cr = compress_ratio;
+    vs.max_visible = max_visible;
+    HIP_CHECK(qsa::launch_topk_rows(scores, ld, vs, rows, kb, out_keys ? 1 : compress_ratio, k, out, s));
+    g_path = "two_pass";
+    return QSA_OK;
+}

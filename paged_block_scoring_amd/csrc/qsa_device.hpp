@@ -1,0 +1,115 @@
+// qsa_device.hpp -- device-side building blocks shared by the gfx950 kernels.
+//
+// The score of (row r, key j) is computed in exactly one way by every kernel
+// of this library, so that the scorer, the fused selectors and the decode
+// path all produce the same bits:
+//   * one v_mfma_f32_16x16x32_f16 per 32-wide slice of the 128-dim head, four
+//     slices in order d = 0..31, 32..63, 64..95, 96..127, accumulating into
+//     an fp32 accumulator that starts at +0;
+//   * inside a slice, lane group g = lane/16 supplies dims 8g..8g+7 of the
+//     slice for both operands (the A operand is the query head, the B
+//     operand the key);
+//   * the MFMA output row m = 4*row + head, so each lane's four accumulator
+//     values are the four head dots of one (row, key) pair, and the head sum
+//     ((h0 + h1) + h2) + h3 is lane-local.
+// Sources: "[Perf][Qwen4Exp] Admit the cuBLAS QSA indexer and exact top-k on
+// Turing", section "Purpose" (FP16 inputs, FP32 accumulation) and "Test Plan"
+// (4 index heads, head dim 128); "spec(MODEL-MM-QWEN4-EXP): Qwen3.8-Flash-Next
+// is a new architecture ...", section "The component deep-dives, and two
+// corrections to the above" (one key head shared by the index heads, scores
+// summed over heads, relu and 1/sqrt(head_dim) in its form).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+constexpr int kHeads = 4;
+constexpr int kHeadDim = 128;
+constexpr int kKeyBytes = kHeadDim * 2;        // 256 B per compressed key
+constexpr int kChunksPerKey = kKeyBytes / 16;  // 16-byte chunks per key
+
+// fp32 nearest 1/sqrt(128) = 2^-3.5 (bit pattern 0x3DB504F3).
+constexpr float kRsqrtHeadDim = 0x1.6a09e6p-4f;
+
+// Visible keys of a row at position `pos`: key j covers tokens cr*j..cr*j+cr-1
+// and exists once token cr*j+cr-1 does, so j < (pos+1)/cr.  Clamped to the
+// caller's bound so that no kernel ever reads beyond it.
+__device__ __forceinline__ int32_t visible_keys(int32_t pos, int32_t cr, int32_t max_visible) {
+    if (pos < 0) return 0;
+    int64_t v = ((int64_t)pos + 1) / cr;
+    return v > (int64_t)max_visible ? max_visible : (int32_t)v;
+}
+
+// Order-preserving map of a finite fp32 to uint32 (larger float -> larger
+// key); -0 is mapped with +0 so that the two tie, as IEEE compares them.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u << 1) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// 64-bit selection key: score key in the high word, inverted index in the low
+// word, so that a larger composite means "higher score, then lower index".
+__device__ __forceinline__ uint64_t compose(uint32_t key, uint32_t j) {
+    return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - j);
+}
+__device__ __forceinline__ uint32_t composite_index(uint64_t c) {
+    return 0xFFFFFFFFu - (uint32_t)(c & 0xFFFFFFFFull);
+}
+
+__device__ __forceinline__ float4v mfma16(half8 a, half8 b, float4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Head reduction of one lane's accumulator (acc[v] = head v's dot).
+template <bool RELU>
+__device__ __forceinline__ float combine_heads(float4v acc) {
+    if (RELU) {
+        float h0 = fmaxf(acc[0], 0.0f), h1 = fmaxf(acc[1], 0.0f);
+        float h2 = fmaxf(acc[2], 0.0f), h3 = fmaxf(acc[3], 0.0f);
+        float s = ((h0 + h1) + h2) + h3;
+        return s * kRsqrtHeadDim;
+    } else {
+        return ((acc[0] + acc[1]) + acc[2]) + acc[3];
+    }
+}
+
+// Byte offset of 16-byte chunk c of key n inside an LDS key tile (256 B per
+// key).  The chunk index is XOR-swizzled with the key's low 4 bits so that the
+// 16 lanes of an MFMA lane group, which read the same chunk of 16 different
+// keys, hit 16 different bank groups.
+__device__ __forceinline__ int lds_key_chunk(int n, int c) {
+    return n * kKeyBytes + ((c ^ (n & 15)) << 4);
+}
+
+// Block-wide inclusive prefix sum of one int per thread (NT threads, NT a
+// multiple of 64).  `wsum` is LDS scratch of NT/64 ints.  Returns the
+// inclusive prefix; *total receives the block total.  Contains barriers.
+template <int NT>
+__device__ __forceinline__ int block_inclusive_scan(int v, int* wsum, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    if (lane == 63) wsum[wave] = v;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        int x = wsum[w];
+        before += (w < wave) ? x : 0;
+        all += x;
+    }
+    __syncthreads();
+    *total = all;
+    return v + before;
+}
+
+}  // namespace qsa

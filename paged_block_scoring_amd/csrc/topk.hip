@@ -1,0 +1,206 @@
+// topk.hip -- exact lexicographic top-k per row over materialised fp32 scores.
+//
+// Sources: "qwen4_exp QSA cooperative_topk cannot launch on NVIDIA Thor
+// (sm_110): cluster misconfiguration", section "What happens" (the top-k op
+// takes the score matrix, each row's visible count, k and the column count,
+// plus a caller workspace); "[Perf][Qwen4Exp] Admit the cuBLAS QSA indexer and
+// exact top-k on Turing", section "Purpose" (an exact selector: higher score
+// first, lower index on ties, so the selected set is unique even when scores
+// tie at the cutoff) and "Test Result" (the invariant that no selected value
+// is below an unselected one).
+//
+// Method: one workgroup per row.  Scores map to order-preserving 32-bit keys;
+// a (key, inverted index) 64-bit composite is a total order whose descending
+// order is exactly the selection order.
+//  * Rows with at most kCap candidates are sorted whole in LDS.
+//  * Longer rows run an MSB radix select with 11/11/10-bit digits and an LDS
+//    histogram per level.  After each level the count of keys whose resolved
+//    high bits are >= the cutoff prefix is known; as soon as it fits in kCap
+//    those candidates (a superset of the top k) are gathered into LDS and
+//    sorted.  If 32 bits are resolved and the cutoff key still has more
+//    copies than fit, the keys above the cutoff are gathered and the
+//    lowest-index copies of the cutoff key are taken by an index-ordered
+//    block prefix scan.
+//  * A bitonic sort of the 64-bit composites in LDS yields rank order; block
+//    j is written as `expand` consecutive entries j*expand .. j*expand+expand-1
+//    (tokens) or as j (keys), and missing ranks as -1.
+#include "qsa_device.hpp"
+#include "qsa_internal.hpp"
+
+namespace qsa {
+namespace {
+
+constexpr int kNT = 512;
+constexpr int kCap = 4096;
+constexpr int kBins = 2048;
+static_assert(kBins == 4 * kNT, "bin scan assumes 4 bins per thread");
+
+struct TopkArgs {
+    const float* scores;
+    int64_t ld;
+    VisibleSource vis;
+    int32_t kk;
+    int32_t expand;
+    int32_t out_len;
+    int32_t* out;
+};
+
+__device__ __forceinline__ int row_visible(const VisibleSource& v, int r) {
+    if (v.visible) return min(max(v.visible[r], 0), v.max_visible);
+    if (v.pos) {
+        const int req = v.row_req ? v.row_req[r] : 0;
+        if (req < 0 || req >= v.num_reqs) return 0;
+        return visible_keys(v.pos[r], v.cr, v.max_visible);
+    }
+    return v.max_visible;
+}
+
+// Descending bitonic sort of n (a power of two, <= kCap) composites in LDS.
+__device__ void bitonic_sort_desc(uint64_t* a, int n) {
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < n; i += kNT) {
+                const int p = i ^ j;
+                if (p > i) {
+                    const uint64_t x = a[i], y = a[p];
+                    const bool desc = (i & k) == 0;
+                    if (desc ? (x < y) : (x > y)) {
+                        a[i] = y;
+                        a[p] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+__global__ __launch_bounds__(kNT) void topk_rows_kernel(TopkArgs A) {
+    __shared__ uint64_t s_cand[kCap];
+    __shared__ uint32_t s_hist[kBins];
+    __shared__ int s_wsum[kNT / 64];
+    __shared__ int s_count, s_bin, s_above;
+
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int V = row_visible(A.vis, row);
+    const float* srow = A.scores + (int64_t)row * A.ld;
+    const int kk = A.kk;
+    const int nsel = min(kk, V);
+    int ncand;
+
+    if (V <= kCap) {
+        for (int j = tid; j < V; j += kNT) s_cand[j] = compose(order_key(srow[j]), (uint32_t)j);
+        ncand = V;
+    } else {
+        uint32_t prefix = 0;
+        int shift = 32, above_total = 0, need = kk;
+        bool done = false;
+        ncand = 0;
+        for (int level = 0; level < 3 && !done; ++level) {
+            const int bits = level < 2 ? 11 : 10;
+            const int nshift = shift - bits;
+            const uint32_t mask = (1u << bits) - 1u;
+            for (int i = tid; i < kBins; i += kNT) s_hist[i] = 0u;
+            __syncthreads();
+            for (int j = tid; j < V; j += kNT) {
+                const uint32_t u = order_key(srow[j]);
+                if (level == 0 || (u >> shift) == prefix) atomicAdd(&s_hist[(u >> nshift) & mask], 1u);
+            }
+            __syncthreads();
+            // Thread t owns bins 2047-4t .. 2044-4t (descending); a block scan
+            // gives the number of keys in higher bins.
+            int local[4], lsum = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                local[i] = (int)s_hist[kBins - 1 - (4 * tid + i)];
+                lsum += local[i];
+            }
+            int total;
+            int run = block_inclusive_scan<kNT>(lsum, s_wsum, &total) - lsum;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (run < need && run + local[i] >= need) {
+                    s_bin = kBins - 1 - (4 * tid + i);
+                    s_above = run;
+                }
+                run += local[i];
+            }
+            __syncthreads();
+            const int b = s_bin, above = s_above;
+            need -= above;
+            above_total += above;
+            prefix = (level == 0) ? (uint32_t)b : ((prefix << bits) | (uint32_t)b);
+            shift = nshift;
+            const int cnt_ge = above_total + (int)s_hist[b];
+            __syncthreads();
+            if (cnt_ge <= kCap) {
+                if (tid == 0) s_count = 0;
+                __syncthreads();
+                for (int j = tid; j < V; j += kNT) {
+                    const uint32_t u = order_key(srow[j]);
+                    if ((u >> shift) >= prefix) s_cand[atomicAdd(&s_count, 1)] = compose(u, (uint32_t)j);
+                }
+                __syncthreads();
+                ncand = s_count;
+                done = true;
+            }
+        }
+        if (!done) {
+            // prefix is the exact cutoff key; above_total keys exceed it and
+            // `need` of its copies are taken, lowest indices first.
+            const uint32_t tau = prefix;
+            if (tid == 0) s_count = 0;
+            __syncthreads();
+            for (int j = tid; j < V; j += kNT) {
+                const uint32_t u = order_key(srow[j]);
+                if (u > tau) s_cand[atomicAdd(&s_count, 1)] = compose(u, (uint32_t)j);
+            }
+            int base = 0;
+            for (int j0 = 0; j0 < V && base < need; j0 += kNT) {
+                const int j = j0 + tid;
+                const int f = (j < V && order_key(srow[j]) == tau) ? 1 : 0;
+                int total;
+                const int incl = block_inclusive_scan<kNT>(f, s_wsum, &total);
+                const int rank = base + incl - f;
+                if (f && rank < need) s_cand[above_total + rank] = compose(tau, (uint32_t)j);
+                base += total;
+            }
+            __syncthreads();
+            ncand = above_total + min(need, base);
+        }
+    }
+
+    int npow = 1;
+    while (npow < ncand) npow <<= 1;
+    for (int i = ncand + tid; i < npow; i += kNT) s_cand[i] = 0ull;
+    __syncthreads();
+    bitonic_sort_desc(s_cand, npow);
+
+    int32_t* orow = A.out + (int64_t)row * A.out_len;
+    for (int i = tid; i < A.out_len; i += kNT) {
+        const int rank = i / A.expand, t = i - rank * A.expand;
+        int v = -1;
+        if (rank < nsel) v = (int)composite_index(s_cand[rank]) * A.expand + t;
+        orow[i] = v;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_topk_rows(const float* scores, int64_t ld, const VisibleSource& vis, int32_t rows,
+                            int32_t kk, int32_t expand, int32_t out_len, int32_t* out,
+                            hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    TopkArgs A;
+    A.scores = scores;
+    A.ld = ld;
+    A.vis = vis;
+    A.kk = kk;
+    A.expand = expand;
+    A.out_len = out_len;
+    A.out = out;
+    topk_rows_kernel<<<dim3((unsigned)rows), kNT, 0, stream>>>(A);
+    return hipGetLastError();
+}
+
+}  // namespace qsa

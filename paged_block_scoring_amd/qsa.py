@@ -1,0 +1,218 @@
+"""Python binding of ``libqsa.so`` (the C ABI of include/qsa.h).
+
+Argument marshalling only: every step of the indexer runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  The binding
+fails loudly when the library is missing or the tensors are not what the C
+ABI expects; it never computes a result itself and has no fallback.
+
+Function names are those of the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsa.so")
+
+QSA_OK = 0
+QSA_ERR_INVALID_ARGUMENT = 1
+QSA_ERR_UNSUPPORTED = 2
+QSA_ERR_WORKSPACE_TOO_SMALL = 3
+QSA_ERR_DEVICE = 4
+
+QSA_SCORE_RELU = 0x1
+QSA_OUT_KEYS = 0x2
+QSA_MAX_SELECT = 4096
+
+EXPORTED = (
+    "qsa_score_paged", "qsa_topk_rows", "qsa_topk_rows_workspace_size",
+    "qsa_select_paged_tokens", "qsa_select_paged_tokens_workspace_size",
+    "qsa_last_error", "qsa_last_path", "qsa_version",
+)
+
+
+class QSAError(RuntimeError):
+    """A non-zero qsa_status; ``status`` holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"qsa status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (ctypes.CDLL).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with paged_block_scoring_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+    L.qsa_score_paged.argtypes = [P, P, P, i64, i32, i32, P, P, i32, i32, i32, i32, i32, i32, u32, P, i64, P]
+    L.qsa_score_paged.restype = ctypes.c_int
+    L.qsa_topk_rows.argtypes = [P, i64, P, i32, i32, i32, P, P, sz, P]
+    L.qsa_topk_rows.restype = ctypes.c_int
+    L.qsa_topk_rows_workspace_size.argtypes = [i32, i32, i32]
+    L.qsa_topk_rows_workspace_size.restype = sz
+    L.qsa_select_paged_tokens.argtypes = [P, P, P, i64, i32, i32, P, P, i32, i32, i32, i32, i32, i32, i32, u32,
+                                          P, P, sz, P]
+    L.qsa_select_paged_tokens.restype = ctypes.c_int
+    L.qsa_select_paged_tokens_workspace_size.argtypes = [i32, i32, i32, i32, i32, u32]
+    L.qsa_select_paged_tokens_workspace_size.restype = sz
+    for name in ("qsa_last_error", "qsa_last_path", "qsa_version"):
+        getattr(L, name).argtypes = []
+        getattr(L, name).restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def qsa_last_error() -> str:
+    return lib().qsa_last_error().decode()
+
+
+def qsa_last_path() -> str:
+    return lib().qsa_last_path().decode()
+
+
+def qsa_version() -> str:
+    return lib().qsa_version().decode()
+
+
+def _check(status: int):
+    if status != QSA_OK:
+        raise QSAError(status, qsa_last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _want(t, name, dtype, device=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _paged_inputs(q, kcache, page_table, pos, row_req):
+    _want(q, "q", torch.float16, ndim=3)
+    dev = q.device
+    _want(kcache, "kcache", torch.float16, dev, 3)
+    _want(page_table, "page_table", torch.int32, dev, 2)
+    _want(pos, "pos", torch.int32, dev, 1)
+    if row_req is not None:
+        _want(row_req, "row_req", torch.int32, dev, 1)
+        if row_req.numel() != q.shape[0]:
+            raise ValueError("row_req must have one entry per row")
+    if pos.numel() != q.shape[0]:
+        raise ValueError("pos must have one entry per row")
+    return dev
+
+
+def visible_bound(pos: torch.Tensor, compress_ratio: int) -> int:
+    """Host upper bound on the visible key count of any row (reads pos)."""
+    if pos.numel() == 0:
+        return 0
+    return max(0, (int(pos.max().item()) + 1) // int(compress_ratio))
+
+
+def qsa_score_paged(q, kcache, page_table, pos, compress_ratio, *, row_req=None, max_visible=None, flags=0,
+                    scores=None, ld_scores=None) -> torch.Tensor:
+    """fp32 scores [rows][ld_scores]; entry (r, j) is written for j < V_r only.
+
+    q fp16 [rows, heads, head_dim]; kcache fp16 [num_pages, page_size/cr, head_dim];
+    page_table int32 [num_reqs, pt_stride]; pos int32 [rows]; row_req int32 [rows] or None.
+    A freshly allocated ``scores`` is zero-filled.
+    """
+    dev = _paged_inputs(q, kcache, page_table, pos, row_req)
+    if max_visible is None:
+        max_visible = visible_bound(pos, compress_ratio)
+    rows, heads, head_dim = q.shape
+    if ld_scores is None:
+        ld_scores = max(1, int(max_visible))
+    if scores is None:
+        scores = torch.zeros((rows, ld_scores), dtype=torch.float32, device=dev)
+    _want(scores, "scores", torch.float32, dev, 2)
+    if scores.shape[1] != ld_scores or scores.shape[0] < rows:
+        raise ValueError("scores must be [rows, ld_scores]")
+    page_size = kcache.shape[1] * int(compress_ratio)
+    _check(lib().qsa_score_paged(
+        _ptr(q), _ptr(kcache), _ptr(page_table), page_table.shape[1], kcache.shape[0], page_table.shape[0],
+        _ptr(row_req), _ptr(pos), rows, heads, head_dim, page_size, int(compress_ratio), int(max_visible),
+        int(flags), _ptr(scores), int(ld_scores), _stream(dev)))
+    return scores
+
+
+def qsa_topk_rows_workspace_size(rows, max_visible, k) -> int:
+    return int(lib().qsa_topk_rows_workspace_size(int(rows), int(max_visible), int(k)))
+
+
+def qsa_topk_rows(scores, k, *, visible=None, max_visible=None, out=None, workspace=None) -> torch.Tensor:
+    """Exact top-k key indices per row of ``scores`` [rows, ld] (rank order, -1 padded)."""
+    _want(scores, "scores", torch.float32, ndim=2)
+    dev = scores.device
+    rows, ld = scores.shape
+    if visible is not None:
+        _want(visible, "visible", torch.int32, dev, 1)
+        if visible.numel() != rows:
+            raise ValueError("visible must have one entry per row")
+    if max_visible is None:
+        max_visible = ld
+    if out is None:
+        out = torch.empty((rows, int(k)), dtype=torch.int32, device=dev)
+    _want(out, "out", torch.int32, dev, 2)
+    need = qsa_topk_rows_workspace_size(rows, max_visible, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().qsa_topk_rows(_ptr(scores), ld, _ptr(visible), rows, int(max_visible), int(k), _ptr(out),
+                               _ptr(workspace), wbytes, _stream(dev)))
+    return out
+
+
+def qsa_select_paged_tokens_workspace_size(rows, num_reqs, max_visible, compress_ratio, k, flags=0) -> int:
+    return int(lib().qsa_select_paged_tokens_workspace_size(int(rows), int(num_reqs), int(max_visible),
+                                                            int(compress_ratio), int(k), int(flags)))
+
+
+def qsa_select_paged_tokens(q, kcache, page_table, pos, compress_ratio, k, *, row_req=None, max_visible=None,
+                            flags=0, out=None, workspace=None) -> torch.Tensor:
+    """The whole indexer: int32 [rows, k] token indices (or key indices with
+    QSA_OUT_KEYS), rank order, -1 padded."""
+    dev = _paged_inputs(q, kcache, page_table, pos, row_req)
+    if max_visible is None:
+        max_visible = visible_bound(pos, compress_ratio)
+    rows, heads, head_dim = q.shape
+    num_reqs = page_table.shape[0]
+    if out is None:
+        out = torch.empty((rows, int(k)), dtype=torch.int32, device=dev)
+    _want(out, "out", torch.int32, dev, 2)
+    need = qsa_select_paged_tokens_workspace_size(rows, num_reqs, max_visible, compress_ratio, k, flags)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    page_size = kcache.shape[1] * int(compress_ratio)
+    _check(lib().qsa_select_paged_tokens(
+        _ptr(q), _ptr(kcache), _ptr(page_table), page_table.shape[1], kcache.shape[0], num_reqs,
+        _ptr(row_req), _ptr(pos), rows, heads, head_dim, page_size, int(compress_ratio), int(max_visible),
+        int(k), int(flags), _ptr(out), _ptr(workspace), wbytes, _stream(dev)))
+    return out

@@ -1,0 +1,149 @@
+"""CPU tests of the C-ABI library: it loads, exports every function declared
+in include/qsa.h, sizes workspaces, and rejects invalid arguments on the host
+before touching a device (no GPU needed; no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from paged_block_scoring_amd import qsa as Q
+
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+FAKE = 0x10000  # an aligned, never-dereferenced pointer value
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    for name in ("qsa_score_paged", "qsa_topk_rows", "qsa_select_paged_tokens",
+                 "qsa_topk_rows_workspace_size", "qsa_select_paged_tokens_workspace_size",
+                 "qsa_last_error", "qsa_version"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol():
+    L = Q.lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+    assert set(header_functions()) == set(Q.EXPORTED)
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in Q.qsa_version()
+    assert Q.qsa_last_error() == ""
+
+
+def test_workspace_sizes():
+    assert Q.qsa_select_paged_tokens_workspace_size(0, 1, 100, 4, 64) == 0
+    assert Q.qsa_select_paged_tokens_workspace_size(10, 1, 0, 4, 64) == 0
+    n = Q.qsa_select_paged_tokens_workspace_size(1616, 1, 46000, 4, 2048)
+    assert n >= 1616 * 46000 * 4
+    assert Q.qsa_topk_rows_workspace_size(10, 100, 8) >= 0
+
+
+def select(**over):
+    a = dict(q=FAKE, kcache=FAKE, page_table=FAKE, pt_stride=16, num_pages=16, num_reqs=1, row_req=None,
+             pos=FAKE, rows=8, heads=4, head_dim=128, page_size=64, cr=4, max_visible=256, k=64, flags=0,
+             out=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    st = Q.lib().qsa_select_paged_tokens(
+        a["q"], a["kcache"], a["page_table"], a["pt_stride"], a["num_pages"], a["num_reqs"], a["row_req"],
+        a["pos"], a["rows"], a["heads"], a["head_dim"], a["page_size"], a["cr"], a["max_visible"], a["k"],
+        a["flags"], a["out"], a["ws"], a["ws_bytes"], a["stream"])
+    return st, Q.qsa_last_error()
+
+
+def score(**over):
+    a = dict(q=FAKE, kcache=FAKE, page_table=FAKE, pt_stride=16, num_pages=16, num_reqs=1, row_req=None,
+             pos=FAKE, rows=8, heads=4, head_dim=128, page_size=64, cr=4, max_visible=256, flags=0,
+             scores=FAKE, ld=256, stream=None)
+    a.update(over)
+    st = Q.lib().qsa_score_paged(
+        a["q"], a["kcache"], a["page_table"], a["pt_stride"], a["num_pages"], a["num_reqs"], a["row_req"],
+        a["pos"], a["rows"], a["heads"], a["head_dim"], a["page_size"], a["cr"], a["max_visible"],
+        a["flags"], a["scores"], a["ld"], a["stream"])
+    return st, Q.qsa_last_error()
+
+
+def topk(**over):
+    a = dict(scores=FAKE, ld=100, visible=None, rows=4, max_visible=100, k=8, out=FAKE, ws=None, ws_bytes=0,
+             stream=None)
+    a.update(over)
+    st = Q.lib().qsa_topk_rows(a["scores"], a["ld"], a["visible"], a["rows"], a["max_visible"], a["k"],
+                               a["out"], a["ws"], a["ws_bytes"], a["stream"])
+    return st, Q.qsa_last_error()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(heads=3), Q.QSA_ERR_UNSUPPORTED),
+    (dict(head_dim=64), Q.QSA_ERR_UNSUPPORTED),
+    (dict(k=63), Q.QSA_ERR_INVALID_ARGUMENT),                 # k not a multiple of cr
+    (dict(k=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(k=4 * (Q.QSA_MAX_SELECT + 1)), Q.QSA_ERR_UNSUPPORTED),
+    (dict(k=Q.QSA_MAX_SELECT + 1, flags=Q.QSA_OUT_KEYS), Q.QSA_ERR_UNSUPPORTED),
+    (dict(q=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(kcache=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(page_table=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(pos=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(out=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(ws_bytes=16), Q.QSA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(page_size=66), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(cr=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(pt_stride=15), Q.QSA_ERR_INVALID_ARGUMENT),        # 256 keys need 16 pages of 16 keys
+    (dict(num_pages=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(num_reqs=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(rows=-1), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(max_visible=-1), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(flags=0x8), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(q=FAKE + 4), Q.QSA_ERR_INVALID_ARGUMENT),           # misaligned
+])
+def test_select_rejects_before_device(over, code):
+    st, msg = select(**over)
+    assert st == code, msg
+    assert re.match(r"^qsa_api\.hip:\d+: .+", msg), msg
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(ld=255), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(scores=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(flags=Q.QSA_OUT_KEYS), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(heads=8), Q.QSA_ERR_UNSUPPORTED),
+])
+def test_score_rejects_before_device(over, code):
+    st, msg = score(**over)
+    assert st == code, msg
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(k=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(k=Q.QSA_MAX_SELECT + 1), Q.QSA_ERR_UNSUPPORTED),
+    (dict(ld=99), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(out=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(rows=-2), Q.QSA_ERR_INVALID_ARGUMENT),
+])
+def test_topk_rejects_before_device(over, code):
+    st, msg = topk(**over)
+    assert st == code, msg
+
+
+def test_zero_rows_is_a_noop_without_device():
+    assert select(rows=0, q=None, out=None, ws=None, ws_bytes=0)[0] == Q.QSA_OK
+    assert score(rows=0, q=None, scores=None)[0] == Q.QSA_OK
+    assert topk(rows=0, out=None)[0] == Q.QSA_OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros((2, 4, 128), dtype=torch.float16)
+    with pytest.raises(ValueError):
+        Q.qsa_select_paged_tokens(q, q, torch.zeros((1, 1), dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
+                                  4, 64)

@@ -1,0 +1,310 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar (from the indexer's definition): integer-valued inputs are exact in fp32
+whatever the summation order, so scores and indices must be bit-exact with
+the oracle; on Gaussian inputs each score must lie within 1e-3 * max(|ref|, 1)
+of the oracle's, and the selection the GPU makes on its own scores must be
+bit-exact with the oracle's selector applied to those same scores.  Sources:
+"[Perf][Qwen4Exp] Admit the cuBLAS QSA indexer and exact top-k on Turing",
+sections "Purpose" (exact lexicographic selector) and "Test Plan" (selected
+token sets identical in all rows); "spec(MODEL-MM-QWEN4-EXP) ...", section
+"The component deep-dives, and two corrections to the above".
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from paged_block_scoring_amd import qsa as Q
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+RELU = Q.QSA_SCORE_RELU
+KEYS = Q.QSA_OUT_KEYS
+
+
+def note(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(w):
+    return dict(q=torch.from_numpy(w.q).to(DEV), kcache=torch.from_numpy(w.kcache).to(DEV),
+                page_table=torch.from_numpy(w.page_table).to(DEV), pos=torch.from_numpy(w.pos).to(DEV),
+                row_req=torch.from_numpy(w.row_req).to(DEV))
+
+
+def visible(oracle_mod, w):
+    return np.array([oracle_mod.visible_keys(int(p), w.compress_ratio) for p in w.pos], np.int32)
+
+
+def gpu_scores(d, w, flags):
+    s = Q.qsa_score_paged(d["q"], d["kcache"], d["page_table"], d["pos"], w.compress_ratio, row_req=d["row_req"],
+                          flags=flags & RELU)
+    torch.cuda.synchronize()
+    return s.cpu().numpy()
+
+
+def gpu_select(d, w, flags, k=None):
+    out = Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"], w.compress_ratio,
+                                    k or w.k, row_req=d["row_req"], flags=flags)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def expand(blocks, cr):
+    rows, kb = blocks.shape
+    t = np.where(blocks[:, :, None] >= 0, blocks[:, :, None] * cr + np.arange(cr), -1)
+    return t.reshape(rows, kb * cr).astype(np.int32)
+
+
+def expected_from_scores(oracle_mod, scores, V, k, cr, flags):
+    kb = k if flags & KEYS else k // cr
+    blocks = oracle_mod.select_rows(scores, V, kb)
+    return blocks if flags & KEYS else expand(blocks, cr)
+
+
+def assert_scores(gs, ref, V, exact, rows=None):
+    rows = range(len(V)) if rows is None else rows
+    worst = 0.0
+    for i, r in enumerate(rows):
+        a = gs[r, :V[r]].astype(np.float64)
+        b = ref[i, :V[r]].astype(np.float64)
+        if exact:
+            assert np.array_equal(a, b), f"row {r}: first mismatch at {np.argmax(a != b)}"
+        else:
+            err = np.abs(a - b) / np.maximum(np.abs(b), 1.0)
+            worst = max(worst, float(err.max(initial=0.0)))
+            assert np.all(err <= 1e-3), f"row {r}: max rel err {err.max()}"
+    return worst
+
+
+def full_parity(oracle_mod, w, flags, integer):
+    """Scores element by element, the GPU selection on its own scores, and
+    (integer inputs) the whole path against the oracle."""
+    d = to_dev(w)
+    V = visible(oracle_mod, w)
+    gs = gpu_scores(d, w, flags)
+    ref = oracle_mod.score_paged(w.q, w.kcache, w.page_table, w.pos, w.compress_ratio, row_req=w.row_req,
+                                 flags=flags & RELU)
+    worst = assert_scores(gs, ref, V, exact=integer)
+    out = gpu_select(d, w, flags)
+    exp = expected_from_scores(oracle_mod, gs, V, w.k, w.compress_ratio, flags)
+    assert np.array_equal(out, exp)
+    if integer:
+        full = oracle_mod.select_paged_tokens(w.q, w.kcache, w.page_table, w.pos, w.compress_ratio, w.k,
+                                              row_req=w.row_req, flags=flags)
+        assert np.array_equal(out, full)
+    note(f"{w.name}: rows={w.rows} sumV={int(V.sum())} flags={flags} max_rel_err={worst:.2e}")
+    return out
+
+
+# ------------------------------------------------------------ small, whole
+
+@pytest.mark.parametrize("flags", [0, RELU, KEYS, RELU | KEYS])
+@pytest.mark.parametrize("integer", [False, True])
+def test_tiny(oracle_mod, flags, integer):
+    full_parity(oracle_mod, W.tiny(integer=integer), flags, integer)
+
+
+REDUCED = {
+    # 80 rows: one full 64-row tile plus a ragged 16-row tail; 46,000 keys
+    # span 45 key chunks and end mid-chunk.
+    "kernel_shape_80": lambda integer: W.kernel_shape(rows=80, integer=integer),
+    "tie_stress_96": lambda integer: W.tie_stress(rows=96),
+    "mixed_small": lambda integer: W.mixed(total_rows=100, max_rows=40, ctx_hi=40_000, integer=integer),
+    "decode_small": lambda integer: W.decode(num_reqs=12, integer=integer),
+    # three requests of 40 rows: 64-row tiles straddle request boundaries
+    "three_reqs_40": lambda integer: W.build("three_reqs_40", np.random.default_rng(31), 31,
+                                             [9000, 5003, 12345], [40, 40, 40], permute_pages=True,
+                                             integer=integer, k=2048),
+}
+
+
+@pytest.mark.parametrize("flags", [0, RELU])
+@pytest.mark.parametrize("integer", [False, True])
+@pytest.mark.parametrize("name", sorted(REDUCED))
+def test_reduced(oracle_mod, name, integer, flags):
+    if name == "tie_stress_96" and not integer:
+        pytest.skip("the tie-stress workload is integer-valued by definition")
+    w = REDUCED[name](integer)
+    full_parity(oracle_mod, w, flags, integer or name == "tie_stress_96")
+
+
+def test_out_keys_reduced(oracle_mod):
+    w = W.kernel_shape(rows=40, ctx=30_000)
+    d = to_dev(w)
+    V = visible(oracle_mod, w)
+    gs = gpu_scores(d, w, 0)
+    for k in (1, 7, 512, 2048, Q.QSA_MAX_SELECT):
+        out = gpu_select(d, w, KEYS, k=k)
+        assert np.array_equal(out, expected_from_scores(oracle_mod, gs, V, k, 4, KEYS)), k
+
+
+def test_interleaved_requests(oracle_mod):
+    """Rows of different requests in any order (not grouped by request)."""
+    rng = np.random.default_rng(41)
+    w = W.build("interleaved", rng, 41, [3000, 7000, 500, 12000], [30, 20, 5, 25], permute_pages=True,
+                integer=True, k=256)
+    perm = rng.permutation(w.rows)
+    w.q, w.pos, w.row_req = np.ascontiguousarray(w.q[perm]), w.pos[perm].copy(), w.row_req[perm].copy()
+    full_parity(oracle_mod, w, 0, True)
+
+
+def test_edges(oracle_mod):
+    """V = 0 rows, V below / equal / above the block budget, k = cr, a
+    partial last page, rows = 1."""
+    rng = np.random.default_rng(42)
+    ctx = 64 * 7 + 13
+    w = W.build("edges", rng, 42, [ctx], [1], permute_pages=True, integer=True, k=4 * 32)
+    w.pos = np.array([ctx - 1], np.int32)
+    cases = [0, 1, 2, 3, 4, 126, 127, 128, 129, 130, 131, 255, ctx - 1]
+    w.q = np.repeat(w.q, len(cases), axis=0)
+    w.pos = np.array(cases, np.int32)
+    w.row_req = np.zeros(len(cases), np.int32)
+    full_parity(oracle_mod, w, 0, True)
+    for k in (4, 8):
+        out = gpu_select(to_dev(w), w, 0, k=k)
+        exp = oracle_mod.select_paged_tokens(w.q, w.kcache, w.page_table, w.pos, 4, k)
+        assert np.array_equal(out, exp), k
+    one = W.build("one", rng, 43, [5000], [1], permute_pages=False, integer=True, k=2048)
+    full_parity(oracle_mod, one, 0, True)
+
+
+def test_golden_fixture_on_gpu():
+    from conftest import golden_arrays, load_golden
+    g = load_golden("paged_ties_expand.json")
+    q, kc, pt, pos = golden_arrays(g)
+    d = dict(q=torch.from_numpy(q).to(DEV), kcache=torch.from_numpy(kc).to(DEV),
+             page_table=torch.from_numpy(pt).to(DEV), pos=torch.from_numpy(pos).to(DEV))
+    cr = g["compress_ratio"]
+    out = Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"], cr, g["k"])
+    assert out.cpu().numpy().tolist() == g["expected_tokens"]
+    out = Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"], cr, g["k"], flags=RELU)
+    assert out.cpu().numpy().tolist() == g["expected_tokens_relu"]
+    out = Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"], cr, g["k_keys"], flags=KEYS)
+    assert out.cpu().numpy().tolist() == g["expected_keys"]
+    s = Q.qsa_score_paged(d["q"], d["kcache"], d["page_table"], d["pos"], cr)
+    assert s[0, :16].cpu().numpy().tolist() == g["expected_scores_row0_first16"]
+
+
+def test_determinism():
+    w = W.kernel_shape(rows=130, ctx=60_000)
+    d = to_dev(w)
+    outs = [gpu_select(d, w, 0) for _ in range(3)]
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        o = Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"], 4, w.k, row_req=d["row_req"])
+    side.synchronize()
+    outs.append(o.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    assert Q.qsa_last_path() != ""
+
+
+# ------------------------------------------------------------ selector alone
+
+def run_topk(scores_np, V, k, max_visible=None):
+    s = torch.from_numpy(scores_np).to(DEV)
+    vis = torch.from_numpy(np.asarray(V, np.int32)).to(DEV)
+    out = Q.qsa_topk_rows(s, k, visible=vis, max_visible=max_visible)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_topk_rows_random_with_ties(oracle_mod):
+    rng = np.random.default_rng(51)
+    for trial, (rows, ld, k) in enumerate([(37, 300, 17), (16, 5000, 512), (9, 20_000, 2048),
+                                           (5, 9000, Q.QSA_MAX_SELECT), (64, 70, 64)]):
+        kind = trial % 3
+        if kind == 0:
+            sc = rng.integers(-3, 4, size=(rows, ld)).astype(np.float32)
+        elif kind == 1:
+            sc = rng.standard_normal((rows, ld)).astype(np.float32)
+        else:
+            sc = rng.choice(np.array([-0.0, 0.0, 1.5, -2.0, 7.0], np.float32), size=(rows, ld))
+        V = rng.integers(0, ld + 1, size=rows).astype(np.int32)
+        V[0] = ld
+        out = run_topk(sc, V, k, max_visible=ld)
+        assert np.array_equal(out, oracle_mod.select_rows(sc, V, k)), (rows, ld, k)
+
+
+def test_topk_rows_stress_row(oracle_mod):
+    """A row of 106,861 scores with k = 2,048: the stress shape of the Turing
+    PR's "Test Result"; no selected value may be below an unselected one."""
+    rng = np.random.default_rng(52)
+    n, k = 106_861, 2048
+    sc = (rng.standard_normal((1, n)) * 100).astype(np.float32)
+    sc[0, rng.integers(0, n, 5000)] = 3.0        # a block of exact ties near the middle
+    out = run_topk(sc, [n], k)[0]
+    assert np.array_equal(out, oracle_mod.select_rows(sc, np.array([n], np.int32), k)[0])
+    sel = np.zeros(n, bool)
+    sel[out] = True
+    assert sc[0, sel].min() >= sc[0, ~sel].max()
+
+
+def test_topk_rows_all_equal(oracle_mod):
+    """More copies of the cutoff key than fit in LDS: the index-ordered path."""
+    n, k = 50_000, Q.QSA_MAX_SELECT
+    sc = np.full((2, n), 0.25, np.float32)
+    sc[1, 7] = 1.0
+    sc[1, 40_000] = 1.0
+    out = run_topk(sc, [n, n], k)
+    assert np.array_equal(out[0], np.arange(k))
+    assert np.array_equal(out, oracle_mod.select_rows(sc, np.array([n, n], np.int32), k))
+
+
+def test_topk_rows_visible_none(oracle_mod):
+    rng = np.random.default_rng(53)
+    sc = rng.standard_normal((7, 6000)).astype(np.float32)
+    s = torch.from_numpy(sc).to(DEV)
+    out = Q.qsa_topk_rows(s, 100).cpu().numpy()
+    assert np.array_equal(out, oracle_mod.select_rows(sc, np.full(7, 6000, np.int32), 100))
+
+
+# ------------------------------------------------------------ full sizes
+
+def sampled_parity(oracle_mod, w, flags, integer, sample_rows):
+    """Full-size launch (the configuration the benchmark times): the oracle
+    scores a sample of rows one by one; the GPU selection over every row is
+    checked against the oracle's selector on the GPU's own scores."""
+    d = to_dev(w)
+    V = visible(oracle_mod, w)
+    gs = gpu_scores(d, w, flags)
+    rows = sorted(set(int(r) for r in sample_rows))
+    ref = oracle_mod.score_paged(w.q[rows], w.kcache, w.page_table, w.pos[rows], w.compress_ratio,
+                                 row_req=w.row_req[rows], flags=flags & RELU)
+    worst = assert_scores(gs, ref, V, exact=integer, rows=rows)
+    out = gpu_select(d, w, flags)
+    exp = expected_from_scores(oracle_mod, gs, V, w.k, w.compress_ratio, flags)
+    assert np.array_equal(out, exp)
+    note(f"{w.name} full: rows={w.rows} sumV={int(V.sum())} sampled={len(rows)} max_rel_err={worst:.2e}")
+    return out
+
+
+def test_full_kernel_shape(oracle_mod):
+    w = W.kernel_shape()
+    sampled_parity(oracle_mod, w, 0, False, [0, 1, 63, 64, 800, 1550, 1599, 1600, 1615])
+
+
+def test_full_tie_stress(oracle_mod):
+    w = W.tie_stress()
+    d = to_dev(w)
+    out = gpu_select(d, w, 0)
+    full = oracle_mod.select_paged_tokens(w.q, w.kcache, w.page_table, w.pos, 4, w.k)
+    assert np.array_equal(out, full)
+
+
+def test_full_mixed(oracle_mod):
+    w = W.mixed()
+    starts = np.concatenate([[0], np.cumsum(np.bincount(w.row_req))])
+    sample = list(starts[:-1]) + list(starts[1:] - 1)
+    sampled_parity(oracle_mod, w, 0, False, sample)
+
+
+@pytest.mark.slow
+def test_full_decode(oracle_mod):
+    w = W.decode()
+    sampled_parity(oracle_mod, w, 0, False, list(range(0, 256, 17)))

@@ -192,6 +192,17 @@ const char* qsa_last_path(void);
 /* Library version string. */
 const char* qsa_version(void);
 
+/* Instrumentation for benchmarks and profilers.  Arms the calling thread's
+ * next qsa_select_paged_tokens call to record events[0] on its stream before
+ * its first kernel and events[i] after its i-th kernel, for at most n events
+ * (hipEvent_t handles created and owned by the caller, passed as void*; they
+ * must stay valid until that call returns).  The call disarms the hook;
+ * qsa_debug_events_recorded() then returns how many events it recorded.
+ * Kernel order: two-pass arm = scorer, selector; fused arm = sampling scorer,
+ * threshold, filtering scorer, final select. */
+qsa_status qsa_debug_record_events(void* const* events, int32_t n);
+int32_t qsa_debug_events_recorded(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,234 @@
+// fused.hip -- the fused arm of qsa_select_paged_tokens: exact lexicographic
+// top-k without materialising the score matrix.
+//
+// Sources: "[Perf][Qwen4Exp] Admit the cuBLAS QSA indexer and exact top-k on
+// Turing", section "Purpose" (exact selector, deterministic ties) and "Test
+// Plan" (top-k 2,048 tokens); "qwen4_exp QSA cooperative_topk cannot launch on
+// NVIDIA Thor (sm_110): cluster misconfiguration", section "What happens" (the
+// two-stage score-then-top-k structure this arm replaces).
+//
+// Every (row, key) has a distinct composite c = (order key of the score,
+// inverted key index); the selected blocks are the row's kb largest
+// composites.  The arm runs in four steps:
+//  1. sampling pass: the scorer materialises the scores of every stride-th
+//     key (logical sample i is key stride*i);
+//  2. threshold: per row, T = the m-th largest sample composite, with m
+//     sized so that about kb + 4 sqrt(kb) ... keys of the whole row are
+//     expected to reach T (T = 0, "keep everything", when the row has fewer
+//     than m samples);
+//  3. filtering pass: the scorer keeps every composite >= T in the row's
+//     candidate list (staged in LDS, one global atomic per row and
+//     workgroup);
+//  4. final select: if the row has at least min(kb, V) and at most cap
+//     candidates they contain its exact top-kb (any kb composites >= T force
+//     the kb-th largest to be >= T), which a radix select and a bitonic sort
+//     in LDS turn into rank order.  Otherwise the workgroup recomputes the
+//     row's scores itself with the same MFMA sequence and keeps an exact
+//     running top-kb in LDS.  Either way the result is exact; the sample only
+//     decides how fast.
+#include <cmath>
+
+#include "qsa_device.hpp"
+#include "qsa_internal.hpp"
+#include "qsa_select.hpp"
+
+namespace qsa {
+namespace {
+
+__device__ __forceinline__ int row_visible_count(const VisibleSource& v, int r) {
+    if (v.visible) return min(max(v.visible[r], 0), v.max_visible);
+    if (v.pos) {
+        const int req = v.row_req ? v.row_req[r] : 0;
+        if (req < 0 || req >= v.num_reqs) return 0;
+        return visible_keys(v.pos[r], v.cr, v.max_visible);
+    }
+    return v.max_visible;
+}
+
+constexpr int kThrNT = 256;
+constexpr int kMaxSamples = 4096;
+
+__global__ __launch_bounds__(kThrNT) void sample_threshold_kernel(const float* __restrict__ samp, int64_t ld_s,
+                                                                  VisibleSource vis, int32_t stride, int32_t m,
+                                                                  int32_t force_fallback,
+                                                                  uint64_t* __restrict__ thresh,
+                                                                  int32_t* __restrict__ cand_count) {
+    __shared__ uint64_t s_a[kMaxSamples];
+    __shared__ KthScratch ks;
+    const int row = blockIdx.x;
+    const int V = row_visible_count(vis, row);
+    const int ns = (V + stride - 1) / stride;
+    uint64_t T = 0ull;
+    if (ns >= m) {
+        const float* srow = samp + (int64_t)row * ld_s;
+        for (int i = threadIdx.x; i < ns; i += kThrNT)
+            s_a[i] = compose(order_key(srow[i]), (uint32_t)(i * stride));
+        __syncthreads();
+        T = lds_kth_largest<kThrNT>(s_a, ns, m, &ks);
+    }
+    if (force_fallback) T = ~0ull;  // nothing can pass: every row takes the recompute path
+    if (threadIdx.x == 0) {
+        thresh[row] = T;
+        cand_count[row] = 0;
+    }
+}
+
+struct FinalArgs {
+    PagedArgs a;
+    VisibleSource vis;
+    const uint64_t* cand;
+    const int32_t* cand_count;
+    int32_t cand_cap;
+    int32_t kb;
+    int32_t expand;
+    int32_t out_len;
+    int32_t* out;
+};
+
+constexpr int kFinNT = 256;
+constexpr int kFinWaves = kFinNT / 64;
+
+// Exact top-kb of one row by recomputation: each wave scores 32 keys at a
+// time straight from the cache with the same MFMA sequence as the tiled
+// scorer (the row's four heads occupy MFMA rows 0..3; the other rows are
+// zero), composites above the running cutoff are
+// appended in LDS, and the buffer is cut back to its kb largest whenever it
+// exceeds kb.  Leaves the selected composites (unsorted) in
+// a[0 .. return value).
+template <int CAPL>
+__device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* a, KthScratch* ks, int* s_pend) {
+    const PagedArgs& p = A.a;
+    const int kb = A.kb;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int ch = (CAPL - kb) / (32 * kFinWaves) * (32 * kFinWaves);
+    if (ch > 2048) ch = 2048;
+    const int req = p.row_req ? p.row_req[row] : 0;
+    const int32_t* ptrow = p.page_table + (int64_t)req * p.pt_stride;
+    const _Float16* qrow = p.q + (int64_t)row * kHeads * kHeadDim;
+    const int m = lane & 31, g = lane >> 5;
+    int na = 0;
+    uint64_t cut = 0ull;  // composites must exceed this to matter once na == kb
+    for (int c0 = 0; c0 < V; c0 += ch) {
+        if (threadIdx.x == 0) *s_pend = 0;
+        __syncthreads();
+        const int cend = min(c0 + ch, V);
+        for (int j0 = c0 + 32 * wave; j0 < cend; j0 += 32 * kFinWaves) {
+            const int j = j0 + m;
+            const int jc = min(j, V - 1);
+            const int lp = jc / p.kpp;
+            const int slot = jc - lp * p.kpp;
+            const int pg = min(max(ptrow[lp], 0), p.num_pages - 1);
+            const _Float16* key = p.kcache + ((size_t)pg * p.kpp + slot) * kHeadDim;
+            half8 kb8[kSlices];
+#pragma unroll
+            for (int s = 0; s < kSlices; ++s) kb8[s] = *reinterpret_cast<const half8*>(key + 16 * s + 8 * g);
+            // MFMA rows 0..3 are the row's four heads; rows 4..31 are zero
+            float16v acc = {};
+#pragma unroll
+            for (int s = 0; s < kSlices; ++s) {
+                half8 qv = {};
+                if (m < 4) qv = *reinterpret_cast<const half8*>(qrow + m * kHeadDim + 16 * s + 8 * g);
+                acc = mfma32(qv, kb8[s], acc);
+            }
+            const float sc = p.relu ? combine_heads<true>(acc[0], acc[1], acc[2], acc[3])
+                                    : combine_heads<false>(acc[0], acc[1], acc[2], acc[3]);
+            // lanes 0..31 hold MFMA row 0 (the row's score) for key j0 + lane
+            if (g == 0 && j < cend) {
+                const uint64_t comp = compose(order_key(sc), (uint32_t)j);
+                if (comp > cut) a[na + atomicAdd(s_pend, 1)] = comp;
+            }
+        }
+        __syncthreads();
+        const int tot = na + *s_pend;
+        __syncthreads();
+        if (tot > kb) {
+            cut = lds_kth_largest<kFinNT>(a, tot, kb, ks);
+            lds_compact_ge<kFinNT, CAPL / kFinNT>(a, tot, cut, ks->wsum);
+            na = kb;
+        } else {
+            na = tot;
+        }
+    }
+    return na;
+}
+
+template <int CAPL>
+__global__ __launch_bounds__(kFinNT) void fused_final_kernel(FinalArgs A) {
+    __shared__ uint64_t s_a[CAPL];
+    __shared__ KthScratch ks;
+    __shared__ int s_pend;
+    const int row = blockIdx.x;
+    const int V = row_visible_count(A.vis, row);
+    const int kb = A.kb;
+    const int nsel = min(kb, V);
+    const int n = A.cand_count[row];
+    int have;
+    if (n >= nsel && n <= A.cand_cap) {
+        const uint64_t* c = A.cand + (int64_t)row * A.cand_cap;
+        for (int i = threadIdx.x; i < n; i += kFinNT) s_a[i] = c[i];
+        __syncthreads();
+        have = n;
+        if (n > kb) {
+            const uint64_t t = lds_kth_largest<kFinNT>(s_a, n, kb, &ks);
+            have = lds_compact_ge<kFinNT, CAPL / kFinNT>(s_a, n, t, ks.wsum);
+        }
+    } else {
+        have = recompute_row_topk<CAPL>(A, row, V, s_a, &ks, &s_pend);
+    }
+    lds_sort_desc<kFinNT>(s_a, have);
+    int32_t* orow = A.out + (int64_t)row * A.out_len;
+    for (int i = threadIdx.x; i < A.out_len; i += kFinNT) {
+        const int rank = i / A.expand, t = i - rank * A.expand;
+        int v = -1;
+        if (rank < nsel) v = (int)composite_index(s_a[rank]) * A.expand + t;
+        orow[i] = v;
+    }
+}
+
+}  // namespace
+
+FusedPlan plan_fused(int32_t max_visible, int32_t kb) {
+    FusedPlan f;
+    int stride = 16;
+    while ((max_visible + stride - 1) / stride > kMaxSamples) stride *= 2;
+    f.stride = stride;
+    const double e = (double)kb / stride;
+    f.m = (int32_t)(e + 4.0 * std::sqrt(e) + 16.0 + 0.999);
+    f.capl = kb <= 1024 ? 4096 : 8192;
+    f.cand_cap = f.capl;
+    f.ld_s = ((max_visible + stride - 1) / stride + 63) / 64 * 64;
+    if (f.ld_s < 64) f.ld_s = 64;
+    return f;
+}
+
+hipError_t launch_sample_threshold(const float* samp, int64_t ld_s, const VisibleSource& vis, const FusedPlan& f,
+                                   bool force_fallback, uint64_t* thresh, int32_t* cand_count, int32_t rows,
+                                   hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    sample_threshold_kernel<<<dim3((unsigned)rows), kThrNT, 0, stream>>>(
+        samp, ld_s, vis, f.stride, f.m, force_fallback ? 1 : 0, thresh, cand_count);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused_final(const PagedArgs& a, const VisibleSource& vis, const FusedPlan& f, const uint64_t* cand,
+                              const int32_t* cand_count, int32_t kb, int32_t expand, int32_t out_len, int32_t* out,
+                              hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    FinalArgs A;
+    A.a = a;
+    A.vis = vis;
+    A.cand = cand;
+    A.cand_count = cand_count;
+    A.cand_cap = f.cand_cap;
+    A.kb = kb;
+    A.expand = expand;
+    A.out_len = out_len;
+    A.out = out;
+    if (f.capl == 4096)
+        fused_final_kernel<4096><<<dim3((unsigned)a.rows), kFinNT, 0, stream>>>(A);
+    else
+        fused_final_kernel<8192><<<dim3((unsigned)a.rows), kFinNT, 0, stream>>>(A);
+    return hipGetLastError();
+}
+
+}  // namespace qsa

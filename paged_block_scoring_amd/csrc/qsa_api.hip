@@ -24,6 +24,15 @@ namespace {
 
 thread_local char g_err[1024] = "";
 thread_local const char* g_path = "";
+thread_local void* const* g_events = nullptr;  // armed instrumentation events
+thread_local int32_t g_nevents = 0;
+thread_local int32_t g_recorded = 0;
+
+// Records the next armed event (if any) on `s`.
+hipError_t mark(hipStream_t s) {
+    if (g_events && g_recorded < g_nevents) return hipEventRecord(static_cast<hipEvent_t>(g_events[g_recorded++]), s);
+    return hipSuccess;
+}
 
 qsa_status fail_at(const char* file, int line, qsa_status code, const char* fmt, ...) {
     const char* base = strrchr(file, '/');
@@ -106,6 +115,8 @@ qsa_status check_paged(const void* q, const void* kcache, const int32_t* page_ta
     REQUIRE(pt_stride >= ceil_div(max_visible, kpp) && pt_stride >= 1, QSA_ERR_INVALID_ARGUMENT,
             "pt_stride (%lld) must be >= ceil(max_visible / keys_per_page) = %lld", (long long)pt_stride,
             (long long)ceil_div(max_visible, kpp));
+    REQUIRE((int64_t)num_pages * kpp <= (int64_t)UINT32_MAX, QSA_ERR_UNSUPPORTED,
+            "num_pages * keys_per_page (%lld) exceeds 2^32 keys", (long long)num_pages * kpp);
     if (rows == 0) return QSA_OK;
     REQUIRE(q && kcache && page_table && pos, QSA_ERR_INVALID_ARGUMENT,
             "null pointer: q=%p kcache=%p page_table=%p pos=%p", q, kcache, (const void*)page_table,
@@ -143,11 +154,70 @@ size_t two_pass_bytes(int32_t rows, int32_t max_visible) {
     return (size_t)rows * (size_t)two_pass_ld(max_visible) * sizeof(float);
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Fused arm: sample scores, per-row threshold and candidate count, candidate lists.
+struct FusedLayout {
+    qsa::FusedPlan plan;
+    size_t off_samp, off_thresh, off_count, off_cand, total;
+};
+
+FusedLayout fused_layout(int32_t rows, int32_t max_visible, int32_t kb) {
+    FusedLayout L;
+    L.plan = qsa::plan_fused(max_visible, kb);
+    size_t o = 0;
+    L.off_samp = o;
+    o = align256(o + (size_t)rows * (size_t)L.plan.ld_s * sizeof(float));
+    L.off_thresh = o;
+    o = align256(o + (size_t)rows * sizeof(uint64_t));
+    L.off_count = o;
+    o = align256(o + (size_t)rows * sizeof(int32_t));
+    L.off_cand = o;
+    o = align256(o + (size_t)rows * (size_t)L.plan.cand_cap * sizeof(uint64_t));
+    L.total = o;
+    return L;
+}
+
+enum class Path { TwoPass, Fused };
+
+// The fused arm scores every key twice over a 1/16 sample but never writes
+// the score matrix; it pays off when many rows share each request's keys.
+// Few rows per request (decode) stream each key once through the two-pass arm.
+Path choose_path(int32_t rows, int32_t num_reqs, int32_t max_visible) {
+    const char* f = getenv("QSA_FORCE_PATH");
+    if (f && strcmp(f, "two_pass") == 0) return Path::TwoPass;
+    if (f && strcmp(f, "fused") == 0) return Path::Fused;
+    if (max_visible <= 0) return Path::TwoPass;
+    return (rows / (num_reqs > 0 ? num_reqs : 1) >= 32) ? Path::Fused : Path::TwoPass;
+}
+
+bool force_fallback() {
+    const char* f = getenv("QSA_DEBUG_FORCE_FALLBACK");
+    return f && f[0] == '1';
+}
+
+int device_cus() {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return cus;
+}
+
 }  // namespace
 
 QSA_EXPORT const char* qsa_last_error(void) { return g_err; }
 QSA_EXPORT const char* qsa_last_path(void) { return g_path; }
 QSA_EXPORT const char* qsa_version(void) { return "qsa-mi355x 0.1.0 (gfx950)"; }
+
+QSA_EXPORT qsa_status qsa_debug_record_events(void* const* events, int32_t n) {
+    g_err[0] = 0;
+    REQUIRE(n >= 0 && (events != nullptr || n == 0), QSA_ERR_INVALID_ARGUMENT, "bad event list");
+    g_events = n > 0 ? events : nullptr;
+    g_nevents = n;
+    g_recorded = 0;
+    return QSA_OK;
+}
+
+QSA_EXPORT int32_t qsa_debug_events_recorded(void) { return g_recorded; }
 
 QSA_EXPORT qsa_status qsa_score_paged(const void* q, const void* kcache, const int32_t* page_table,
                                       int64_t pt_stride, int32_t num_pages, int32_t num_reqs,
@@ -215,11 +285,10 @@ QSA_EXPORT qsa_status qsa_topk_rows(const float* scores, int64_t ld_scores, cons
 
 QSA_EXPORT size_t qsa_select_paged_tokens_workspace_size(int32_t rows, int32_t num_reqs, int32_t max_visible,
                                                          int32_t compress_ratio, int32_t k, uint32_t flags) {
-    (void)num_reqs;
-    (void)compress_ratio;
-    (void)k;
-    (void)flags;
-    if (rows <= 0 || max_visible <= 0) return 0;
+    if (rows <= 0 || max_visible <= 0 || k < 1 || compress_ratio < 1) return 0;
+    const int32_t kb = (flags & QSA_OUT_KEYS) ? k : k / compress_ratio;
+    if (kb < 1) return 0;
+    if (choose_path(rows, num_reqs, max_visible) == Path::Fused) return fused_layout(rows, max_visible, kb).total;
     return two_pass_bytes(rows, max_visible);
 }
 
@@ -231,6 +300,7 @@ QSA_EXPORT qsa_status qsa_select_paged_tokens(const void* q, const void* kcache,
                                               uint32_t flags, int32_t* out, void* workspace,
                                               size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
+    g_recorded = 0;
     qsa_status st = check_paged(q, kcache, page_table, pt_stride, num_pages, num_reqs, pos, rows, heads,
                                 head_dim, page_size, compress_ratio, max_visible);
     if (st != QSA_OK) return st;
@@ -256,9 +326,6 @@ QSA_EXPORT qsa_status qsa_select_paged_tokens(const void* q, const void* kcache,
 
     qsa::PagedArgs a = make_paged(q, kcache, page_table, pt_stride, num_pages, num_reqs, row_req, pos, rows,
                                   page_size, compress_ratio, max_visible, flags);
-    float* scores = static_cast<float*>(workspace);
-    const int64_t ld = two_pass_ld(max_visible);
-    if (max_visible > 0) HIP_CHECK(qsa::launch_score_paged(a, scores, ld, s));
     qsa::VisibleSource vs;
     vs.visible = nullptr;
     vs.pos = pos;
@@ -266,7 +333,36 @@ QSA_EXPORT qsa_status qsa_select_paged_tokens(const void* q, const void* kcache,
     vs.num_reqs = num_reqs;
     vs.cr = compress_ratio;
     vs.max_visible = max_visible;
-    HIP_CHECK(qsa::launch_topk_rows(scores, ld, vs, rows, kb, out_keys ? 1 : compress_ratio, k, out, s));
+    const int32_t expand = out_keys ? 1 : compress_ratio;
+    if (choose_path(rows, num_reqs, max_visible) == Path::Fused) {
+        const FusedLayout L = fused_layout(rows, max_visible, kb);
+        unsigned char* w = static_cast<unsigned char*>(workspace);
+        float* samp = reinterpret_cast<float*>(w + L.off_samp);
+        uint64_t* thresh = reinterpret_cast<uint64_t*>(w + L.off_thresh);
+        int32_t* count = reinterpret_cast<int32_t*>(w + L.off_count);
+        uint64_t* cand = reinterpret_cast<uint64_t*>(w + L.off_cand);
+        const int cus = device_cus();
+        HIP_CHECK(mark(s));
+        HIP_CHECK(qsa::launch_score_store(a, L.plan.stride, samp, L.plan.ld_s, cus, s));
+        HIP_CHECK(mark(s));
+        HIP_CHECK(qsa::launch_sample_threshold(samp, L.plan.ld_s, vs, L.plan, force_fallback(), thresh, count, rows, s));
+        HIP_CHECK(mark(s));
+        HIP_CHECK(qsa::launch_score_filter(a, thresh, cand, count, L.plan.cand_cap, cus, s));
+        HIP_CHECK(mark(s));
+        HIP_CHECK(qsa::launch_fused_final(a, vs, L.plan, cand, count, kb, expand, k, out, s));
+        HIP_CHECK(mark(s));
+        g_events = nullptr;
+        g_path = "fused";
+        return QSA_OK;
+    }
+    float* scores = static_cast<float*>(workspace);
+    const int64_t ld = two_pass_ld(max_visible);
+    HIP_CHECK(mark(s));
+    if (max_visible > 0) HIP_CHECK(qsa::launch_score_paged(a, scores, ld, s));
+    HIP_CHECK(mark(s));
+    HIP_CHECK(qsa::launch_topk_rows(scores, ld, vs, rows, kb, expand, k, out, s));
+    HIP_CHECK(mark(s));
+    g_events = nullptr;
     g_path = "two_pass";
     return QSA_OK;
 }

@@ -1,17 +1,19 @@
 // qsa_device.hpp -- device-side building blocks shared by the gfx950 kernels.
 //
 // The score of (row r, key j) is computed in exactly one way by every kernel
-// of this library, so that the scorer, the fused selectors and the decode
-// path all produce the same bits:
-//   * one v_mfma_f32_16x16x32_f16 per 32-wide slice of the 128-dim head, four
-//     slices in order d = 0..31, 32..63, 64..95, 96..127, accumulating into
-//     an fp32 accumulator that starts at +0;
-//   * inside a slice, lane group g = lane/16 supplies dims 8g..8g+7 of the
-//     slice for both operands (the A operand is the query head, the B
-//     operand the key);
-//   * the MFMA output row m = 4*row + head, so each lane's four accumulator
-//     values are the four head dots of one (row, key) pair, and the head sum
-//     ((h0 + h1) + h2) + h3 is lane-local.
+// of this library, so that the scorer, the fused selectors and the fallback
+// paths all produce the same bits.  All of them use v_mfma_f32_32x32x16_f16
+// (the full-rate fp16 MFMA shape of gfx950) with MFMA row m = 4*row + head
+// (8 query rows x 4 heads per 32-row tile) and the key as the column.  A
+// chain of 8 MFMAs over head-dim slices s = 0..7 (lane half g = lane/32
+// supplies dims 16s+8g .. 16s+8g+7 of both operands), accumulating in fp32
+// from +0, gives every head's dot.  The 32x32 output layout puts rows
+// 8*(v/4) + 4*(l/32) + (v%4) of column l%32 in accumulator element v of lane
+// l, so each group of four elements is the four heads of one (row, key) and
+// the head reduction is lane-local:
+//   default form: ((h0 + h1) + h2) + h3;
+//   relu form:    ((relu h0 + relu h1) + relu h2) + relu h3, times the fp32
+//                 value nearest 1/sqrt(128).
 // Sources: "[Perf][Qwen4Exp] Admit the cuBLAS QSA indexer and exact top-k on
 // Turing", section "Purpose" (FP16 inputs, FP32 accumulation) and "Test Plan"
 // (4 index heads, head dim 128); "spec(MODEL-MM-QWEN4-EXP): Qwen3.8-Flash-Next
@@ -27,11 +29,14 @@ namespace qsa {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kHeads = 4;
 constexpr int kHeadDim = 128;
 constexpr int kKeyBytes = kHeadDim * 2;        // 256 B per compressed key
 constexpr int kChunksPerKey = kKeyBytes / 16;  // 16-byte chunks per key
+constexpr int kSlices = kHeadDim / 16;         // K-slices of one head per 32x32x16 MFMA chain
 
 // fp32 nearest 1/sqrt(128) = 2^-3.5 (bit pattern 0x3DB504F3).
 constexpr float kRsqrtHeadDim = 0x1.6a09e6p-4f;
@@ -53,6 +58,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of order_key (for keys produced by it).
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // 64-bit selection key: score key in the high word, inverted index in the low
 // word, so that a larger composite means "higher score, then lower index".
 __device__ __forceinline__ uint64_t compose(uint32_t key, uint32_t j) {
@@ -62,27 +72,26 @@ __device__ __forceinline__ uint32_t composite_index(uint64_t c) {
     return 0xFFFFFFFFu - (uint32_t)(c & 0xFFFFFFFFull);
 }
 
-__device__ __forceinline__ float4v mfma16(half8 a, half8 b, float4v c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ float16v mfma32(half8 a, half8 b, float16v c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// Head reduction of one lane's accumulator (acc[v] = head v's dot).
+// The four head dots of one (row, key) -> score.
 template <bool RELU>
-__device__ __forceinline__ float combine_heads(float4v acc) {
-    if (RELU) {
-        float h0 = fmaxf(acc[0], 0.0f), h1 = fmaxf(acc[1], 0.0f);
-        float h2 = fmaxf(acc[2], 0.0f), h3 = fmaxf(acc[3], 0.0f);
-        float s = ((h0 + h1) + h2) + h3;
-        return s * kRsqrtHeadDim;
-    } else {
-        return ((acc[0] + acc[1]) + acc[2]) + acc[3];
-    }
+__device__ __forceinline__ float combine_heads(float h0, float h1, float h2, float h3) {
+    if (!RELU) return ((h0 + h1) + h2) + h3;
+    h0 = fmaxf(h0, 0.0f);
+    h1 = fmaxf(h1, 0.0f);
+    h2 = fmaxf(h2, 0.0f);
+    h3 = fmaxf(h3, 0.0f);
+    const float s = ((h0 + h1) + h2) + h3;
+    return s * kRsqrtHeadDim;
 }
 
 // Byte offset of 16-byte chunk c of key n inside an LDS key tile (256 B per
-// key).  The chunk index is XOR-swizzled with the key's low 4 bits so that the
-// 16 lanes of an MFMA lane group, which read the same chunk of 16 different
-// keys, hit 16 different bank groups.
+// key).  The chunk index is XOR-swizzled with the key's low 4 bits so that 16
+// consecutive lanes, which read the same chunk of 16 consecutive keys, hit 16
+// different bank groups.
 __device__ __forceinline__ int lds_key_chunk(int n, int c) {
     return n * kKeyBytes + ((c ^ (n & 15)) << 4);
 }

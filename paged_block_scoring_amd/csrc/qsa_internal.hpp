@@ -28,6 +28,14 @@ struct PagedArgs {
 // Scorer: writes scores[r*ld + j] for j < V_r.
 hipError_t launch_score_paged(const PagedArgs& a, float* scores, int64_t ld, hipStream_t stream);
 
+// Scorer over logical keys i (key stride*i): out[r*ld + i] for i < ceil(V_r/stride).
+hipError_t launch_score_store(const PagedArgs& a, int32_t stride, float* out, int64_t ld, int32_t cus,
+                              hipStream_t stream);
+
+// Scorer that appends every composite >= thresh[r] to row r's candidate list.
+hipError_t launch_score_filter(const PagedArgs& a, const uint64_t* thresh, uint64_t* cand, int32_t* cand_count,
+                               int32_t cand_cap, int32_t cus, hipStream_t stream);
+
 // Where a selector takes each row's candidate count from.
 struct VisibleSource {
     const int32_t* visible;  // explicit counts, or
@@ -44,5 +52,23 @@ struct VisibleSource {
 hipError_t launch_topk_rows(const float* scores, int64_t ld, const VisibleSource& vis, int32_t rows,
                             int32_t kk, int32_t expand, int32_t out_len, int32_t* out,
                             hipStream_t stream);
+
+// Sizes of the fused arm for one call.
+struct FusedPlan {
+    int32_t stride;    // sampling stride
+    int32_t m;         // rank of the sample composite used as threshold
+    int32_t capl;      // LDS candidate capacity of the final kernel
+    int32_t cand_cap;  // candidate list capacity per row
+    int64_t ld_s;      // row stride of the sample scores
+};
+FusedPlan plan_fused(int32_t max_visible, int32_t kb);
+
+hipError_t launch_sample_threshold(const float* samp, int64_t ld_s, const VisibleSource& vis, const FusedPlan& f,
+                                   bool force_fallback, uint64_t* thresh, int32_t* cand_count, int32_t rows,
+                                   hipStream_t stream);
+
+hipError_t launch_fused_final(const PagedArgs& a, const VisibleSource& vis, const FusedPlan& f, const uint64_t* cand,
+                              const int32_t* cand_count, int32_t kb, int32_t expand, int32_t out_len, int32_t* out,
+                              hipStream_t stream);
 
 }  // namespace qsa

@@ -1,171 +1,68 @@
-// score.hip -- paged MQA index scorer on gfx950 MFMA (fp16 inputs, fp32
-// accumulation), writing one fp32 score per (row, visible key).
-//
-// Sources: "[Perf][Qwen4Exp] Admit the cuBLAS QSA indexer and exact top-k on
-// Turing", section "Purpose" (the scorer is an FP16 product with FP32
-// accumulation followed by an epilogue; the paged scorer reads keys through
-// the page table) and "Test Plan" (4 index heads, head dim 128, compress
-// ratio 4); "spec(MODEL-MM-QWEN4-EXP) ...", section "The component
-// deep-dives, and two corrections to the above" (one key per ratio tokens
-// shared by all index heads; one score per query token, summed over heads).
-//
-// Work decomposition.  A workgroup of 4 waves owns a tile of TR = 16*MT
-// consecutive rows and a chunk of `chunk` consecutive key indices.  Wave w
-// holds the query fragments of MT groups of 4 rows (16 MFMA rows: 4 rows x 4
-// heads) in registers for the whole chunk.  Keys are staged 64 at a time in
-// LDS (16 KB): each 16-byte chunk of a key is fetched by one thread through
-// the page table, so a page's keys are read as contiguous 4 KB runs, and
-// stored XOR-swizzled.  Each wave then runs 4 MFMAs (K = 128) per 16 keys per
-// row group, sums the heads in registers and writes the visible scores.
-// Rows of different requests in one tile are handled in successive passes
-// over the chunk, one request per pass.
-#include "qsa_device.hpp"
+// score.hip -- launchers of the tiled scoring kernel (score_core.hpp): the
+// materialising scorer behind qsa_score_paged and the two-pass arm, the
+// strided sampling pass and the filtering pass of the fused arm.
 #include "qsa_internal.hpp"
+#include "score_core.hpp"
 
 namespace qsa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kTileKeys = 64;
-
-template <int MT, bool RELU>
-__global__ __launch_bounds__(kThreads) void score_paged_kernel(PagedArgs a, float* __restrict__ scores,
-                                                               int64_t ld, int32_t chunk) {
-    constexpr int TR = 4 * MT * kWaves;
-    __shared__ __attribute__((aligned(16))) unsigned char s_keys[kTileKeys * kKeyBytes];
-    __shared__ int64_t s_keyoff[kTileKeys];
-    __shared__ int32_t s_req[TR], s_vis[TR], s_todo[TR], s_active[TR];
-    __shared__ int32_t s_act, s_vmax;
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int r0 = blockIdx.x * TR;
-    const int c0 = blockIdx.y * chunk;
-    if (c0 >= a.max_visible) return;
-    const int c1 = min(c0 + chunk, a.max_visible);
-
-    if (tid < TR) {
-        int r = r0 + tid, req = -1, vis = 0;
-        if (r < a.rows) {
-            req = a.row_req ? a.row_req[r] : 0;
-            if (req < 0 || req >= a.num_reqs) req = -1;
-            else vis = visible_keys(a.pos[r], a.cr, a.max_visible);
-        }
-        s_req[tid] = req;
-        s_vis[tid] = vis;
-        s_todo[tid] = (req >= 0 && vis > c0) ? 1 : 0;
-    }
-    __syncthreads();
-
-    for (;;) {
-        // One pass per distinct request among the tile's rows that still have
-        // visible keys in this chunk.
-        if (tid == 0) {
-            int act = -1, vmax = 0;
-            for (int t = 0; t < TR; ++t)
-                if (s_todo[t]) { act = s_req[t]; break; }
-            for (int t = 0; t < TR; ++t) {
-                int on = (act >= 0 && s_todo[t] && s_req[t] == act) ? 1 : 0;
-                s_active[t] = on;
-                if (on) { s_todo[t] = 0; vmax = max(vmax, s_vis[t]); }
-            }
-            s_act = act;
-            s_vmax = vmax;
-        }
-        __syncthreads();
-        const int act = s_act;
-        if (act < 0) break;
-        const int cend = min(c1, s_vmax);
-
-        half8 qa[MT][4];
-        int lim[MT];     // keys this lane may write for its output row (0: none)
-        int orow[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int tr_a = wave * 4 * MT + 4 * mt + ((lane & 15) >> 2);
-            const int h = lane & 3;
-            const int r = r0 + tr_a;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                half8 v = {};
-                if (r < a.rows)
-                    v = *reinterpret_cast<const half8*>(a.q + ((int64_t)r * kHeads + h) * kHeadDim + 32 * s +
-                                                        8 * (lane >> 4));
-                qa[mt][s] = v;
-            }
-            const int tr_o = wave * 4 * MT + 4 * mt + (lane >> 4);
-            orow[mt] = r0 + tr_o;
-            lim[mt] = s_active[tr_o] ? min(s_vis[tr_o], c1) : 0;
-        }
-
-        const int32_t* ptrow = a.page_table + (int64_t)act * a.pt_stride;
-        for (int j0 = c0; j0 < cend; j0 += kTileKeys) {
-            if (tid < kTileKeys) {
-                const int j = j0 + tid;
-                int64_t off = -1;
-                if (j < cend) {
-                    const int lp = j / a.kpp;
-                    const int slot = j - lp * a.kpp;
-                    int p = ptrow[lp];
-                    p = min(max(p, 0), a.num_pages - 1);
-                    off = ((int64_t)p * a.kpp + slot) * kHeadDim;
-                }
-                s_keyoff[tid] = off;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int i = 0; i < kTileKeys * kChunksPerKey / kThreads; ++i) {
-                const int flat = i * kThreads + tid, n = flat >> 4, c = flat & 15;
-                const int64_t off = s_keyoff[n];
-                uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (off >= 0) v = *reinterpret_cast<const uint4*>(a.kcache + off + c * 8);
-                *reinterpret_cast<uint4*>(s_keys + lds_key_chunk(n, c)) = v;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int nt = 0; nt < kTileKeys / 16; ++nt) {
-                const int n = nt * 16 + (lane & 15);
-                half8 kb[4];
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    kb[s] = *reinterpret_cast<const half8*>(s_keys + lds_key_chunk(n, 4 * s + (lane >> 4)));
-                const int j = j0 + n;
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) acc = mfma16(qa[mt][s], kb[s], acc);
-                    if (j < lim[mt]) scores[(int64_t)orow[mt] * ld + j] = combine_heads<RELU>(acc);
-                }
-            }
-            __syncthreads();
-        }
-    }
+// Even shares of each XCD's (tile, key) positions: about `wg_per_cu`
+// workgroups per compute unit, but no share below `min_seg` positions.
+template <bool RELU, Epi EPI>
+hipError_t launch_form(ScoreKernelArgs A, int32_t cus, int32_t wg_per_cu, int64_t min_seg, hipStream_t stream) {
+    using S = ScoreShape;
+    A.tiles = (A.a.rows + kTileRows - 1) / kTileRows;
+    const int64_t stripe = ((int64_t)(A.lmax + kXcds - 1) / kXcds + kStepKeys - 1) / kStepKeys * kStepKeys;
+    A.xcd_keys = (int32_t)stripe;
+    const int64_t positions = (int64_t)A.tiles * stripe;
+    int64_t per_xcd = (int64_t)(cus / kXcds > 0 ? cus / kXcds : 1) * wg_per_cu;
+    int64_t seg = (positions + per_xcd - 1) / per_xcd;
+    if (seg < min_seg) seg = min_seg;
+    per_xcd = (positions + seg - 1) / seg;
+    A.seg_len = seg;
+    score_tiles_kernel<RELU, EPI><<<dim3((unsigned)(kXcds * per_xcd)), S::NT, 0, stream>>>(A);
+    return hipGetLastError();
 }
 
-template <int MT>
-hipError_t launch_mt(const PagedArgs& a, float* scores, int64_t ld, hipStream_t stream) {
-    constexpr int TR = 16 * MT;
-    int64_t chunk = 1024;
-    const int64_t min_chunk = ((int64_t)a.max_visible + 65534) / 65535;
-    if (chunk < min_chunk) chunk = (min_chunk + kTileKeys - 1) / kTileKeys * kTileKeys;
-    dim3 grid((unsigned)((a.rows + TR - 1) / TR), (unsigned)((a.max_visible + chunk - 1) / chunk));
-    if (a.relu)
-        score_paged_kernel<MT, true><<<grid, kThreads, 0, stream>>>(a, scores, ld, (int32_t)chunk);
-    else
-        score_paged_kernel<MT, false><<<grid, kThreads, 0, stream>>>(a, scores, ld, (int32_t)chunk);
-    return hipGetLastError();
+template <Epi EPI>
+hipError_t launch_epi(const ScoreKernelArgs& A, int32_t cus, hipStream_t stream) {
+    if (A.a.relu) return launch_form<true, EPI>(A, cus, 2, 256, stream);
+    return launch_form<false, EPI>(A, cus, 2, 256, stream);
 }
 
 }  // namespace
 
-hipError_t launch_score_paged(const PagedArgs& a, float* scores, int64_t ld, hipStream_t stream) {
+hipError_t launch_score_store(const PagedArgs& a, int32_t stride, float* out, int64_t ld, int32_t cus,
+                              hipStream_t stream) {
     if (a.rows <= 0 || a.max_visible <= 0) return hipSuccess;
-    // Many rows per request: 64-row tiles share every staged key tile.
-    // Few rows per request (decode): 16-row tiles keep the grid wide.
-    const int64_t rows_per_req = a.rows / (a.num_reqs > 0 ? a.num_reqs : 1);
-    if (rows_per_req >= 32) return launch_mt<4>(a, scores, ld, stream);
-    return launch_mt<1>(a, scores, ld, stream);
+    ScoreKernelArgs A = {};
+    A.a = a;
+    A.stride = stride;
+    A.lmax = (a.max_visible + stride - 1) / stride;
+    A.out = out;
+    A.ld = ld;
+    return launch_epi<Epi::Store>(A, cus, stream);
+}
+
+hipError_t launch_score_paged(const PagedArgs& a, float* scores, int64_t ld, hipStream_t stream) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    return launch_score_store(a, 1, scores, ld, cus, stream);
+}
+
+hipError_t launch_score_filter(const PagedArgs& a, const uint64_t* thresh, uint64_t* cand, int32_t* cand_count,
+                               int32_t cand_cap, int32_t cus, hipStream_t stream) {
+    if (a.rows <= 0 || a.max_visible <= 0) return hipSuccess;
+    ScoreKernelArgs A = {};
+    A.a = a;
+    A.stride = 1;
+    A.lmax = a.max_visible;
+    A.thresh = thresh;
+    A.cand = cand;
+    A.cand_count = cand_count;
+    A.cand_cap = cand_cap;
+    return launch_epi<Epi::Filter>(A, cus, stream);
 }
 
 }  // namespace qsa

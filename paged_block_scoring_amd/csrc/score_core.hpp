@@ -1,0 +1,340 @@
+// score_core.hpp -- the tiled paged MQA scoring kernel shared by every arm.
+//
+// Sources: "[Perf][Qwen4Exp] Admit the cuBLAS QSA indexer and exact top-k on
+// Turing", sections "Purpose" (FP16 product with FP32 accumulation and an
+// epilogue; a paged scorer reading keys through the page table) and "Test
+// Plan" (4 index heads, head dim 128, compress ratio 4); "spec(MODEL-MM-QWEN4-
+// EXP) ...", section "The component deep-dives, and two corrections to the
+// above" (one key per ratio tokens shared by all heads; one score per query
+// token summed over heads).
+//
+// Work.  Rows are cut into tiles of 64 consecutive rows; the logical keys
+// (logical key i is key stride*i of the request; stride is 1 except for the
+// sampling pass) are cut into 8 stripes, one per XCD.  Workgroup w runs on
+// XCD w % 8 (the hardware's round-robin dispatch) and owns a contiguous,
+// equal share of that XCD's (tile, key) positions, so every XCD streams only
+// its stripe of keys (which stays in its L2) and every workgroup does the
+// same amount of work.  A share is processed as pieces of one tile and a key
+// range.
+//
+// A piece.  Each wave holds the fp16 query fragments of its rows in
+// registers.  Keys are staged 32 at a time: a per-piece table gives every
+// logical key's slot in the cache; each thread prefetches its 16-byte pieces
+// of the next 32 keys into registers while the current ones are consumed from
+// one half of a double-buffered, XOR-swizzled LDS tile (one barrier per 32
+// keys).  Per 8 rows x 4 heads a chain of 8 MFMAs (32x32x16) gives 32 keys'
+// head dots; each lane reduces its four heads to a score, which goes to the
+// epilogue:
+//   Store  -- out[row*ld + i] = score (two-pass arm, sampling pass);
+//   Filter -- keep the composite (score, key) if it is >= the row's
+//             threshold: one compare per score; the rare candidates get
+//             slots from wave-uniform per-row counters (ballot + mbcnt),
+//             are staged per row in LDS and appended to the row's global
+//             list with one atomic per row and piece.
+// Rows of different requests in one tile are processed in successive passes.
+#pragma once
+
+#include "qsa_device.hpp"
+#include "qsa_internal.hpp"
+
+namespace qsa {
+
+enum class Epi { Store, Filter };
+
+constexpr int kStepKeys = 32;    // keys per LDS stage
+constexpr int kMaxPiece = 2048;  // logical keys per piece (slot-table size)
+constexpr int kLCap = 32;        // per-row LDS staging slots of the Filter epilogue
+constexpr int kTileRows = 64;    // rows per tile
+constexpr int kXcds = 8;         // XCDs of an MI355X (256 CUs = 8 x 32)
+
+struct ScoreKernelArgs {
+    PagedArgs a;
+    int32_t stride;    // logical key i is key stride*i
+    int32_t lmax;      // logical keys of the longest row: ceil(max_visible / stride)
+    int32_t tiles;     // ceil(rows / kTileRows)
+    int32_t xcd_keys;  // logical keys per XCD stripe
+    int64_t seg_len;   // (tile, key) positions per workgroup
+    // Store
+    float* out;
+    int64_t ld;
+    // Filter
+    const uint64_t* thresh;  // [rows]
+    uint64_t* cand;          // [rows][cand_cap]
+    int32_t* cand_count;     // [rows]
+    int32_t cand_cap;
+};
+
+struct ScoreShape {
+    static constexpr int WAVES = 4;
+    static constexpr int NT = 64 * WAVES;
+    static constexpr int RPW = kTileRows / WAVES;                    // rows per wave (two 8-row MFMA tiles)
+    static constexpr int NLOAD = kStepKeys * kChunksPerKey / NT;     // 16-byte pieces per thread per stage
+    static constexpr int NOUT = 8;                                   // scores per lane per 32 keys
+};
+
+// Tile row (0..63) of this lane's output o = 4*mt + g: MFMA tile mt of the
+// wave, element group g (rows 8*g/2.. of the 32 MFMA rows = query row 2g + l/32).
+__device__ __forceinline__ int out_tile_row(int o, int wave, int lane) {
+    return wave * 16 + (o >> 2) * 8 + 2 * (o & 3) + (lane >> 5);
+}
+
+// Filter epilogue for one output index o of a wave: `c` is this lane's
+// exact keep decision for (tile row tr, key jn).  The two 32-lane halves of
+// the wave hold two different rows, each owned by this wave alone, so the
+// slot of a kept composite is the row's running count (a wave-uniform value)
+// plus the lane's rank among the kept lanes of its half; no atomics.
+__device__ __forceinline__ void filter_append(const ScoreKernelArgs& A, bool c, float sc, int tr, int r0, int jn,
+                                              int lane, int& cnt_lo, int& cnt_hi, uint64_t* s_lbuf) {
+    const uint64_t m = __ballot(c);
+    if (m == 0ull) return;
+    const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+    const bool upper = lane >= 32;
+    const int rank = (int)__builtin_amdgcn_mbcnt_hi(upper ? hi : 0u, __builtin_amdgcn_mbcnt_lo(upper ? 0u : lo, 0u));
+    const int slot = (upper ? cnt_hi : cnt_lo) + rank;
+    cnt_lo += __popc(lo);
+    cnt_hi += __popc(hi);
+    if (c) {
+        const uint64_t comp = compose(order_key(sc), (uint32_t)jn);
+        if (slot < kLCap) {
+            s_lbuf[tr * kLCap + slot] = comp;
+        } else {
+            const int g = atomicAdd(&A.cand_count[r0 + tr], 1);
+            if (g < A.cand_cap) A.cand[(int64_t)(r0 + tr) * A.cand_cap + g] = comp;
+        }
+    }
+}
+
+template <bool RELU, Epi EPI>
+__global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKernelArgs A) {
+    using S = ScoreShape;
+    constexpr int NT = S::NT, NOUT = S::NOUT;
+    constexpr bool FILTER = EPI == Epi::Filter;
+
+    __shared__ __attribute__((aligned(16))) unsigned char s_keys[2][kStepKeys * kKeyBytes];
+    __shared__ uint32_t s_slot[kMaxPiece];
+    __shared__ int32_t s_req[kTileRows], s_lv[kTileRows], s_todo[kTileRows], s_lim[kTileRows];
+    __shared__ __attribute__((aligned(16))) float s_fT[FILTER ? kTileRows : 1];
+    __shared__ int32_t s_jT[FILTER ? kTileRows : 1];
+    __shared__ int32_t s_lc[FILTER ? kTileRows : 1];
+    __shared__ uint64_t s_lbuf[FILTER ? kTileRows * kLCap : 1];
+    __shared__ int32_t s_act, s_vmax;
+
+    const PagedArgs& a = A.a;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int xcd = blockIdx.x % kXcds, loc = blockIdx.x / kXcds;
+    const int xk0 = xcd * A.xcd_keys;
+    const int span = min(A.xcd_keys, A.lmax - xk0);
+    if (span <= 0) return;
+    const int64_t total = (int64_t)A.tiles * span;
+    int64_t p = (int64_t)loc * A.seg_len;
+    const int64_t pend = min(p + A.seg_len, total);
+
+    while (p < pend) {
+        const int tile = (int)(p / span);
+        const int off = (int)(p - (int64_t)tile * span);
+        const int len = (int)min<int64_t>(min<int64_t>((int64_t)(span - off), pend - p), (int64_t)kMaxPiece);
+        const int c0 = xk0 + off, c1 = c0 + len;
+        p += len;
+        const int r0 = tile * kTileRows;
+
+        for (int t = tid; t < kTileRows; t += NT) {
+            const int r = r0 + t;
+            int req = -1, lv = 0;
+            if (r < a.rows) {
+                req = a.row_req ? a.row_req[r] : 0;
+                if (req < 0 || req >= a.num_reqs) {
+                    req = -1;
+                } else {
+                    const int v = visible_keys(a.pos[r], a.cr, a.max_visible);
+                    lv = (v + A.stride - 1) / A.stride;
+                }
+            }
+            s_req[t] = req;
+            s_lv[t] = lv;
+            s_todo[t] = (req >= 0 && lv > c0) ? 1 : 0;
+            if (FILTER) {
+                float fT = 0.0f;
+                int jT = 0;
+                if (req >= 0 && lv > c0) {
+                    // threshold composite -> (score, index); 0 means "keep all"
+                    const uint64_t T = A.thresh[r];
+                    fT = key_to_float((uint32_t)(T >> 32));
+                    jT = (int)(0xFFFFFFFFu - (uint32_t)T);
+                    if (T == 0ull) {
+                        fT = -__builtin_huge_valf();
+                        jT = 0x7FFFFFFF;
+                    }
+                }
+                s_fT[t] = fT;
+                s_jT[t] = jT;
+            }
+        }
+        __syncthreads();
+
+        // kept-candidate counts of this wave's 16 rows (output o, lane half)
+        int cnt_lo[ScoreShape::NOUT], cnt_hi[ScoreShape::NOUT];
+#pragma unroll
+        for (int o = 0; o < ScoreShape::NOUT; ++o) cnt_lo[o] = cnt_hi[o] = 0;
+
+        for (;;) {
+            // one pass per request present among the tile's pending rows
+            // (smallest request id first): wave 0 elects it and marks the rows
+            if (wave == 0) {
+                int best = 0x7FFFFFFF;
+                for (int t = lane; t < kTileRows; t += 64)
+                    if (s_todo[t]) best = min(best, s_req[t]);
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o, 64));
+                int vmax = 0;
+                for (int t = lane; t < kTileRows; t += 64) {
+                    const bool on = s_todo[t] && s_req[t] == best;
+                    s_lim[t] = on ? min(s_lv[t], c1) : 0;
+                    if (on) {
+                        s_todo[t] = 0;
+                        vmax = max(vmax, s_lv[t]);
+                    }
+                }
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) vmax = max(vmax, __shfl_xor(vmax, o, 64));
+                if (lane == 0) {
+                    s_act = best == 0x7FFFFFFF ? -1 : best;
+                    s_vmax = vmax;
+                }
+            }
+            __syncthreads();
+            const int act = s_act;
+            if (act < 0) break;
+            const int cend = min(c1, s_vmax);
+
+            const int32_t* ptrow = a.page_table + (int64_t)act * a.pt_stride;
+            for (int i = tid; i < cend - c0; i += NT) {
+                const int j = (c0 + i) * A.stride;
+                const int lp = j / a.kpp;
+                const int slot = j - lp * a.kpp;
+                const int pg = min(max(ptrow[lp], 0), a.num_pages - 1);
+                s_slot[i] = (uint32_t)pg * (uint32_t)a.kpp + (uint32_t)slot;
+            }
+
+            // query fragments: MFMA tile mt of this wave holds rows
+            // r0 + 16*wave + 8*mt .. +7, MFMA row m = 4*(row offset) + head
+            half8 qa[2 * kSlices];
+#pragma unroll
+            for (int t = 0; t < 2 * kSlices; ++t) {
+                const int mt = t / kSlices, s = t % kSlices, m = lane & 31;
+                const int row = r0 + wave * 16 + mt * 8 + (m >> 2);
+                const int h = m & 3;
+                half8 v = {};
+                if (row < a.rows)
+                    v = *reinterpret_cast<const half8*>(a.q + ((int64_t)row * kHeads + h) * kHeadDim + 16 * s +
+                                                        8 * (lane >> 5));
+                qa[t] = v;
+            }
+            // smallest visible bound over this wave's rows: steps entirely
+            // below it need no per-row mask
+            int wlim = 0x7FFFFFFF;
+            for (int t = lane; t < S::RPW; t += 64) wlim = min(wlim, s_lim[wave * S::RPW + t]);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) wlim = min(wlim, __shfl_xor(wlim, o, 64));
+            __syncthreads();
+
+            float fT[NOUT];
+#pragma unroll
+            for (int o = 0; o < NOUT; ++o) fT[o] = FILTER ? s_fT[out_tile_row(o, wave, lane)] : 0.0f;
+
+            // Step i: barrier (tile i staged) -> issue the loads of tile i+1
+            // -> MFMAs on tile i -> wait for tile i+1 and stage it in the other
+            // buffer -> epilogue of tile i.  The epilogue's global stores are
+            // issued after the wait, so they drain during the next step's
+            // MFMAs instead of being waited on.
+            const _Float16* kc = a.kcache;
+            u32x4 pf[S::NLOAD];
+#pragma unroll
+            for (int i = 0; i < S::NLOAD; ++i) {
+                const int flat = i * NT + tid, n = flat >> 4, c = flat & 15;
+                const int li = min(c0 + n, cend - 1) - c0;
+                pf[i] = *reinterpret_cast<const u32x4*>(kc + (size_t)s_slot[li] * kHeadDim + c * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < S::NLOAD; ++i) {
+                const int flat = i * NT + tid, n = flat >> 4, c = flat & 15;
+                *reinterpret_cast<u32x4*>(s_keys[0] + lds_key_chunk(n, c)) = pf[i];
+            }
+            int buf = 0;
+            for (int j0 = c0; j0 < cend; j0 += kStepKeys) {
+                __syncthreads();
+                const unsigned char* sk = s_keys[buf];
+#pragma unroll
+                for (int i = 0; i < S::NLOAD; ++i) {
+                    const int flat = i * NT + tid, n = flat >> 4, c = flat & 15;
+                    const int li = min(j0 + kStepKeys + n, cend - 1) - c0;
+                    pf[i] = *reinterpret_cast<const u32x4*>(kc + (size_t)s_slot[li] * kHeadDim + c * 8);
+                }
+                // keep the prefetch issued here, ahead of the MFMAs that hide it
+                __builtin_amdgcn_sched_barrier(0);
+                float16v acc[2];
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) acc[mt] = float16v{};
+#pragma unroll
+                for (int s = 0; s < kSlices; ++s) {
+                    const half8 kbs = *reinterpret_cast<const half8*>(sk + lds_key_chunk(lane & 31, 2 * s + (lane >> 5)));
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt) acc[mt] = mfma32(qa[mt * kSlices + s], kbs, acc[mt]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // (after the last step this fills the idle buffer, which no
+                // wave reads any more: every wave has passed this step's barrier)
+#pragma unroll
+                for (int i = 0; i < S::NLOAD; ++i) {
+                    const int flat = i * NT + tid, n = flat >> 4, c = flat & 15;
+                    *reinterpret_cast<u32x4*>(s_keys[buf ^ 1] + lds_key_chunk(n, c)) = pf[i];
+                }
+                const int jn = j0 + (lane & 31);  // this lane's key (logical index)
+                const bool full = j0 + kStepKeys <= wlim;
+#pragma unroll
+                for (int o = 0; o < NOUT; ++o) {
+                    const int mt = o >> 2, g = o & 3;
+                    const float sc = combine_heads<RELU>(acc[mt][4 * g], acc[mt][4 * g + 1], acc[mt][4 * g + 2],
+                                                         acc[mt][4 * g + 3]);
+                    const int tr = out_tile_row(o, wave, lane);
+                    if (!FILTER) {
+                        if (full || jn < s_lim[tr]) A.out[(int64_t)(r0 + tr) * A.ld + jn] = sc;
+                    } else {
+                        // keep iff composite (sc, jn) >= (fT, jT) and the key is visible
+                        bool c = sc >= fT[o];
+                        if (!full) c = c && jn < s_lim[tr];
+                        if (__any(c && sc == fT[o])) c = c && (sc > fT[o] || jn <= s_jT[tr]);
+                        filter_append(A, c, sc, tr, r0, jn, lane, cnt_lo[o], cnt_hi[o], s_lbuf);
+                    }
+                }
+                buf ^= 1;
+            }
+            // every wave is done with this pass's s_lim before wave 0 rewrites it
+            __syncthreads();
+        }
+
+        if (FILTER) {
+            // flush the staged candidates: one global atomic per row
+            if (lane == 0) {
+#pragma unroll
+                for (int o = 0; o < NOUT; ++o) {
+                    s_lc[out_tile_row(o, wave, 0)] = cnt_lo[o];
+                    s_lc[out_tile_row(o, wave, 32)] = cnt_hi[o];
+                }
+            }
+            __syncthreads();
+            for (int t = wave; t < kTileRows; t += S::WAVES) {
+                const int n = min(s_lc[t], kLCap);
+                if (n == 0) continue;
+                const int row = r0 + t;
+                int base = 0;
+                if (lane == 0) base = atomicAdd(&A.cand_count[row], n);
+                base = __shfl(base, 0, 64);
+                for (int i = lane; i < n; i += 64)
+                    if (base + i < A.cand_cap) A.cand[(int64_t)row * A.cand_cap + base + i] = s_lbuf[t * kLCap + i];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace qsa

@@ -32,6 +32,7 @@ EXPORTED = (
     "qsa_score_paged", "qsa_topk_rows", "qsa_topk_rows_workspace_size",
     "qsa_select_paged_tokens", "qsa_select_paged_tokens_workspace_size",
     "qsa_last_error", "qsa_last_path", "qsa_version",
+    "qsa_debug_record_events", "qsa_debug_events_recorded",
 )
 
 
@@ -66,6 +67,10 @@ def lib():
     L.qsa_select_paged_tokens.restype = ctypes.c_int
     L.qsa_select_paged_tokens_workspace_size.argtypes = [i32, i32, i32, i32, i32, u32]
     L.qsa_select_paged_tokens_workspace_size.restype = sz
+    L.qsa_debug_record_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
+    L.qsa_debug_record_events.restype = ctypes.c_int
+    L.qsa_debug_events_recorded.argtypes = []
+    L.qsa_debug_events_recorded.restype = i32
     for name in ("qsa_last_error", "qsa_last_path", "qsa_version"):
         getattr(L, name).argtypes = []
         getattr(L, name).restype = ctypes.c_char_p
@@ -83,6 +88,25 @@ def qsa_last_path() -> str:
 
 def qsa_version() -> str:
     return lib().qsa_version().decode()
+
+
+class record_events:
+    """Arms the next qsa_select_paged_tokens call on this thread to record
+    the given torch.cuda.Event objects between its kernels (see
+    qsa_debug_record_events in include/qsa.h).  Keep the object alive until
+    that call has returned."""
+
+    def __init__(self, events):
+        self.events = list(events)
+        for e in self.events:
+            if not e.cuda_event:   # torch creates the HIP event on its first record
+                e.record()
+        self._arr = (ctypes.c_void_p * len(self.events))(*[e.cuda_event for e in self.events])
+        _check(lib().qsa_debug_record_events(self._arr, len(self.events)))
+
+    @staticmethod
+    def recorded() -> int:
+        return int(lib().qsa_debug_events_recorded())
 
 
 def _check(status: int):

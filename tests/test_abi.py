@@ -44,8 +44,16 @@ def test_version_and_empty_error():
 def test_workspace_sizes():
     assert Q.qsa_select_paged_tokens_workspace_size(0, 1, 100, 4, 64) == 0
     assert Q.qsa_select_paged_tokens_workspace_size(10, 1, 0, 4, 64) == 0
-    n = Q.qsa_select_paged_tokens_workspace_size(1616, 1, 46000, 4, 2048)
-    assert n >= 1616 * 46000 * 4
+    fused = Q.qsa_select_paged_tokens_workspace_size(1616, 1, 46000, 4, 2048)
+    os.environ["QSA_FORCE_PATH"] = "two_pass"
+    try:
+        two_pass = Q.qsa_select_paged_tokens_workspace_size(1616, 1, 46000, 4, 2048)
+    finally:
+        del os.environ["QSA_FORCE_PATH"]
+    assert two_pass >= 1616 * 46000 * 4          # the materialised score matrix
+    assert 0 < fused < two_pass                   # the fused arm never holds it
+    # decode-like batches (one row per request) take the two-pass arm
+    assert Q.qsa_select_paged_tokens_workspace_size(256, 256, 46000, 4, 2048) >= 256 * 46000 * 4
     assert Q.qsa_topk_rows_workspace_size(10, 100, 8) >= 0
 
 

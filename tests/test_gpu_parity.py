@@ -10,6 +10,8 @@ sections "Purpose" (exact lexicographic selector) and "Test Plan" (selected
 token sets identical in all rows); "spec(MODEL-MM-QWEN4-EXP) ...", section
 "The component deep-dives, and two corrections to the above".
 """
+import contextlib
+import os
 import sys
 
 import numpy as np
@@ -24,6 +26,29 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 RELU = Q.QSA_SCORE_RELU
 KEYS = Q.QSA_OUT_KEYS
+
+
+PATHS = ["two_pass", "fused", "fused_fallback"]
+
+
+@contextlib.contextmanager
+def force_path(name):
+    """Drive one execution arm deliberately (the library reads these
+    variables on every call); "fused_fallback" makes every row of the fused
+    arm take its exact recompute path."""
+    old = {k: os.environ.get(k) for k in ("QSA_FORCE_PATH", "QSA_DEBUG_FORCE_FALLBACK")}
+    if name is not None:
+        os.environ["QSA_FORCE_PATH"] = "fused" if name.startswith("fused") else name
+        if name == "fused_fallback":
+            os.environ["QSA_DEBUG_FORCE_FALLBACK"] = "1"
+    try:
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 def note(*a):
@@ -81,22 +106,30 @@ def assert_scores(gs, ref, V, exact, rows=None):
     return worst
 
 
-def full_parity(oracle_mod, w, flags, integer):
+def full_parity(oracle_mod, w, flags, integer, paths=(None,)):
     """Scores element by element, the GPU selection on its own scores, and
-    (integer inputs) the whole path against the oracle."""
+    (integer inputs) the whole path against the oracle, for each forced arm."""
     d = to_dev(w)
     V = visible(oracle_mod, w)
     gs = gpu_scores(d, w, flags)
     ref = oracle_mod.score_paged(w.q, w.kcache, w.page_table, w.pos, w.compress_ratio, row_req=w.row_req,
                                  flags=flags & RELU)
     worst = assert_scores(gs, ref, V, exact=integer)
-    out = gpu_select(d, w, flags)
     exp = expected_from_scores(oracle_mod, gs, V, w.k, w.compress_ratio, flags)
-    assert np.array_equal(out, exp)
+    full = None
     if integer:
         full = oracle_mod.select_paged_tokens(w.q, w.kcache, w.page_table, w.pos, w.compress_ratio, w.k,
                                               row_req=w.row_req, flags=flags)
-        assert np.array_equal(out, full)
+    out = None
+    for path in paths:
+        with force_path(path):
+            out = gpu_select(d, w, flags)
+            ran = Q.qsa_last_path()
+        if path is not None:
+            assert ran == ("fused" if path.startswith("fused") else path)
+        assert np.array_equal(out, exp), f"{w.name} path={path}: selection differs from oracle_select(GPU scores)"
+        if full is not None:
+            assert np.array_equal(out, full), f"{w.name} path={path}: differs from the oracle end to end"
     note(f"{w.name}: rows={w.rows} sumV={int(V.sum())} flags={flags} max_rel_err={worst:.2e}")
     return out
 
@@ -106,7 +139,7 @@ def full_parity(oracle_mod, w, flags, integer):
 @pytest.mark.parametrize("flags", [0, RELU, KEYS, RELU | KEYS])
 @pytest.mark.parametrize("integer", [False, True])
 def test_tiny(oracle_mod, flags, integer):
-    full_parity(oracle_mod, W.tiny(integer=integer), flags, integer)
+    full_parity(oracle_mod, W.tiny(integer=integer), flags, integer, paths=PATHS)
 
 
 REDUCED = {
@@ -130,7 +163,7 @@ def test_reduced(oracle_mod, name, integer, flags):
     if name == "tie_stress_96" and not integer:
         pytest.skip("the tie-stress workload is integer-valued by definition")
     w = REDUCED[name](integer)
-    full_parity(oracle_mod, w, flags, integer or name == "tie_stress_96")
+    full_parity(oracle_mod, w, flags, integer or name == "tie_stress_96", paths=PATHS)
 
 
 def test_out_keys_reduced(oracle_mod):
@@ -138,9 +171,11 @@ def test_out_keys_reduced(oracle_mod):
     d = to_dev(w)
     V = visible(oracle_mod, w)
     gs = gpu_scores(d, w, 0)
-    for k in (1, 7, 512, 2048, Q.QSA_MAX_SELECT):
-        out = gpu_select(d, w, KEYS, k=k)
-        assert np.array_equal(out, expected_from_scores(oracle_mod, gs, V, k, 4, KEYS)), k
+    for path in PATHS:
+        for k in (1, 7, 512, 2048, Q.QSA_MAX_SELECT):
+            with force_path(path):
+                out = gpu_select(d, w, KEYS, k=k)
+            assert np.array_equal(out, expected_from_scores(oracle_mod, gs, V, k, 4, KEYS)), (path, k)
 
 
 def test_interleaved_requests(oracle_mod):
@@ -150,7 +185,7 @@ def test_interleaved_requests(oracle_mod):
                 integer=True, k=256)
     perm = rng.permutation(w.rows)
     w.q, w.pos, w.row_req = np.ascontiguousarray(w.q[perm]), w.pos[perm].copy(), w.row_req[perm].copy()
-    full_parity(oracle_mod, w, 0, True)
+    full_parity(oracle_mod, w, 0, True, paths=PATHS)
 
 
 def test_edges(oracle_mod):
@@ -164,13 +199,15 @@ def test_edges(oracle_mod):
     w.q = np.repeat(w.q, len(cases), axis=0)
     w.pos = np.array(cases, np.int32)
     w.row_req = np.zeros(len(cases), np.int32)
-    full_parity(oracle_mod, w, 0, True)
-    for k in (4, 8):
-        out = gpu_select(to_dev(w), w, 0, k=k)
-        exp = oracle_mod.select_paged_tokens(w.q, w.kcache, w.page_table, w.pos, 4, k)
-        assert np.array_equal(out, exp), k
+    full_parity(oracle_mod, w, 0, True, paths=PATHS)
+    for path in PATHS:
+        for k in (4, 8):
+            with force_path(path):
+                out = gpu_select(to_dev(w), w, 0, k=k)
+            exp = oracle_mod.select_paged_tokens(w.q, w.kcache, w.page_table, w.pos, 4, k)
+            assert np.array_equal(out, exp), (path, k)
     one = W.build("one", rng, 43, [5000], [1], permute_pages=False, integer=True, k=2048)
-    full_parity(oracle_mod, one, 0, True)
+    full_parity(oracle_mod, one, 0, True, paths=PATHS)
 
 
 def test_golden_fixture_on_gpu():
@@ -190,12 +227,14 @@ def test_golden_fixture_on_gpu():
     assert s[0, :16].cpu().numpy().tolist() == g["expected_scores_row0_first16"]
 
 
-def test_determinism():
+@pytest.mark.parametrize("path", ["two_pass", "fused"])
+def test_determinism(path):
     w = W.kernel_shape(rows=130, ctx=60_000)
     d = to_dev(w)
-    outs = [gpu_select(d, w, 0) for _ in range(3)]
+    with force_path(path):
+        outs = [gpu_select(d, w, 0) for _ in range(3)]
     side = torch.cuda.Stream()
-    with torch.cuda.stream(side):
+    with force_path(path), torch.cuda.stream(side):
         o = Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"], 4, w.k, row_req=d["row_req"])
     side.synchronize()
     outs.append(o.cpu().numpy())
@@ -266,7 +305,7 @@ def test_topk_rows_visible_none(oracle_mod):
 
 # ------------------------------------------------------------ full sizes
 
-def sampled_parity(oracle_mod, w, flags, integer, sample_rows):
+def sampled_parity(oracle_mod, w, flags, integer, sample_rows, paths=(None,)):
     """Full-size launch (the configuration the benchmark times): the oracle
     scores a sample of rows one by one; the GPU selection over every row is
     checked against the oracle's selector on the GPU's own scores."""
@@ -277,31 +316,37 @@ def sampled_parity(oracle_mod, w, flags, integer, sample_rows):
     ref = oracle_mod.score_paged(w.q[rows], w.kcache, w.page_table, w.pos[rows], w.compress_ratio,
                                  row_req=w.row_req[rows], flags=flags & RELU)
     worst = assert_scores(gs, ref, V, exact=integer, rows=rows)
-    out = gpu_select(d, w, flags)
     exp = expected_from_scores(oracle_mod, gs, V, w.k, w.compress_ratio, flags)
-    assert np.array_equal(out, exp)
+    out = None
+    for path in paths:
+        with force_path(path):
+            out = gpu_select(d, w, flags)
+        assert np.array_equal(out, exp), f"{w.name} full, path={path}"
     note(f"{w.name} full: rows={w.rows} sumV={int(V.sum())} sampled={len(rows)} max_rel_err={worst:.2e}")
     return out
 
 
 def test_full_kernel_shape(oracle_mod):
     w = W.kernel_shape()
-    sampled_parity(oracle_mod, w, 0, False, [0, 1, 63, 64, 800, 1550, 1599, 1600, 1615])
+    sampled_parity(oracle_mod, w, 0, False, [0, 1, 63, 64, 800, 1550, 1599, 1600, 1615],
+                   paths=(None, "two_pass"))
 
 
 def test_full_tie_stress(oracle_mod):
     w = W.tie_stress()
     d = to_dev(w)
-    out = gpu_select(d, w, 0)
     full = oracle_mod.select_paged_tokens(w.q, w.kcache, w.page_table, w.pos, 4, w.k)
-    assert np.array_equal(out, full)
+    for path in (None, "two_pass", "fused"):
+        with force_path(path):
+            out = gpu_select(d, w, 0)
+        assert np.array_equal(out, full), path
 
 
 def test_full_mixed(oracle_mod):
     w = W.mixed()
     starts = np.concatenate([[0], np.cumsum(np.bincount(w.row_req))])
     sample = list(starts[:-1]) + list(starts[1:] - 1)
-    sampled_parity(oracle_mod, w, 0, False, sample)
+    sampled_parity(oracle_mod, w, 0, False, sample, paths=(None, "two_pass"))
 
 
 @pytest.mark.slow

@@ -54,7 +54,35 @@ def parse():
                     choices=["tiny", "kernel_shape", "tie_stress", "mixed", "decode"])
     ap.add_argument("--path", choices=["two_pass", "fused"], default=None,
                     help="force one execution arm (default: the library's choice)")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="after timing, copy this many MiB device to device (counter scale probe)")
+    ap.add_argument("--summarize-profile", action="store_true",
+                    help="write profiles/ summaries from rocprofv3 output instead of benchmarking")
+    ap.add_argument("--stats-dir", default=None)
+    ap.add_argument("--fetch-dir", default=None)
+    ap.add_argument("--write-dir", default=None)
+    ap.add_argument("--kernel", default="filter_scorer")
+    ap.add_argument("--command", default=None)
     return ap.parse_args()
+
+
+# kernel name in the bench -> (substrings of the demangled symbol, source files)
+KERNEL_SOURCES = {
+    "filter_scorer": (("score_tiles_kernel", "(qsa::Epi)1"),
+                      ["paged_block_scoring_amd/csrc/score_core.hpp", "paged_block_scoring_amd/csrc/score.hip",
+                       "paged_block_scoring_amd/csrc/qsa_device.hpp"]),
+    "sample_scorer": (("score_tiles_kernel", "(qsa::Epi)0"),
+                      ["paged_block_scoring_amd/csrc/score_core.hpp", "paged_block_scoring_amd/csrc/score.hip",
+                       "paged_block_scoring_amd/csrc/qsa_device.hpp"]),
+    "scorer": (("score_tiles_kernel", "(qsa::Epi)0"),
+               ["paged_block_scoring_amd/csrc/score_core.hpp", "paged_block_scoring_amd/csrc/score.hip",
+                "paged_block_scoring_amd/csrc/qsa_device.hpp"]),
+    "sample_threshold": (("sample_threshold_kernel",),
+                         ["paged_block_scoring_amd/csrc/fused.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
+    "final_select": (("fused_final_kernel",),
+                     ["paged_block_scoring_amd/csrc/fused.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
+    "topk_rows": (("topk_rows_kernel",), ["paged_block_scoring_amd/csrc/topk.hip"]),
+}
 
 
 def source_digest(paths):
@@ -65,17 +93,88 @@ def source_digest(paths):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel_name, src_files, launches_per_step):
+def traffic_for(kernel_name, workload):
     """HBM bytes per launch from a committed rocprofv3 --pmc summary, only if
     it was taken on the kernel's current source."""
-    path = os.path.join(ROOT, "profiles", f"{kernel_name}_traffic.json")
-    if not os.path.exists(path):
+    path = os.path.join(ROOT, "profiles", f"{kernel_name}_{workload}_traffic.json")
+    if not os.path.exists(path) or kernel_name not in KERNEL_SOURCES:
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_digest") != source_digest(src_files):
+    if rec.get("source_digest") != source_digest(KERNEL_SOURCES[kernel_name][1]):
         return None
     return rec.get("bytes_per_launch")
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profile(args):
+    """Turn rocprofv3 CSV output into the text summaries kept under profiles/.
+
+    --stats-dir   : a `rocprofv3 --kernel-trace --stats` run of this script;
+    --fetch-dir / --write-dir : `--pmc FETCH_SIZE` and `--pmc WRITE_SIZE` runs
+                    of this script with --copy-probe, which end with a plain
+                    device copy of known size used to scale the counters.
+    """
+    import glob
+    out = {}
+    name = args.workload
+    if args.stats_dir:
+        stats = _read_csv(glob.glob(os.path.join(args.stats_dir, "*_kernel_stats.csv"))[0])
+        lines = [f"# Kernel time, {name} (rocprofv3 --kernel-trace --stats)", "",
+                 "Command (from the repository root, on the GPU box):", "", "```", args.command or "", "```", "",
+                 "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+        for r in stats:
+            lines.append(f"| `{r['Name'][:110]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                         f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+        path = os.path.join(ROOT, "profiles", f"kernel_trace_{name}.md")
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        out["stats"] = path
+    if args.fetch_dir and args.write_dir:
+        def per_dispatch(d, counter):
+            rows = _read_csv(glob.glob(os.path.join(d, "*_counter_collection.csv"))[0])
+            res = {}
+            for r in rows:
+                if r["Counter_Name"] != counter:
+                    continue
+                key = int(r["Dispatch_Id"])
+                res.setdefault(key, [r["Kernel_Name"], 0.0])
+                res[key][1] += float(r["Counter_Value"])
+            return res
+        fetch = per_dispatch(args.fetch_dir, "FETCH_SIZE")
+        write = per_dispatch(args.write_dir, "WRITE_SIZE")
+        probe_bytes = args.copy_probe * (1 << 20)
+
+        def probe(res):
+            ids = [k for k, (n, _) in res.items() if "copyBuffer" in n]
+            return res[max(ids)][1] * 1024.0
+        f_scale = probe_bytes / probe(fetch)
+        w_scale = probe_bytes / probe(write)
+        kname = args.kernel
+        subs = KERNEL_SOURCES[kname][0]
+
+        def mean_for(res):
+            vals = [v for n, v in res.values() if all(sub in n for sub in subs)]
+            return sum(vals) / len(vals) * 1024.0, len(vals)
+        fb, nf = mean_for(fetch)
+        wb, nw = mean_for(write)
+        rec = {"kernel": kname, "workload": name, "symbol_substrings": list(subs),
+               "source_digest": source_digest(KERNEL_SOURCES[kname][1]),
+               "fetch_bytes_per_launch_raw": fb, "write_bytes_per_launch_raw": wb,
+               "copy_probe_bytes": probe_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+               "bytes_per_launch": round(fb * f_scale + wb * w_scale),
+               "dispatches": [nf, nw], "command": args.command}
+        path = os.path.join(ROOT, "profiles", f"{kname}_{name}_traffic.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        out["traffic"] = path
+    print(json.dumps(out))
+    return 0
 
 
 def time_calls(fn, steps, warmup, torch):
@@ -120,6 +219,8 @@ def kernel_times(fn, steps, names, torch, Q):
 
 def main():
     args = parse()
+    if args.summarize_profile:
+        return summarize_profile(args)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the indexer shards across GPUs only as a design, see the design notes)", file=sys.stderr)
@@ -173,9 +274,8 @@ def main():
     bound, work, peak, unit = units[dom_name]
     scale = 1e12 if unit == "TFLOP/s" else 1e9
     achieved = work / (kms[dom_name] * 1e-3) / scale
-    src = ["paged_block_scoring_amd/csrc/score_core.hpp", "paged_block_scoring_amd/csrc/qsa_device.hpp"]
     roofline = {"kernel": dom_name, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": traffic_for(dom_name, src, 1),
+                "frac": round(achieved / peak, 4), "traffic": traffic_for(dom_name, args.workload),
                 "ms_per_launch": round(kms[dom_name], 4)}
 
     rows_per_s = rows / (ms_step * 1e-3)
@@ -203,6 +303,13 @@ def main():
         "roofline": roofline,
         "wall_s_timed": round(wall, 4),
     }
+
+    if args.copy_probe > 0:
+        n = args.copy_probe * (1 << 20)
+        src_t = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst_t = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
 
     if not args.no_cpu_baseline:
         import oracle

@@ -12,20 +12,21 @@
 // composites.  The arm runs in four steps:
 //  1. sampling pass: the scorer materialises the scores of every stride-th
 //     key (logical sample i is key stride*i);
-//  2. threshold: per row, T = the m-th largest sample composite, with m
-//     sized so that about kb + 4 sqrt(kb) ... keys of the whole row are
-//     expected to reach T (T = 0, "keep everything", when the row has fewer
-//     than m samples);
-//  3. filtering pass: the scorer keeps every composite >= T in the row's
-//     candidate list (staged in LDS, one global atomic per row and
-//     workgroup);
+//  2. threshold: per row, fT = the score of the m-th largest sample
+//     composite, with m sized so that comfortably more than kb keys of the
+//     whole row are expected to score >= fT; a row with fewer than m samples
+//     gets a threshold no score reaches;
+//  3. filtering pass: the scorer keeps every key with score >= fT in the
+//     row's candidate list (staged in LDS, one global atomic per row and
+//     piece);
 //  4. final select: if the row has at least min(kb, V) and at most cap
-//     candidates they contain its exact top-kb (any kb composites >= T force
-//     the kb-th largest to be >= T), which a radix select and a bitonic sort
-//     in LDS turn into rank order.  Otherwise the workgroup recomputes the
-//     row's scores itself with the same MFMA sequence and keeps an exact
-//     running top-kb in LDS.  Either way the result is exact; the sample only
-//     decides how fast.
+//     candidates they contain its exact top-kb (kb scores >= fT force the
+//     kb-th largest score to be >= fT, so every member of the top-kb passed
+//     the filter), which a radix select over composites and a bitonic sort in
+//     LDS turn into rank order.  Otherwise the workgroup recomputes the row's
+//     scores itself with the same MFMA sequence and keeps an exact running
+//     top-kb in LDS.  Either way the result is exact; the sample only decides
+//     how fast.
 #include <cmath>
 
 #include "qsa_device.hpp"
@@ -58,15 +59,14 @@ __global__ __launch_bounds__(kThrNT) void sample_threshold_kernel(const float* _
     const int row = blockIdx.x;
     const int V = row_visible_count(vis, row);
     const int ns = (V + stride - 1) / stride;
-    uint64_t T = 0ull;
-    if (ns >= m) {
+    uint64_t T = ~0ull;  // decodes to a NaN threshold score: nothing passes
+    if (ns >= m && !force_fallback) {
         const float* srow = samp + (int64_t)row * ld_s;
         for (int i = threadIdx.x; i < ns; i += kThrNT)
             s_a[i] = compose(order_key(srow[i]), (uint32_t)(i * stride));
         __syncthreads();
         T = lds_kth_largest<kThrNT>(s_a, ns, m, &ks);
     }
-    if (force_fallback) T = ~0ull;  // nothing can pass: every row takes the recompute path
     if (threadIdx.x == 0) {
         thresh[row] = T;
         cand_count[row] = 0;
@@ -89,12 +89,12 @@ constexpr int kFinNT = 256;
 constexpr int kFinWaves = kFinNT / 64;
 
 // Exact top-kb of one row by recomputation: each wave scores 32 keys at a
-// time straight from the cache with the same MFMA sequence as the tiled
-// scorer (the row's four heads occupy MFMA rows 0..3; the other rows are
-// zero), composites above the running cutoff are
-// appended in LDS, and the buffer is cut back to its kb largest whenever it
-// exceeds kb.  Leaves the selected composites (unsorted) in
-// a[0 .. return value).
+// time straight from the cache with the same MFMA sequences as the tiled
+// scorer, with the row in MFMA row slot 0 and zero query fragments elsewhere
+// (default form: MFMA rows 0, 1 are the two head pairs; relu form: rows 0..3
+// are the four heads).  Composites above the running cutoff are appended in
+// LDS, and the buffer is cut back to its kb largest whenever it exceeds kb.
+// Leaves the selected composites (unsorted) in a[0 .. return value).
 template <int CAPL>
 __device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* a, KthScratch* ks, int* s_pend) {
     const PagedArgs& p = A.a;
@@ -122,16 +122,26 @@ __device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* 
             half8 kb8[kSlices];
 #pragma unroll
             for (int s = 0; s < kSlices; ++s) kb8[s] = *reinterpret_cast<const half8*>(key + 16 * s + 8 * g);
-            // MFMA rows 0..3 are the row's four heads; rows 4..31 are zero
             float16v acc = {};
+            float sc;
+            if (p.relu) {
 #pragma unroll
-            for (int s = 0; s < kSlices; ++s) {
-                half8 qv = {};
-                if (m < 4) qv = *reinterpret_cast<const half8*>(qrow + m * kHeadDim + 16 * s + 8 * g);
-                acc = mfma32(qv, kb8[s], acc);
+                for (int s = 0; s < kSlices; ++s) {
+                    half8 qv = {};
+                    if (m < 4) qv = *reinterpret_cast<const half8*>(qrow + m * kHeadDim + 16 * s + 8 * g);
+                    acc = mfma32(qv, kb8[s], acc);
+                }
+                sc = combine_relu_heads(acc[0], acc[1], acc[2], acc[3]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < 2 * kSlices; ++t) {
+                    half8 qv = {};
+                    const int s = t >> 1, h = 2 * m + (t & 1);
+                    if (m < 2) qv = *reinterpret_cast<const half8*>(qrow + h * kHeadDim + 16 * s + 8 * g);
+                    acc = mfma32(qv, kb8[s], acc);
+                }
+                sc = combine_pairs(acc[0], acc[1]);
             }
-            const float sc = p.relu ? combine_heads<true>(acc[0], acc[1], acc[2], acc[3])
-                                    : combine_heads<false>(acc[0], acc[1], acc[2], acc[3]);
             // lanes 0..31 hold MFMA row 0 (the row's score) for key j0 + lane
             if (g == 0 && j < cend) {
                 const uint64_t comp = compose(order_key(sc), (uint32_t)j);
@@ -165,7 +175,11 @@ __global__ __launch_bounds__(kFinNT) void fused_final_kernel(FinalArgs A) {
     int have;
     if (n >= nsel && n <= A.cand_cap) {
         const uint64_t* c = A.cand + (int64_t)row * A.cand_cap;
-        for (int i = threadIdx.x; i < n; i += kFinNT) s_a[i] = c[i];
+        // (score bits, key) entries -> composites
+        for (int i = threadIdx.x; i < n; i += kFinNT) {
+            const uint64_t e = c[i];
+            s_a[i] = compose(order_key(__uint_as_float((uint32_t)(e >> 32))), (uint32_t)e);
+        }
         __syncthreads();
         have = n;
         if (n > kb) {

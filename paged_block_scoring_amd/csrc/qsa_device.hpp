@@ -3,17 +3,21 @@
 // The score of (row r, key j) is computed in exactly one way by every kernel
 // of this library, so that the scorer, the fused selectors and the fallback
 // paths all produce the same bits.  All of them use v_mfma_f32_32x32x16_f16
-// (the full-rate fp16 MFMA shape of gfx950) with MFMA row m = 4*row + head
-// (8 query rows x 4 heads per 32-row tile) and the key as the column.  A
-// chain of 8 MFMAs over head-dim slices s = 0..7 (lane half g = lane/32
-// supplies dims 16s+8g .. 16s+8g+7 of both operands), accumulating in fp32
-// from +0, gives every head's dot.  The 32x32 output layout puts rows
-// 8*(v/4) + 4*(l/32) + (v%4) of column l%32 in accumulator element v of lane
-// l, so each group of four elements is the four heads of one (row, key) and
-// the head reduction is lane-local:
-//   default form: ((h0 + h1) + h2) + h3;
-//   relu form:    ((relu h0 + relu h1) + relu h2) + relu h3, times the fp32
-//                 value nearest 1/sqrt(128).
+// (the full-rate fp16 MFMA shape of gfx950) with the key as the column; lane
+// half g = lane/32 supplies dims 16s+8g .. 16s+8g+7 of head-dim slice s of
+// both operands, and the 32x32 output puts rows 8*(v/4) + 4*(l/32) + (v%4) of
+// column l%32 in accumulator element v of lane l.  Accumulation is fp32 from
+// +0 in the order given.
+//   default form (head pairs): MFMA row m = 2*row + p (16 query rows x 2 head
+//     pairs); a chain of 16 MFMAs, step t = (slice t/2, head 2p + t%2), adds
+//     both heads of pair p into one sum, so accumulator elements 2o and 2o+1
+//     of a lane are the two pair sums of one (row, key) and the score is
+//     pair0 + pair1.
+//   relu form (per head): MFMA row m = 4*row + head (8 query rows x 4 heads);
+//     a chain of 8 MFMAs over the slices gives every head's dot, elements
+//     4o'..4o'+3 are the four heads of one (row, key), and the score is
+//     ((relu h0 + relu h1) + relu h2) + relu h3 times the fp32 value nearest
+//     1/sqrt(128).
 // Sources: "[Perf][Qwen4Exp] Admit the cuBLAS QSA indexer and exact top-k on
 // Turing", section "Purpose" (FP16 inputs, FP32 accumulation) and "Test Plan"
 // (4 index heads, head dim 128); "spec(MODEL-MM-QWEN4-EXP): Qwen3.8-Flash-Next
@@ -76,10 +80,11 @@ __device__ __forceinline__ float16v mfma32(half8 a, half8 b, float16v c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// The four head dots of one (row, key) -> score.
-template <bool RELU>
-__device__ __forceinline__ float combine_heads(float h0, float h1, float h2, float h3) {
-    if (!RELU) return ((h0 + h1) + h2) + h3;
+// The two head-pair sums of one (row, key) -> score (default form).
+__device__ __forceinline__ float combine_pairs(float p0, float p1) { return p0 + p1; }
+
+// The four head dots of one (row, key) -> score (relu form).
+__device__ __forceinline__ float combine_relu_heads(float h0, float h1, float h2, float h3) {
     h0 = fmaxf(h0, 0.0f);
     h1 = fmaxf(h1, 0.0f);
     h2 = fmaxf(h2, 0.0f);

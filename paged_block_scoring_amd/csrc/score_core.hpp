@@ -14,23 +14,23 @@
 // XCD w % 8 (the hardware's round-robin dispatch) and owns a contiguous,
 // equal share of that XCD's (tile, key) positions, so every XCD streams only
 // its stripe of keys (which stays in its L2) and every workgroup does the
-// same amount of work.  A share is processed as pieces of one tile and a key
-// range.
+// same amount of work.  A share is processed as pieces of one tile and at
+// most kMaxPiece keys.
 //
-// A piece.  Each wave holds the fp16 query fragments of its rows in
-// registers.  Keys are staged 32 at a time: a per-piece table gives every
-// logical key's slot in the cache; each thread prefetches its 16-byte pieces
-// of the next 32 keys into registers while the current ones are consumed from
-// one half of a double-buffered, XOR-swizzled LDS tile (one barrier per 32
-// keys).  Per 8 rows x 4 heads a chain of 8 MFMAs (32x32x16) gives 32 keys'
-// head dots; each lane reduces its four heads to a score, which goes to the
-// epilogue:
+// A piece.  Each of the 4 waves holds the fp16 query fragments of its 16 rows
+// in registers (loaded once per tile).  Keys are staged 64 at a time: a
+// per-piece table gives every logical key's slot in the cache; each thread
+// prefetches its 16-byte pieces of the next 64 keys into registers while the
+// current ones are consumed from one half of a double-buffered, XOR-swizzled
+// LDS tile (one barrier per 64 keys = two 32-key MFMA column tiles, whose
+// MFMA chains are interleaved).  The MFMA arrangements are the canonical ones
+// of qsa_device.hpp.  Each visible score goes to the epilogue:
 //   Store  -- out[row*ld + i] = score (two-pass arm, sampling pass);
-//   Filter -- keep the composite (score, key) if it is >= the row's
-//             threshold: one compare per score; the rare candidates get
-//             slots from wave-uniform per-row counters (ballot + mbcnt),
-//             are staged per row in LDS and appended to the row's global
-//             list with one atomic per row and piece.
+//   Filter -- keep (score, key) if score >= the row's threshold score: one
+//             compare per score; kept entries get slots from wave-uniform
+//             per-row counters (ballot + mbcnt), are staged per row in LDS
+//             as (score bits, key) and appended to the row's global list with
+//             one atomic per row and piece.
 // Rows of different requests in one tile are processed in successive passes.
 #pragma once
 
@@ -41,11 +41,12 @@ namespace qsa {
 
 enum class Epi { Store, Filter };
 
-constexpr int kStepKeys = 32;    // keys per LDS stage
-constexpr int kMaxPiece = 2048;  // logical keys per piece (slot-table size)
-constexpr int kLCap = 32;        // per-row LDS staging slots of the Filter epilogue
-constexpr int kTileRows = 64;    // rows per tile
-constexpr int kXcds = 8;         // XCDs of an MI355X (256 CUs = 8 x 32)
+constexpr int kSub = 2;                // 32-key column tiles per LDS stage
+constexpr int kStepKeys = 32 * kSub;   // keys per LDS stage
+constexpr int kMaxPiece = 1024;        // logical keys per piece (slot-table size)
+constexpr int kLCap = 64;              // per-row LDS staging slots of the Filter epilogue
+constexpr int kTileRows = 64;          // rows per tile
+constexpr int kXcds = 8;               // XCDs of an MI355X (256 CUs = 8 x 32)
 
 struct ScoreKernelArgs {
     PagedArgs a;
@@ -58,8 +59,8 @@ struct ScoreKernelArgs {
     float* out;
     int64_t ld;
     // Filter
-    const uint64_t* thresh;  // [rows]
-    uint64_t* cand;          // [rows][cand_cap]
+    const uint64_t* thresh;  // [rows] threshold composite; only its score is used
+    uint64_t* cand;          // [rows][cand_cap] entries (score bits << 32 | key)
     int32_t* cand_count;     // [rows]
     int32_t cand_cap;
 };
@@ -67,22 +68,36 @@ struct ScoreKernelArgs {
 struct ScoreShape {
     static constexpr int WAVES = 4;
     static constexpr int NT = 64 * WAVES;
-    static constexpr int RPW = kTileRows / WAVES;                    // rows per wave (two 8-row MFMA tiles)
+    static constexpr int RPW = kTileRows / WAVES;                    // rows per wave
     static constexpr int NLOAD = kStepKeys * kChunksPerKey / NT;     // 16-byte pieces per thread per stage
     static constexpr int NOUT = 8;                                   // scores per lane per 32 keys
+    static constexpr int NQ = 2 * kSlices;                           // query fragments per lane
 };
 
-// Tile row (0..63) of this lane's output o = 4*mt + g: MFMA tile mt of the
-// wave, element group g (rows 8*g/2.. of the 32 MFMA rows = query row 2g + l/32).
+// Row (within the wave's 16) of output o of a lane in lane half 0; lane half
+// 1 adds out_half_offset.  Default form: MFMA rows 8*(v/4) + (v%4) hold
+// (row, pair) = (m/2, m%2), so outputs o = v/2 are rows 4*(o/2) + o%2 and the
+// upper lane half (MFMA rows +4) is rows +2.  Relu form: outputs o = 4*mt + g
+// of MFMA tile mt are rows 8*mt + 2*g, and the upper lane half is rows +1.
+template <bool RELU>
+__device__ __forceinline__ constexpr int out_row_offset(int o) {
+    return RELU ? 8 * (o >> 2) + 2 * (o & 3) : 4 * (o >> 1) + (o & 1);
+}
+template <bool RELU>
+__device__ __forceinline__ constexpr int out_half_offset() {
+    return RELU ? 1 : 2;
+}
+template <bool RELU>
 __device__ __forceinline__ int out_tile_row(int o, int wave, int lane) {
-    return wave * 16 + (o >> 2) * 8 + 2 * (o & 3) + (lane >> 5);
+    return wave * ScoreShape::RPW + out_half_offset<RELU>() * (lane >> 5) + out_row_offset<RELU>(o);
 }
 
-// Filter epilogue for one output index o of a wave: `c` is this lane's
-// exact keep decision for (tile row tr, key jn).  The two 32-lane halves of
-// the wave hold two different rows, each owned by this wave alone, so the
-// slot of a kept composite is the row's running count (a wave-uniform value)
-// plus the lane's rank among the kept lanes of its half; no atomics.
+// Filter epilogue for one output index o of a wave: `c` is this lane's keep
+// decision for (tile row tr, key jn).  The two 32-lane halves of the wave
+// hold two different rows, each owned by this wave alone, so the slot of a
+// kept entry is the row's running count (a wave-uniform value) plus the
+// lane's rank among the kept lanes of its half; no atomics unless the row's
+// LDS staging is full.
 __device__ __forceinline__ void filter_append(const ScoreKernelArgs& A, bool c, float sc, int tr, int r0, int jn,
                                               int lane, int& cnt_lo, int& cnt_hi, uint64_t* s_lbuf) {
     const uint64_t m = __ballot(c);
@@ -94,12 +109,12 @@ __device__ __forceinline__ void filter_append(const ScoreKernelArgs& A, bool c, 
     cnt_lo += __popc(lo);
     cnt_hi += __popc(hi);
     if (c) {
-        const uint64_t comp = compose(order_key(sc), (uint32_t)jn);
+        const uint64_t e = ((uint64_t)__float_as_uint(sc) << 32) | (uint32_t)jn;
         if (slot < kLCap) {
-            s_lbuf[tr * kLCap + slot] = comp;
+            s_lbuf[tr * kLCap + slot] = e;
         } else {
             const int g = atomicAdd(&A.cand_count[r0 + tr], 1);
-            if (g < A.cand_cap) A.cand[(int64_t)(r0 + tr) * A.cand_cap + g] = comp;
+            if (g < A.cand_cap) A.cand[(int64_t)(r0 + tr) * A.cand_cap + g] = e;
         }
     }
 }
@@ -113,8 +128,7 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
     __shared__ __attribute__((aligned(16))) unsigned char s_keys[2][kStepKeys * kKeyBytes];
     __shared__ uint32_t s_slot[kMaxPiece];
     __shared__ int32_t s_req[kTileRows], s_lv[kTileRows], s_todo[kTileRows], s_lim[kTileRows];
-    __shared__ __attribute__((aligned(16))) float s_fT[FILTER ? kTileRows : 1];
-    __shared__ int32_t s_jT[FILTER ? kTileRows : 1];
+    __shared__ float s_fT[FILTER ? kTileRows : 1];
     __shared__ int32_t s_lc[FILTER ? kTileRows : 1];
     __shared__ uint64_t s_lbuf[FILTER ? kTileRows * kLCap : 1];
     __shared__ int32_t s_act, s_vmax;
@@ -129,6 +143,10 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
     int64_t p = (int64_t)loc * A.seg_len;
     const int64_t pend = min(p + A.seg_len, total);
 
+    half8 qa[S::NQ];
+    float fT[NOUT];
+    int loaded_tile = -1;
+
     while (p < pend) {
         const int tile = (int)(p / span);
         const int off = (int)(p - (int64_t)tile * span);
@@ -136,6 +154,7 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
         const int c0 = xk0 + off, c1 = c0 + len;
         p += len;
         const int r0 = tile * kTileRows;
+        const bool new_tile = tile != loaded_tile;
 
         for (int t = tid; t < kTileRows; t += NT) {
             const int r = r0 + t;
@@ -152,29 +171,44 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
             s_req[t] = req;
             s_lv[t] = lv;
             s_todo[t] = (req >= 0 && lv > c0) ? 1 : 0;
-            if (FILTER) {
-                float fT = 0.0f;
-                int jT = 0;
-                if (req >= 0 && lv > c0) {
-                    // threshold composite -> (score, index); 0 means "keep all"
-                    const uint64_t T = A.thresh[r];
-                    fT = key_to_float((uint32_t)(T >> 32));
-                    jT = (int)(0xFFFFFFFFu - (uint32_t)T);
-                    if (T == 0ull) {
-                        fT = -__builtin_huge_valf();
-                        jT = 0x7FFFFFFF;
-                    }
+            // the threshold composite's score (an all-ones composite decodes
+            // to NaN, which no score reaches)
+            if (FILTER && new_tile) s_fT[t] = req >= 0 ? key_to_float((uint32_t)(A.thresh[r] >> 32)) : 0.0f;
+        }
+        if (new_tile) {
+            // query fragments of this wave's 16 rows
+#pragma unroll
+            for (int t = 0; t < S::NQ; ++t) {
+                const int m = lane & 31;
+                int row, h, s;
+                if (RELU) {  // MFMA tile t/8: rows 8*(t/8) + m/4, head m%4; slice t%8
+                    row = wave * S::RPW + (t / kSlices) * 8 + (m >> 2);
+                    h = m & 3;
+                    s = t % kSlices;
+                } else {     // MFMA row m = (row m/2, pair m%2); step t = (slice t/2, head 2*pair + t%2)
+                    row = wave * S::RPW + (m >> 1);
+                    h = 2 * (m & 1) + (t & 1);
+                    s = t >> 1;
                 }
-                s_fT[t] = fT;
-                s_jT[t] = jT;
+                row += r0;
+                half8 v = {};
+                if (row < a.rows)
+                    v = *reinterpret_cast<const half8*>(a.q + ((int64_t)row * kHeads + h) * kHeadDim + 16 * s +
+                                                        8 * (lane >> 5));
+                qa[t] = v;
             }
         }
         __syncthreads();
-
-        // kept-candidate counts of this wave's 16 rows (output o, lane half)
-        int cnt_lo[ScoreShape::NOUT], cnt_hi[ScoreShape::NOUT];
+        if (FILTER && new_tile) {
 #pragma unroll
-        for (int o = 0; o < ScoreShape::NOUT; ++o) cnt_lo[o] = cnt_hi[o] = 0;
+            for (int o = 0; o < NOUT; ++o) fT[o] = s_fT[out_tile_row<RELU>(o, wave, lane)];
+        }
+        loaded_tile = tile;
+
+        // kept-entry counts of this wave's 16 rows (output o, lane half)
+        int cnt_lo[NOUT], cnt_hi[NOUT];
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o) cnt_lo[o] = cnt_hi[o] = 0;
 
         for (;;) {
             // one pass per request present among the tile's pending rows
@@ -214,38 +248,18 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                 const int pg = min(max(ptrow[lp], 0), a.num_pages - 1);
                 s_slot[i] = (uint32_t)pg * (uint32_t)a.kpp + (uint32_t)slot;
             }
-
-            // query fragments: MFMA tile mt of this wave holds rows
-            // r0 + 16*wave + 8*mt .. +7, MFMA row m = 4*(row offset) + head
-            half8 qa[2 * kSlices];
-#pragma unroll
-            for (int t = 0; t < 2 * kSlices; ++t) {
-                const int mt = t / kSlices, s = t % kSlices, m = lane & 31;
-                const int row = r0 + wave * 16 + mt * 8 + (m >> 2);
-                const int h = m & 3;
-                half8 v = {};
-                if (row < a.rows)
-                    v = *reinterpret_cast<const half8*>(a.q + ((int64_t)row * kHeads + h) * kHeadDim + 16 * s +
-                                                        8 * (lane >> 5));
-                qa[t] = v;
-            }
-            // smallest visible bound over this wave's rows: steps entirely
-            // below it need no per-row mask
+            // smallest visible bound over this wave's rows: column tiles
+            // entirely below it need no per-row mask
             int wlim = 0x7FFFFFFF;
             for (int t = lane; t < S::RPW; t += 64) wlim = min(wlim, s_lim[wave * S::RPW + t]);
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) wlim = min(wlim, __shfl_xor(wlim, o, 64));
             __syncthreads();
 
-            float fT[NOUT];
-#pragma unroll
-            for (int o = 0; o < NOUT; ++o) fT[o] = FILTER ? s_fT[out_tile_row(o, wave, lane)] : 0.0f;
-
-            // Step i: barrier (tile i staged) -> issue the loads of tile i+1
-            // -> MFMAs on tile i -> wait for tile i+1 and stage it in the other
-            // buffer -> epilogue of tile i.  The epilogue's global stores are
-            // issued after the wait, so they drain during the next step's
-            // MFMAs instead of being waited on.
+            // Step: barrier (tile staged) -> issue the loads of the next tile
+            // -> MFMAs -> wait for the next tile and stage it in the other
+            // buffer -> epilogue.  The epilogue's global stores are issued
+            // after the wait, so they drain during the next step's MFMAs.
             const _Float16* kc = a.kcache;
             u32x4 pf[S::NLOAD];
 #pragma unroll
@@ -259,6 +273,7 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                 const int flat = i * NT + tid, n = flat >> 4, c = flat & 15;
                 *reinterpret_cast<u32x4*>(s_keys[0] + lds_key_chunk(n, c)) = pf[i];
             }
+            const int tr0 = out_tile_row<RELU>(0, wave, lane);
             int buf = 0;
             for (int j0 = c0; j0 < cend; j0 += kStepKeys) {
                 __syncthreads();
@@ -271,39 +286,88 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                 }
                 // keep the prefetch issued here, ahead of the MFMAs that hide it
                 __builtin_amdgcn_sched_barrier(0);
-                float16v acc[2];
+
+                float sc[kSub][NOUT];
+                if (RELU) {
+                    float16v acc[kSub][2];
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) acc[mt] = float16v{};
+                    for (int st = 0; st < kSub; ++st) acc[st][0] = acc[st][1] = float16v{};
 #pragma unroll
-                for (int s = 0; s < kSlices; ++s) {
-                    const half8 kbs = *reinterpret_cast<const half8*>(sk + lds_key_chunk(lane & 31, 2 * s + (lane >> 5)));
+                    for (int s = 0; s < kSlices; ++s) {
+                        half8 kbs[kSub];
 #pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) acc[mt] = mfma32(qa[mt * kSlices + s], kbs, acc[mt]);
+                        for (int st = 0; st < kSub; ++st)
+                            kbs[st] = *reinterpret_cast<const half8*>(
+                                sk + lds_key_chunk(32 * st + (lane & 31), 2 * s + (lane >> 5)));
+#pragma unroll
+                        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                            for (int st = 0; st < kSub; ++st)
+                                acc[st][mt] = mfma32(qa[mt * kSlices + s], kbs[st], acc[st][mt]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int st = 0; st < kSub; ++st)
+#pragma unroll
+                        for (int o = 0; o < NOUT; ++o) {
+                            const int mt = o >> 2, g = o & 3;
+                            sc[st][o] = combine_relu_heads(acc[st][mt][4 * g], acc[st][mt][4 * g + 1],
+                                                           acc[st][mt][4 * g + 2], acc[st][mt][4 * g + 3]);
+                        }
+                } else {
+                    float16v acc[kSub];
+#pragma unroll
+                    for (int st = 0; st < kSub; ++st) acc[st] = float16v{};
+#pragma unroll
+                    for (int s = 0; s < kSlices; ++s) {
+                        half8 kbs[kSub];
+#pragma unroll
+                        for (int st = 0; st < kSub; ++st)
+                            kbs[st] = *reinterpret_cast<const half8*>(
+                                sk + lds_key_chunk(32 * st + (lane & 31), 2 * s + (lane >> 5)));
+#pragma unroll
+                        for (int t = 2 * s; t < 2 * s + 2; ++t)
+#pragma unroll
+                            for (int st = 0; st < kSub; ++st) acc[st] = mfma32(qa[t], kbs[st], acc[st]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int st = 0; st < kSub; ++st)
+#pragma unroll
+                        for (int o = 0; o < NOUT; ++o) sc[st][o] = combine_pairs(acc[st][2 * o], acc[st][2 * o + 1]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
-                // (after the last step this fills the idle buffer, which no
-                // wave reads any more: every wave has passed this step's barrier)
+                // stage the prefetched tile in the idle buffer (after the last
+                // step this fills a buffer no wave reads any more: every wave
+                // has passed this step's barrier)
 #pragma unroll
                 for (int i = 0; i < S::NLOAD; ++i) {
                     const int flat = i * NT + tid, n = flat >> 4, c = flat & 15;
                     *reinterpret_cast<u32x4*>(s_keys[buf ^ 1] + lds_key_chunk(n, c)) = pf[i];
                 }
-                const int jn = j0 + (lane & 31);  // this lane's key (logical index)
-                const bool full = j0 + kStepKeys <= wlim;
+
 #pragma unroll
-                for (int o = 0; o < NOUT; ++o) {
-                    const int mt = o >> 2, g = o & 3;
-                    const float sc = combine_heads<RELU>(acc[mt][4 * g], acc[mt][4 * g + 1], acc[mt][4 * g + 2],
-                                                         acc[mt][4 * g + 3]);
-                    const int tr = out_tile_row(o, wave, lane);
+                for (int st = 0; st < kSub; ++st) {
+                    const int jn = j0 + 32 * st + (lane & 31);  // this lane's key (logical index)
+                    const bool full = j0 + 32 * (st + 1) <= wlim;
                     if (!FILTER) {
-                        if (full || jn < s_lim[tr]) A.out[(int64_t)(r0 + tr) * A.ld + jn] = sc;
+                        float* base = A.out + (int64_t)(r0 + tr0) * A.ld + jn;
+                        if (full) {
+#pragma unroll
+                            for (int o = 0; o < NOUT; ++o) base[(int64_t)out_row_offset<RELU>(o) * A.ld] = sc[st][o];
+                        } else {
+#pragma unroll
+                            for (int o = 0; o < NOUT; ++o)
+                                if (jn < s_lim[tr0 + out_row_offset<RELU>(o)])
+                                    base[(int64_t)out_row_offset<RELU>(o) * A.ld] = sc[st][o];
+                        }
                     } else {
-                        // keep iff composite (sc, jn) >= (fT, jT) and the key is visible
-                        bool c = sc >= fT[o];
-                        if (!full) c = c && jn < s_lim[tr];
-                        if (__any(c && sc == fT[o])) c = c && (sc > fT[o] || jn <= s_jT[tr]);
-                        filter_append(A, c, sc, tr, r0, jn, lane, cnt_lo[o], cnt_hi[o], s_lbuf);
+#pragma unroll
+                        for (int o = 0; o < NOUT; ++o) {
+                            const int tr = tr0 + out_row_offset<RELU>(o);
+                            bool c = sc[st][o] >= fT[o];
+                            if (!full) c = c && jn < s_lim[tr];
+                            filter_append(A, c, sc[st][o], tr, r0, jn, lane, cnt_lo[o], cnt_hi[o], s_lbuf);
+                        }
                     }
                 }
                 buf ^= 1;
@@ -313,12 +377,12 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
         }
 
         if (FILTER) {
-            // flush the staged candidates: one global atomic per row
+            // flush the staged entries: one global atomic per row
             if (lane == 0) {
 #pragma unroll
                 for (int o = 0; o < NOUT; ++o) {
-                    s_lc[out_tile_row(o, wave, 0)] = cnt_lo[o];
-                    s_lc[out_tile_row(o, wave, 32)] = cnt_hi[o];
+                    s_lc[out_tile_row<RELU>(o, wave, 0)] = cnt_lo[o];
+                    s_lc[out_tile_row<RELU>(o, wave, 32)] = cnt_hi[o];
                 }
             }
             __syncthreads();

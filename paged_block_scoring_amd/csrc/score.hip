@@ -7,8 +7,9 @@
 namespace qsa {
 namespace {
 
-// Even shares of each XCD's (tile, key) positions: about `wg_per_cu`
-// workgroups per compute unit, but no share below `min_seg` positions.
+// Even shares of each XCD's (tile, key) positions, in whole stages: about
+// `wg_per_cu` workgroups per compute unit, but no share below `min_seg`
+// positions (a multiple of kStepKeys).
 template <bool RELU, Epi EPI>
 hipError_t launch_form(ScoreKernelArgs A, int32_t cus, int32_t wg_per_cu, int64_t min_seg, hipStream_t stream) {
     using S = ScoreShape;
@@ -17,7 +18,7 @@ hipError_t launch_form(ScoreKernelArgs A, int32_t cus, int32_t wg_per_cu, int64_
     A.xcd_keys = (int32_t)stripe;
     const int64_t positions = (int64_t)A.tiles * stripe;
     int64_t per_xcd = (int64_t)(cus / kXcds > 0 ? cus / kXcds : 1) * wg_per_cu;
-    int64_t seg = (positions + per_xcd - 1) / per_xcd;
+    int64_t seg = ((positions + per_xcd - 1) / per_xcd + kStepKeys - 1) / kStepKeys * kStepKeys;
     if (seg < min_seg) seg = min_seg;
     per_xcd = (positions + seg - 1) / seg;
     A.seg_len = seg;
@@ -42,6 +43,7 @@ hipError_t launch_score_store(const PagedArgs& a, int32_t stride, float* out, in
     A.lmax = (a.max_visible + stride - 1) / stride;
     A.out = out;
     A.ld = ld;
+    A.vec_store = (ld % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) ? 1 : 0;
     return launch_epi<Epi::Store>(A, cus, stream);
 }
 

@@ -24,13 +24,20 @@
 // current ones are consumed from one half of a double-buffered, XOR-swizzled
 // LDS tile (one barrier per 64 keys = two 32-key MFMA column tiles, whose
 // MFMA chains are interleaved).  The MFMA arrangements are the canonical ones
-// of qsa_device.hpp.  Each visible score goes to the epilogue:
-//   Store  -- out[row*ld + i] = score (two-pass arm, sampling pass);
+// of qsa_device.hpp.
+//
+// Epilogue.  A 32-key column tile leaves each wave 16 rows x 32 scores spread
+// over the MFMA output layout.  The wave transposes them through a small LDS
+// buffer of its own so that each lane holds 8 consecutive keys of one row
+// (lanes 4r..4r+3 share row r):
+//   Store  -- out[row*ld + i] = score with two 16-byte stores per lane
+//             (two-pass arm, sampling pass);
 //   Filter -- keep (score, key) if score >= the row's threshold score: one
-//             compare per score; kept entries get slots from wave-uniform
-//             per-row counters (ballot + mbcnt), are staged per row in LDS
-//             as (score bits, key) and appended to the row's global list with
-//             one atomic per row and piece.
+//             compare per score against a per-lane threshold; a quad prefix
+//             sum gives each kept entry its slot in the row's LDS staging list
+//             (score bits, key), which the wave moves to the row's global
+//             list -- one atomic per row -- when it would overflow and when
+//             the workgroup leaves the tile.  No other synchronisation.
 // Rows of different requests in one tile are processed in successive passes.
 #pragma once
 
@@ -47,17 +54,19 @@ constexpr int kMaxPiece = 1024;        // logical keys per piece (slot-table siz
 constexpr int kLCap = 64;              // per-row LDS staging slots of the Filter epilogue
 constexpr int kTileRows = 64;          // rows per tile
 constexpr int kXcds = 8;               // XCDs of an MI355X (256 CUs = 8 x 32)
+constexpr int kTrStride = 36;          // floats per row of the transpose buffer (32 + 4: conflict-free reads)
 
 struct ScoreKernelArgs {
     PagedArgs a;
     int32_t stride;    // logical key i is key stride*i
     int32_t lmax;      // logical keys of the longest row: ceil(max_visible / stride)
     int32_t tiles;     // ceil(rows / kTileRows)
-    int32_t xcd_keys;  // logical keys per XCD stripe
-    int64_t seg_len;   // (tile, key) positions per workgroup
+    int32_t xcd_keys;  // logical keys per XCD stripe (a multiple of kStepKeys)
+    int64_t seg_len;   // (tile, key) positions per workgroup (a multiple of kStepKeys)
     // Store
     float* out;
     int64_t ld;
+    int32_t vec_store;  // out and ld allow 16-byte stores
     // Filter
     const uint64_t* thresh;  // [rows] threshold composite; only its score is used
     uint64_t* cand;          // [rows][cand_cap] entries (score bits << 32 | key)
@@ -73,9 +82,10 @@ struct ScoreShape {
     static constexpr int NOUT = 8;                                   // scores per lane per 32 keys
     static constexpr int NQ = 2 * kSlices;                           // query fragments per lane
 };
+static_assert(ScoreShape::NLOAD == 4, "each thread stages 4 consecutive keys per stage");
 
-// Row (within the wave's 16) of output o of a lane in lane half 0; lane half
-// 1 adds out_half_offset.  Default form: MFMA rows 8*(v/4) + (v%4) hold
+// Row (within the wave's 16) of MFMA output o of a lane in lane half 0; lane
+// half 1 adds out_half_offset.  Default form: MFMA rows 8*(v/4) + (v%4) hold
 // (row, pair) = (m/2, m%2), so outputs o = v/2 are rows 4*(o/2) + o%2 and the
 // upper lane half (MFMA rows +4) is rows +2.  Relu form: outputs o = 4*mt + g
 // of MFMA tile mt are rows 8*mt + 2*g, and the upper lane half is rows +1.
@@ -87,36 +97,32 @@ template <bool RELU>
 __device__ __forceinline__ constexpr int out_half_offset() {
     return RELU ? 1 : 2;
 }
-template <bool RELU>
-__device__ __forceinline__ int out_tile_row(int o, int wave, int lane) {
-    return wave * ScoreShape::RPW + out_half_offset<RELU>() * (lane >> 5) + out_row_offset<RELU>(o);
+
+// Quad (lanes 4k..4k+3) exclusive prefix sum of x; *total gets the quad sum.
+__device__ __forceinline__ int quad_exclusive_sum(int x, int* total) {
+    const int q = threadIdx.x & 3;
+    // quad_perm(0,0,1,2): lane q reads lane q-1 (lane 0 reads itself)
+    const int a = __builtin_amdgcn_mov_dpp(x, 0x90, 0xF, 0xF, false);
+    const int s1 = x + (q >= 1 ? a : 0);
+    // quad_perm(0,0,0,1): lanes 2, 3 read lanes 0, 1
+    const int b = __builtin_amdgcn_mov_dpp(s1, 0x40, 0xF, 0xF, false);
+    const int incl = s1 + (q >= 2 ? b : 0);
+    // quad_perm(3,3,3,3): everyone reads lane 3
+    *total = __builtin_amdgcn_mov_dpp(incl, 0xFF, 0xF, 0xF, false);
+    return incl - x;
 }
 
-// Filter epilogue for one output index o of a wave: `c` is this lane's keep
-// decision for (tile row tr, key jn).  The two 32-lane halves of the wave
-// hold two different rows, each owned by this wave alone, so the slot of a
-// kept entry is the row's running count (a wave-uniform value) plus the
-// lane's rank among the kept lanes of its half; no atomics unless the row's
-// LDS staging is full.
-__device__ __forceinline__ void filter_append(const ScoreKernelArgs& A, bool c, float sc, int tr, int r0, int jn,
-                                              int lane, int& cnt_lo, int& cnt_hi, uint64_t* s_lbuf) {
-    const uint64_t m = __ballot(c);
-    if (m == 0ull) return;
-    const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
-    const bool upper = lane >= 32;
-    const int rank = (int)__builtin_amdgcn_mbcnt_hi(upper ? hi : 0u, __builtin_amdgcn_mbcnt_lo(upper ? 0u : lo, 0u));
-    const int slot = (upper ? cnt_hi : cnt_lo) + rank;
-    cnt_lo += __popc(lo);
-    cnt_hi += __popc(hi);
-    if (c) {
-        const uint64_t e = ((uint64_t)__float_as_uint(sc) << 32) | (uint32_t)jn;
-        if (slot < kLCap) {
-            s_lbuf[tr * kLCap + slot] = e;
-        } else {
-            const int g = atomicAdd(&A.cand_count[r0 + tr], 1);
-            if (g < A.cand_cap) A.cand[(int64_t)(r0 + tr) * A.cand_cap + g] = e;
-        }
-    }
+// Moves this wave's staged entries of tile rows (one row per quad, `row` =
+// its global row) to the rows' global candidate lists: the quad's first lane
+// reserves space with one atomic, the quad copies.  Wave-local.
+__device__ __forceinline__ void flush_staged(const ScoreKernelArgs& A, const uint64_t* lb, int row, int& cnt) {
+    int base = 0;
+    if ((threadIdx.x & 3) == 0 && cnt > 0) base = atomicAdd(&A.cand_count[row], cnt);
+    base = __builtin_amdgcn_mov_dpp(base, 0x00, 0xF, 0xF, false);  // quad_perm(0,0,0,0)
+    uint64_t* dst = A.cand + (int64_t)row * A.cand_cap;
+    for (int i = threadIdx.x & 3; i < cnt; i += 4)
+        if (base + i < A.cand_cap) dst[base + i] = lb[i];
+    cnt = 0;
 }
 
 template <bool RELU, Epi EPI>
@@ -126,10 +132,10 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
     constexpr bool FILTER = EPI == Epi::Filter;
 
     __shared__ __attribute__((aligned(16))) unsigned char s_keys[2][kStepKeys * kKeyBytes];
-    __shared__ uint32_t s_slot[kMaxPiece];
+    __shared__ __attribute__((aligned(16))) uint32_t s_slot[kMaxPiece];
+    __shared__ __attribute__((aligned(16))) float s_tr[S::WAVES][S::RPW * kTrStride];
     __shared__ int32_t s_req[kTileRows], s_lv[kTileRows], s_todo[kTileRows], s_lim[kTileRows];
     __shared__ float s_fT[FILTER ? kTileRows : 1];
-    __shared__ int32_t s_lc[FILTER ? kTileRows : 1];
     __shared__ uint64_t s_lbuf[FILTER ? kTileRows * kLCap : 1];
     __shared__ int32_t s_act, s_vmax;
 
@@ -137,15 +143,29 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int xcd = blockIdx.x % kXcds, loc = blockIdx.x / kXcds;
     const int xk0 = xcd * A.xcd_keys;
-    const int span = min(A.xcd_keys, A.lmax - xk0);
+    // keys of this XCD's stripe, padded to whole stages so that every piece
+    // starts on a stage boundary (keys past the end are invisible to every row)
+    const int span = min(A.xcd_keys, (A.lmax - xk0 + kStepKeys - 1) / kStepKeys * kStepKeys);
     if (span <= 0) return;
     const int64_t total = (int64_t)A.tiles * span;
     int64_t p = (int64_t)loc * A.seg_len;
     const int64_t pend = min(p + A.seg_len, total);
 
+    // staging: this thread's 4 consecutive keys of a stage and its chunk
+    const int pk = 4 * (tid >> 4), pc = tid & 15;
+    // transposed epilogue: this lane's row of the wave and its 8 keys of a column tile
+    const int rr = lane >> 2, cq = lane & 3;
+    const int trow = wave * S::RPW + rr;
+    float* const tw = s_tr[wave];
+
+    // every slot-table entry always holds a valid cache slot, so the prefetch
+    // may read entries past the end of a pass's table
+    for (int i = tid; i < kMaxPiece; i += NT) s_slot[i] = 0u;
+
     half8 qa[S::NQ];
-    float fT[NOUT];
-    int loaded_tile = -1;
+    float fT_r = 0.0f;  // threshold score of this lane's row (Filter)
+    int cnt_r = 0;      // staged entries of this lane's row (Filter)
+    int tile_r0 = -1;   // first row of the tile held in registers
 
     while (p < pend) {
         const int tile = (int)(p / span);
@@ -154,7 +174,8 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
         const int c0 = xk0 + off, c1 = c0 + len;
         p += len;
         const int r0 = tile * kTileRows;
-        const bool new_tile = tile != loaded_tile;
+        const bool new_tile = r0 != tile_r0;
+        if (FILTER && new_tile && tile_r0 >= 0) flush_staged(A, s_lbuf + trow * kLCap, tile_r0 + trow, cnt_r);
 
         for (int t = tid; t < kTileRows; t += NT) {
             const int r = r0 + t;
@@ -199,16 +220,8 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
             }
         }
         __syncthreads();
-        if (FILTER && new_tile) {
-#pragma unroll
-            for (int o = 0; o < NOUT; ++o) fT[o] = s_fT[out_tile_row<RELU>(o, wave, lane)];
-        }
-        loaded_tile = tile;
-
-        // kept-entry counts of this wave's 16 rows (output o, lane half)
-        int cnt_lo[NOUT], cnt_hi[NOUT];
-#pragma unroll
-        for (int o = 0; o < NOUT; ++o) cnt_lo[o] = cnt_hi[o] = 0;
+        if (FILTER && new_tile) fT_r = s_fT[trow];
+        tile_r0 = r0;
 
         for (;;) {
             // one pass per request present among the tile's pending rows
@@ -248,12 +261,13 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                 const int pg = min(max(ptrow[lp], 0), a.num_pages - 1);
                 s_slot[i] = (uint32_t)pg * (uint32_t)a.kpp + (uint32_t)slot;
             }
-            // smallest visible bound over this wave's rows: column tiles
-            // entirely below it need no per-row mask
-            int wlim = 0x7FFFFFFF;
-            for (int t = lane; t < S::RPW; t += 64) wlim = min(wlim, s_lim[wave * S::RPW + t]);
+            // this lane's row bound, and the smallest over the wave's rows:
+            // column tiles entirely below it need no per-row mask
+            const int lim_r = s_lim[trow];
+            int wlim = lim_r;
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) wlim = min(wlim, __shfl_xor(wlim, o, 64));
+            for (int o = 4; o < 64; o <<= 1) wlim = min(wlim, __shfl_xor(wlim, o, 64));
+            wlim = __builtin_amdgcn_readfirstlane(wlim);
             __syncthreads();
 
             // Step: barrier (tile staged) -> issue the loads of the next tile
@@ -262,27 +276,25 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
             // after the wait, so they drain during the next step's MFMAs.
             const _Float16* kc = a.kcache;
             u32x4 pf[S::NLOAD];
+            {
+                const u32x4 sl = *reinterpret_cast<const u32x4*>(&s_slot[pk]);
 #pragma unroll
-            for (int i = 0; i < S::NLOAD; ++i) {
-                const int flat = i * NT + tid, n = flat >> 4, c = flat & 15;
-                const int li = min(c0 + n, cend - 1) - c0;
-                pf[i] = *reinterpret_cast<const u32x4*>(kc + (size_t)s_slot[li] * kHeadDim + c * 8);
-            }
+                for (int i = 0; i < S::NLOAD; ++i)
+                    pf[i] = *reinterpret_cast<const u32x4*>(kc + (size_t)sl[i] * kHeadDim + pc * 8);
 #pragma unroll
-            for (int i = 0; i < S::NLOAD; ++i) {
-                const int flat = i * NT + tid, n = flat >> 4, c = flat & 15;
-                *reinterpret_cast<u32x4*>(s_keys[0] + lds_key_chunk(n, c)) = pf[i];
+                for (int i = 0; i < S::NLOAD; ++i)
+                    *reinterpret_cast<u32x4*>(s_keys[0] + lds_key_chunk(pk + i, pc)) = pf[i];
             }
-            const int tr0 = out_tile_row<RELU>(0, wave, lane);
             int buf = 0;
             for (int j0 = c0; j0 < cend; j0 += kStepKeys) {
                 __syncthreads();
                 const unsigned char* sk = s_keys[buf];
+                {
+                    const int li = min(j0 + kStepKeys - c0 + pk, kMaxPiece - 4);
+                    const u32x4 sl = *reinterpret_cast<const u32x4*>(&s_slot[li]);
 #pragma unroll
-                for (int i = 0; i < S::NLOAD; ++i) {
-                    const int flat = i * NT + tid, n = flat >> 4, c = flat & 15;
-                    const int li = min(j0 + kStepKeys + n, cend - 1) - c0;
-                    pf[i] = *reinterpret_cast<const u32x4*>(kc + (size_t)s_slot[li] * kHeadDim + c * 8);
+                    for (int i = 0; i < S::NLOAD; ++i)
+                        pf[i] = *reinterpret_cast<const u32x4*>(kc + (size_t)sl[i] * kHeadDim + pc * 8);
                 }
                 // keep the prefetch issued here, ahead of the MFMAs that hide it
                 __builtin_amdgcn_sched_barrier(0);
@@ -340,34 +352,49 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                 // step this fills a buffer no wave reads any more: every wave
                 // has passed this step's barrier)
 #pragma unroll
-                for (int i = 0; i < S::NLOAD; ++i) {
-                    const int flat = i * NT + tid, n = flat >> 4, c = flat & 15;
-                    *reinterpret_cast<u32x4*>(s_keys[buf ^ 1] + lds_key_chunk(n, c)) = pf[i];
-                }
+                for (int i = 0; i < S::NLOAD; ++i)
+                    *reinterpret_cast<u32x4*>(s_keys[buf ^ 1] + lds_key_chunk(pk + i, pc)) = pf[i];
 
 #pragma unroll
                 for (int st = 0; st < kSub; ++st) {
-                    const int jn = j0 + 32 * st + (lane & 31);  // this lane's key (logical index)
+                    // transpose: lane (row rr, keys 8cq..8cq+7) of this column tile
+                    const int wr = out_half_offset<RELU>() * (lane >> 5);
+#pragma unroll
+                    for (int o = 0; o < NOUT; ++o) tw[(wr + out_row_offset<RELU>(o)) * kTrStride + (lane & 31)] = sc[st][o];
+                    __builtin_amdgcn_wave_barrier();
+                    const float4v v0 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq);
+                    const float4v v1 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq + 4);
+                    __builtin_amdgcn_wave_barrier();
+                    const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    const int key0 = j0 + 32 * st + 8 * cq;
                     const bool full = j0 + 32 * (st + 1) <= wlim;
                     if (!FILTER) {
-                        float* base = A.out + (int64_t)(r0 + tr0) * A.ld + jn;
-                        if (full) {
-#pragma unroll
-                            for (int o = 0; o < NOUT; ++o) base[(int64_t)out_row_offset<RELU>(o) * A.ld] = sc[st][o];
+                        float* dst = A.out + (int64_t)(r0 + trow) * A.ld + key0;
+                        if (full && A.vec_store) {
+                            *reinterpret_cast<float4v*>(dst) = v0;
+                            *reinterpret_cast<float4v*>(dst + 4) = v1;
                         } else {
 #pragma unroll
-                            for (int o = 0; o < NOUT; ++o)
-                                if (jn < s_lim[tr0 + out_row_offset<RELU>(o)])
-                                    base[(int64_t)out_row_offset<RELU>(o) * A.ld] = sc[st][o];
+                            for (int i = 0; i < 8; ++i)
+                                if (full || key0 + i < lim_r) dst[i] = v[i];
                         }
                     } else {
+                        bool kp[8];
+                        int n = 0;
 #pragma unroll
-                        for (int o = 0; o < NOUT; ++o) {
-                            const int tr = tr0 + out_row_offset<RELU>(o);
-                            bool c = sc[st][o] >= fT[o];
-                            if (!full) c = c && jn < s_lim[tr];
-                            filter_append(A, c, sc[st][o], tr, r0, jn, lane, cnt_lo[o], cnt_hi[o], s_lbuf);
+                        for (int i = 0; i < 8; ++i) {
+                            kp[i] = v[i] >= fT_r && (full || key0 + i < lim_r);
+                            n += kp[i] ? 1 : 0;
                         }
+                        int tot;
+                        const int excl = quad_exclusive_sum(n, &tot);
+                        uint64_t* lb = s_lbuf + trow * kLCap;
+                        if (__any(cnt_r + tot > kLCap)) flush_staged(A, lb, r0 + trow, cnt_r);
+                        int slot = cnt_r + excl;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            if (kp[i]) lb[slot++] = ((uint64_t)__float_as_uint(v[i]) << 32) | (uint32_t)(key0 + i);
+                        cnt_r += tot;
                     }
                 }
                 buf ^= 1;
@@ -375,30 +402,9 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
             // every wave is done with this pass's s_lim before wave 0 rewrites it
             __syncthreads();
         }
-
-        if (FILTER) {
-            // flush the staged entries: one global atomic per row
-            if (lane == 0) {
-#pragma unroll
-                for (int o = 0; o < NOUT; ++o) {
-                    s_lc[out_tile_row<RELU>(o, wave, 0)] = cnt_lo[o];
-                    s_lc[out_tile_row<RELU>(o, wave, 32)] = cnt_hi[o];
-                }
-            }
-            __syncthreads();
-            for (int t = wave; t < kTileRows; t += S::WAVES) {
-                const int n = min(s_lc[t], kLCap);
-                if (n == 0) continue;
-                const int row = r0 + t;
-                int base = 0;
-                if (lane == 0) base = atomicAdd(&A.cand_count[row], n);
-                base = __shfl(base, 0, 64);
-                for (int i = lane; i < n; i += 64)
-                    if (base + i < A.cand_cap) A.cand[(int64_t)row * A.cand_cap + base + i] = s_lbuf[t * kLCap + i];
-            }
-        }
         __syncthreads();
     }
+    if (FILTER && tile_r0 >= 0) flush_staged(A, s_lbuf + trow * kLCap, tile_r0 + trow, cnt_r);
 }
 
 }  // namespace qsa

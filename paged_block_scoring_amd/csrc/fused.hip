@@ -91,8 +91,8 @@ constexpr int kFinWaves = kFinNT / 64;
 // Exact top-kb of one row by recomputation: each wave scores 32 keys at a
 // time straight from the cache with the same MFMA sequences as the tiled
 // scorer, with the row in MFMA row slot 0 and zero query fragments elsewhere
-// (default form: MFMA rows 0, 1 are the two head pairs; relu form: rows 0..3
-// are the four heads).  Composites above the running cutoff are appended in
+// (default form: MFMA row 0 is the row, heads in K; relu form: rows 0..3 are
+// the four heads).  Composites above the running cutoff are appended in
 // LDS, and the buffer is cut back to its kb largest whenever it exceeds kb.
 // Leaves the selected composites (unsorted) in a[0 .. return value).
 template <int CAPL>
@@ -134,13 +134,13 @@ __device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* 
                 sc = combine_relu_heads(acc[0], acc[1], acc[2], acc[3]);
             } else {
 #pragma unroll
-                for (int t = 0; t < 2 * kSlices; ++t) {
+                for (int t = 0; t < kHeads * kSlices; ++t) {
                     half8 qv = {};
-                    const int s = t >> 1, h = 2 * m + (t & 1);
-                    if (m < 2) qv = *reinterpret_cast<const half8*>(qrow + h * kHeadDim + 16 * s + 8 * g);
+                    const int s = t >> 2, h = t & 3;
+                    if (m == 0) qv = *reinterpret_cast<const half8*>(qrow + h * kHeadDim + 16 * s + 8 * g);
                     acc = mfma32(qv, kb8[s], acc);
                 }
-                sc = combine_pairs(acc[0], acc[1]);
+                sc = acc[0];
             }
             // lanes 0..31 hold MFMA row 0 (the row's score) for key j0 + lane
             if (g == 0 && j < cend) {

@@ -8,11 +8,11 @@
 // both operands, and the 32x32 output puts rows 8*(v/4) + 4*(l/32) + (v%4) of
 // column l%32 in accumulator element v of lane l.  Accumulation is fp32 from
 // +0 in the order given.
-//   default form (head pairs): MFMA row m = 2*row + p (16 query rows x 2 head
-//     pairs); a chain of 16 MFMAs, step t = (slice t/2, head 2p + t%2), adds
-//     both heads of pair p into one sum, so accumulator elements 2o and 2o+1
-//     of a lane are the two pair sums of one (row, key) and the score is
-//     pair0 + pair1.
+//   default form (heads in K): MFMA row = query row (32 per tile); a chain
+//     of 32 MFMAs, step t = (slice t/4, head t%4), accumulates the whole
+//     score q_0.k + q_1.k + q_2.k + q_3.k in one sum: the A operand of step t
+//     is head t%4 of the query, the B operand slice t/4 of the key.  Element v
+//     of a lane is the score of row 8*(v/4) + 4*(lane/32) + v%4.
 //   relu form (per head): MFMA row m = 4*row + head (8 query rows x 4 heads);
 //     a chain of 8 MFMAs over the slices gives every head's dot, elements
 //     4o'..4o'+3 are the four heads of one (row, key), and the score is
@@ -79,9 +79,6 @@ __device__ __forceinline__ uint32_t composite_index(uint64_t c) {
 __device__ __forceinline__ float16v mfma32(half8 a, half8 b, float16v c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
-
-// The two head-pair sums of one (row, key) -> score (default form).
-__device__ __forceinline__ float combine_pairs(float p0, float p1) { return p0 + p1; }
 
 // The four head dots of one (row, key) -> score (relu form).
 __device__ __forceinline__ float combine_relu_heads(float h0, float h1, float h2, float h3) {

@@ -13,7 +13,7 @@ namespace {
 template <bool RELU, Epi EPI>
 hipError_t launch_form(ScoreKernelArgs A, int32_t cus, int32_t wg_per_cu, int64_t min_seg, hipStream_t stream) {
     using S = ScoreShape;
-    A.tiles = (A.a.rows + kTileRows - 1) / kTileRows;
+    A.tiles = (A.a.rows + Form<RELU>::TILE - 1) / Form<RELU>::TILE;
     const int64_t stripe = ((int64_t)(A.lmax + kXcds - 1) / kXcds + kStepKeys - 1) / kStepKeys * kStepKeys;
     A.xcd_keys = (int32_t)stripe;
     const int64_t positions = (int64_t)A.tiles * stripe;

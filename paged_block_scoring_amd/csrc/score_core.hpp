@@ -8,7 +8,8 @@
 // above" (one key per ratio tokens shared by all heads; one score per query
 // token summed over heads).
 //
-// Work.  Rows are cut into tiles of 64 consecutive rows; the logical keys
+// Work.  Rows are cut into tiles of consecutive rows (128 in the default
+// form, 64 in the relu form: 4 waves of 32 or 16 rows); the logical keys
 // (logical key i is key stride*i of the request; stride is 1 except for the
 // sampling pass) are cut into 8 stripes, one per XCD.  Workgroup w runs on
 // XCD w % 8 (the hardware's round-robin dispatch) and owns a contiguous,
@@ -17,7 +18,7 @@
 // same amount of work.  A share is processed as pieces of one tile and at
 // most kMaxPiece keys.
 //
-// A piece.  Each of the 4 waves holds the fp16 query fragments of its 16 rows
+// A piece.  Each of the 4 waves holds the fp16 query fragments of its rows
 // in registers (loaded once per tile).  Keys are staged 64 at a time: a
 // per-piece table gives every logical key's slot in the cache; each thread
 // prefetches its 16-byte pieces of the next 64 keys into registers while the
@@ -26,10 +27,10 @@
 // MFMA chains are interleaved).  The MFMA arrangements are the canonical ones
 // of qsa_device.hpp.
 //
-// Epilogue.  A 32-key column tile leaves each wave 16 rows x 32 scores spread
-// over the MFMA output layout.  The wave transposes them through a small LDS
-// buffer of its own so that each lane holds 8 consecutive keys of one row
-// (lanes 4r..4r+3 share row r):
+// Epilogue.  A 32-key column tile leaves each wave 32 (or 16) rows x 32
+// scores spread over the MFMA output layout.  The wave transposes them, 16
+// rows at a time, through a small LDS buffer of its own so that each lane
+// holds 8 consecutive keys of one row (lanes 4r..4r+3 share row r):
 //   Store  -- out[row*ld + i] = score with two 16-byte stores per lane
 //             (two-pass arm, sampling pass);
 //   Filter -- keep (score, key) if score >= the row's threshold score: one
@@ -51,8 +52,8 @@ enum class Epi { Store, Filter };
 constexpr int kSub = 2;                // 32-key column tiles per LDS stage
 constexpr int kStepKeys = 32 * kSub;   // keys per LDS stage
 constexpr int kMaxPiece = 1024;        // logical keys per piece (slot-table size)
-constexpr int kLCap = 64;              // per-row LDS staging slots of the Filter epilogue
-constexpr int kTileRows = 64;          // rows per tile
+constexpr int kLCap = 32;              // per-row LDS staging slots of the Filter epilogue (>= 32)
+constexpr int kMaxTileRows = 128;      // rows per tile, largest form
 constexpr int kXcds = 8;               // XCDs of an MI355X (256 CUs = 8 x 32)
 constexpr int kTrStride = 36;          // floats per row of the transpose buffer (32 + 4: conflict-free reads)
 
@@ -60,7 +61,7 @@ struct ScoreKernelArgs {
     PagedArgs a;
     int32_t stride;    // logical key i is key stride*i
     int32_t lmax;      // logical keys of the longest row: ceil(max_visible / stride)
-    int32_t tiles;     // ceil(rows / kTileRows)
+    int32_t tiles;     // ceil(rows / rows per tile)
     int32_t xcd_keys;  // logical keys per XCD stripe (a multiple of kStepKeys)
     int64_t seg_len;   // (tile, key) positions per workgroup (a multiple of kStepKeys)
     // Store
@@ -77,26 +78,38 @@ struct ScoreKernelArgs {
 struct ScoreShape {
     static constexpr int WAVES = 4;
     static constexpr int NT = 64 * WAVES;
-    static constexpr int RPW = kTileRows / WAVES;                    // rows per wave
     static constexpr int NLOAD = kStepKeys * kChunksPerKey / NT;     // 16-byte pieces per thread per stage
-    static constexpr int NOUT = 8;                                   // scores per lane per 32 keys
-    static constexpr int NQ = 2 * kSlices;                           // query fragments per lane
 };
 static_assert(ScoreShape::NLOAD == 4, "each thread stages 4 consecutive keys per stage");
 
-// Row (within the wave's 16) of MFMA output o of a lane in lane half 0; lane
-// half 1 adds out_half_offset.  Default form: MFMA rows 8*(v/4) + (v%4) hold
-// (row, pair) = (m/2, m%2), so outputs o = v/2 are rows 4*(o/2) + o%2 and the
-// upper lane half (MFMA rows +4) is rows +2.  Relu form: outputs o = 4*mt + g
-// of MFMA tile mt are rows 8*mt + 2*g, and the upper lane half is rows +1.
+// The two MFMA arrangements (qsa_device.hpp), as seen by the tiled kernel.
+// A lane's MFMA outputs for a 32-key column tile come in rounds of 8 scores
+// that cover 16 rows of the wave; out_row(o) is the row (within the round) of
+// output o in lane half 0, and lane half 1 adds HALF.
 template <bool RELU>
-__device__ __forceinline__ constexpr int out_row_offset(int o) {
-    return RELU ? 8 * (o >> 2) + 2 * (o & 3) : 4 * (o >> 1) + (o & 1);
-}
-template <bool RELU>
-__device__ __forceinline__ constexpr int out_half_offset() {
-    return RELU ? 1 : 2;
-}
+struct Form;
+// default form: heads in K; MFMA row = query row (32 per wave); output
+// element v of the 16 is row 8*(v/4) + 4*(lane/32) + v%4, i.e. round v/8
+template <>
+struct Form<false> {
+    static constexpr int RPW = 32;                 // rows per wave
+    static constexpr int TILE = 4 * RPW;           // rows per tile
+    static constexpr int NQ = kHeads * kSlices;    // query fragments per lane: (slice, head)
+    static constexpr int ROUNDS = 2;
+    static constexpr int HALF = 4;
+    __device__ static constexpr int out_row(int o) { return 8 * (o >> 2) + (o & 3); }
+};
+// relu form: heads in M; two MFMA tiles of 8 rows x 4 heads per wave; the
+// head-combined outputs o = 4*mt + g are rows 8*mt + 2*g (+1 for lane half 1)
+template <>
+struct Form<true> {
+    static constexpr int RPW = 16;
+    static constexpr int TILE = 4 * RPW;
+    static constexpr int NQ = 2 * kSlices;
+    static constexpr int ROUNDS = 1;
+    static constexpr int HALF = 1;
+    __device__ static constexpr int out_row(int o) { return 8 * (o >> 2) + 2 * (o & 3); }
+};
 
 // Quad (lanes 4k..4k+3) exclusive prefix sum of x; *total gets the quad sum.
 __device__ __forceinline__ int quad_exclusive_sum(int x, int* total) {
@@ -128,15 +141,16 @@ __device__ __forceinline__ void flush_staged(const ScoreKernelArgs& A, const uin
 template <bool RELU, Epi EPI>
 __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKernelArgs A) {
     using S = ScoreShape;
-    constexpr int NT = S::NT, NOUT = S::NOUT;
+    using F = Form<RELU>;
+    constexpr int NT = S::NT, TILE = F::TILE, RPW = F::RPW, ROUNDS = F::ROUNDS;
     constexpr bool FILTER = EPI == Epi::Filter;
 
     __shared__ __attribute__((aligned(16))) unsigned char s_keys[2][kStepKeys * kKeyBytes];
     __shared__ __attribute__((aligned(16))) uint32_t s_slot[kMaxPiece];
-    __shared__ __attribute__((aligned(16))) float s_tr[S::WAVES][S::RPW * kTrStride];
-    __shared__ int32_t s_req[kTileRows], s_lv[kTileRows], s_todo[kTileRows], s_lim[kTileRows];
-    __shared__ float s_fT[FILTER ? kTileRows : 1];
-    __shared__ uint64_t s_lbuf[FILTER ? kTileRows * kLCap : 1];
+    __shared__ __attribute__((aligned(16))) float s_tr[S::WAVES][16 * kTrStride];
+    __shared__ int32_t s_req[TILE], s_lv[TILE], s_todo[TILE], s_lim[TILE];
+    __shared__ float s_fT[FILTER ? TILE : 1];
+    __shared__ uint64_t s_lbuf[FILTER ? TILE * kLCap : 1];
     __shared__ int32_t s_act, s_vmax;
 
     const PagedArgs& a = A.a;
@@ -153,19 +167,27 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
 
     // staging: this thread's 4 consecutive keys of a stage and its chunk
     const int pk = 4 * (tid >> 4), pc = tid & 15;
-    // transposed epilogue: this lane's row of the wave and its 8 keys of a column tile
+    // transposed epilogue: this lane's rows of the wave (rr + 16*round) and
+    // its 8 keys of a column tile
     const int rr = lane >> 2, cq = lane & 3;
-    const int trow = wave * S::RPW + rr;
+    int trow[ROUNDS];
+#pragma unroll
+    for (int h = 0; h < ROUNDS; ++h) trow[h] = wave * RPW + 16 * h + rr;
     float* const tw = s_tr[wave];
 
     // every slot-table entry always holds a valid cache slot, so the prefetch
     // may read entries past the end of a pass's table
     for (int i = tid; i < kMaxPiece; i += NT) s_slot[i] = 0u;
 
-    half8 qa[S::NQ];
-    float fT_r = 0.0f;  // threshold score of this lane's row (Filter)
-    int cnt_r = 0;      // staged entries of this lane's row (Filter)
-    int tile_r0 = -1;   // first row of the tile held in registers
+    half8 qa[F::NQ];
+    float fT_r[ROUNDS];  // threshold scores of this lane's rows (Filter)
+    int cnt_r[ROUNDS];   // staged entries of this lane's rows (Filter)
+#pragma unroll
+    for (int h = 0; h < ROUNDS; ++h) {
+        fT_r[h] = 0.0f;
+        cnt_r[h] = 0;
+    }
+    int tile_r0 = -1;    // first row of the tile held in registers
 
     while (p < pend) {
         const int tile = (int)(p / span);
@@ -173,11 +195,14 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
         const int len = (int)min<int64_t>(min<int64_t>((int64_t)(span - off), pend - p), (int64_t)kMaxPiece);
         const int c0 = xk0 + off, c1 = c0 + len;
         p += len;
-        const int r0 = tile * kTileRows;
+        const int r0 = tile * TILE;
         const bool new_tile = r0 != tile_r0;
-        if (FILTER && new_tile && tile_r0 >= 0) flush_staged(A, s_lbuf + trow * kLCap, tile_r0 + trow, cnt_r);
+        if (FILTER && new_tile && tile_r0 >= 0) {
+#pragma unroll
+            for (int h = 0; h < ROUNDS; ++h) flush_staged(A, s_lbuf + trow[h] * kLCap, tile_r0 + trow[h], cnt_r[h]);
+        }
 
-        for (int t = tid; t < kTileRows; t += NT) {
+        for (int t = tid; t < TILE; t += NT) {
             const int r = r0 + t;
             int req = -1, lv = 0;
             if (r < a.rows) {
@@ -197,19 +222,19 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
             if (FILTER && new_tile) s_fT[t] = req >= 0 ? key_to_float((uint32_t)(A.thresh[r] >> 32)) : 0.0f;
         }
         if (new_tile) {
-            // query fragments of this wave's 16 rows
+            // query fragments of this wave's rows
 #pragma unroll
-            for (int t = 0; t < S::NQ; ++t) {
+            for (int t = 0; t < F::NQ; ++t) {
                 const int m = lane & 31;
                 int row, h, s;
                 if (RELU) {  // MFMA tile t/8: rows 8*(t/8) + m/4, head m%4; slice t%8
-                    row = wave * S::RPW + (t / kSlices) * 8 + (m >> 2);
+                    row = wave * RPW + (t / kSlices) * 8 + (m >> 2);
                     h = m & 3;
                     s = t % kSlices;
-                } else {     // MFMA row m = (row m/2, pair m%2); step t = (slice t/2, head 2*pair + t%2)
-                    row = wave * S::RPW + (m >> 1);
-                    h = 2 * (m & 1) + (t & 1);
-                    s = t >> 1;
+                } else {     // MFMA row m = row m; step t = (slice t/4, head t%4)
+                    row = wave * RPW + m;
+                    h = t & 3;
+                    s = t >> 2;
                 }
                 row += r0;
                 half8 v = {};
@@ -220,7 +245,10 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
             }
         }
         __syncthreads();
-        if (FILTER && new_tile) fT_r = s_fT[trow];
+        if (FILTER && new_tile) {
+#pragma unroll
+            for (int h = 0; h < ROUNDS; ++h) fT_r[h] = s_fT[trow[h]];
+        }
         tile_r0 = r0;
 
         for (;;) {
@@ -228,12 +256,12 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
             // (smallest request id first): wave 0 elects it and marks the rows
             if (wave == 0) {
                 int best = 0x7FFFFFFF;
-                for (int t = lane; t < kTileRows; t += 64)
+                for (int t = lane; t < TILE; t += 64)
                     if (s_todo[t]) best = min(best, s_req[t]);
 #pragma unroll
                 for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o, 64));
                 int vmax = 0;
-                for (int t = lane; t < kTileRows; t += 64) {
+                for (int t = lane; t < TILE; t += 64) {
                     const bool on = s_todo[t] && s_req[t] == best;
                     s_lim[t] = on ? min(s_lv[t], c1) : 0;
                     if (on) {
@@ -261,10 +289,15 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                 const int pg = min(max(ptrow[lp], 0), a.num_pages - 1);
                 s_slot[i] = (uint32_t)pg * (uint32_t)a.kpp + (uint32_t)slot;
             }
-            // this lane's row bound, and the smallest over the wave's rows:
+            // this lane's row bounds, and the smallest over the wave's rows:
             // column tiles entirely below it need no per-row mask
-            const int lim_r = s_lim[trow];
-            int wlim = lim_r;
+            int lim_r[ROUNDS];
+            int wlim = 0x7FFFFFFF;
+#pragma unroll
+            for (int h = 0; h < ROUNDS; ++h) {
+                lim_r[h] = s_lim[trow[h]];
+                wlim = min(wlim, lim_r[h]);
+            }
 #pragma unroll
             for (int o = 4; o < 64; o <<= 1) wlim = min(wlim, __shfl_xor(wlim, o, 64));
             wlim = __builtin_amdgcn_readfirstlane(wlim);
@@ -299,7 +332,7 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                 // keep the prefetch issued here, ahead of the MFMAs that hide it
                 __builtin_amdgcn_sched_barrier(0);
 
-                float sc[kSub][NOUT];
+                float sc[kSub][ROUNDS][8];
                 if (RELU) {
                     float16v acc[kSub][2];
 #pragma unroll
@@ -321,10 +354,10 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
 #pragma unroll
                     for (int st = 0; st < kSub; ++st)
 #pragma unroll
-                        for (int o = 0; o < NOUT; ++o) {
+                        for (int o = 0; o < 8; ++o) {
                             const int mt = o >> 2, g = o & 3;
-                            sc[st][o] = combine_relu_heads(acc[st][mt][4 * g], acc[st][mt][4 * g + 1],
-                                                           acc[st][mt][4 * g + 2], acc[st][mt][4 * g + 3]);
+                            sc[st][0][o] = combine_relu_heads(acc[st][mt][4 * g], acc[st][mt][4 * g + 1],
+                                                              acc[st][mt][4 * g + 2], acc[st][mt][4 * g + 3]);
                         }
                 } else {
                     float16v acc[kSub];
@@ -338,15 +371,17 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                             kbs[st] = *reinterpret_cast<const half8*>(
                                 sk + lds_key_chunk(32 * st + (lane & 31), 2 * s + (lane >> 5)));
 #pragma unroll
-                        for (int t = 2 * s; t < 2 * s + 2; ++t)
+                        for (int h = 0; h < kHeads; ++h)
 #pragma unroll
-                            for (int st = 0; st < kSub; ++st) acc[st] = mfma32(qa[t], kbs[st], acc[st]);
+                            for (int st = 0; st < kSub; ++st) acc[st] = mfma32(qa[kHeads * s + h], kbs[st], acc[st]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int st = 0; st < kSub; ++st)
 #pragma unroll
-                        for (int o = 0; o < NOUT; ++o) sc[st][o] = combine_pairs(acc[st][2 * o], acc[st][2 * o + 1]);
+                        for (int h = 0; h < ROUNDS; ++h)
+#pragma unroll
+                            for (int o = 0; o < 8; ++o) sc[st][h][o] = acc[st][8 * h + o];
                 }
                 // stage the prefetched tile in the idle buffer (after the last
                 // step this fills a buffer no wave reads any more: every wave
@@ -357,44 +392,47 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
 
 #pragma unroll
                 for (int st = 0; st < kSub; ++st) {
-                    // transpose: lane (row rr, keys 8cq..8cq+7) of this column tile
-                    const int wr = out_half_offset<RELU>() * (lane >> 5);
-#pragma unroll
-                    for (int o = 0; o < NOUT; ++o) tw[(wr + out_row_offset<RELU>(o)) * kTrStride + (lane & 31)] = sc[st][o];
-                    __builtin_amdgcn_wave_barrier();
-                    const float4v v0 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq);
-                    const float4v v1 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq + 4);
-                    __builtin_amdgcn_wave_barrier();
-                    const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                     const int key0 = j0 + 32 * st + 8 * cq;
                     const bool full = j0 + 32 * (st + 1) <= wlim;
-                    if (!FILTER) {
-                        float* dst = A.out + (int64_t)(r0 + trow) * A.ld + key0;
-                        if (full && A.vec_store) {
-                            *reinterpret_cast<float4v*>(dst) = v0;
-                            *reinterpret_cast<float4v*>(dst + 4) = v1;
+#pragma unroll
+                    for (int h = 0; h < ROUNDS; ++h) {
+                        // transpose: lane (row rr, keys 8cq..8cq+7) of this round
+                        const int wr = F::HALF * (lane >> 5);
+#pragma unroll
+                        for (int o = 0; o < 8; ++o) tw[(wr + F::out_row(o)) * kTrStride + (lane & 31)] = sc[st][h][o];
+                        __builtin_amdgcn_wave_barrier();
+                        const float4v v0 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq);
+                        const float4v v1 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq + 4);
+                        __builtin_amdgcn_wave_barrier();
+                        const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                        if (!FILTER) {
+                            float* dst = A.out + (int64_t)(r0 + trow[h]) * A.ld + key0;
+                            if (full && A.vec_store) {
+                                *reinterpret_cast<float4v*>(dst) = v0;
+                                *reinterpret_cast<float4v*>(dst + 4) = v1;
+                            } else {
+#pragma unroll
+                                for (int i = 0; i < 8; ++i)
+                                    if (full || key0 + i < lim_r[h]) dst[i] = v[i];
+                            }
                         } else {
+                            bool kp[8];
+                            int n = 0;
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                kp[i] = v[i] >= fT_r[h] && (full || key0 + i < lim_r[h]);
+                                n += kp[i] ? 1 : 0;
+                            }
+                            int tot;
+                            const int excl = quad_exclusive_sum(n, &tot);
+                            uint64_t* lb = s_lbuf + trow[h] * kLCap;
+                            if (__any(cnt_r[h] + tot > kLCap)) flush_staged(A, lb, r0 + trow[h], cnt_r[h]);
+                            int slot = cnt_r[h] + excl;
 #pragma unroll
                             for (int i = 0; i < 8; ++i)
-                                if (full || key0 + i < lim_r) dst[i] = v[i];
+                                if (kp[i]) lb[slot++] = ((uint64_t)__float_as_uint(v[i]) << 32) | (uint32_t)(key0 + i);
+                            cnt_r[h] += tot;
                         }
-                    } else {
-                        bool kp[8];
-                        int n = 0;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            kp[i] = v[i] >= fT_r && (full || key0 + i < lim_r);
-                            n += kp[i] ? 1 : 0;
-                        }
-                        int tot;
-                        const int excl = quad_exclusive_sum(n, &tot);
-                        uint64_t* lb = s_lbuf + trow * kLCap;
-                        if (__any(cnt_r + tot > kLCap)) flush_staged(A, lb, r0 + trow, cnt_r);
-                        int slot = cnt_r + excl;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            if (kp[i]) lb[slot++] = ((uint64_t)__float_as_uint(v[i]) << 32) | (uint32_t)(key0 + i);
-                        cnt_r += tot;
                     }
                 }
                 buf ^= 1;
@@ -404,7 +442,10 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
         }
         __syncthreads();
     }
-    if (FILTER && tile_r0 >= 0) flush_staged(A, s_lbuf + trow * kLCap, tile_r0 + trow, cnt_r);
+    if (FILTER && tile_r0 >= 0) {
+#pragma unroll
+        for (int h = 0; h < ROUNDS; ++h) flush_staged(A, s_lbuf + trow[h] * kLCap, tile_r0 + trow[h], cnt_r[h]);
+    }
 }
 
 }  // namespace qsa

@@ -49,23 +49,32 @@ __device__ __forceinline__ int row_visible_count(const VisibleSource& v, int r) 
 constexpr int kThrNT = 256;
 constexpr int kMaxSamples = 4096;
 
+// Threshold of one row: a composite T with exactly m sample composites >= T
+// (found by a histogram descent; T itself need not be a sample).
 __global__ __launch_bounds__(kThrNT) void sample_threshold_kernel(const float* __restrict__ samp, int64_t ld_s,
                                                                   VisibleSource vis, int32_t stride, int32_t m,
                                                                   int32_t force_fallback,
                                                                   uint64_t* __restrict__ thresh,
                                                                   int32_t* __restrict__ cand_count) {
-    __shared__ uint64_t s_a[kMaxSamples];
-    __shared__ KthScratch ks;
+    constexpr int EPT = kMaxSamples / kThrNT;
+    __shared__ HistScratch hs;
     const int row = blockIdx.x;
     const int V = row_visible_count(vis, row);
     const int ns = (V + stride - 1) / stride;
     uint64_t T = ~0ull;  // decodes to a NaN threshold score: nothing passes
     if (ns >= m && !force_fallback) {
         const float* srow = samp + (int64_t)row * ld_s;
-        for (int i = threadIdx.x; i < ns; i += kThrNT)
-            s_a[i] = compose(order_key(srow[i]), (uint32_t)(i * stride));
-        __syncthreads();
-        T = lds_kth_largest<kThrNT>(s_a, ns, m, &ks);
+        uint64_t v[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int i = e * kThrNT + (int)threadIdx.x;
+            v[e] = i < ns ? compose(order_key(srow[i]), (uint32_t)(i * stride)) : 0ull;
+        }
+        uint64_t mn, mx;
+        block_minmax_nonzero<kThrNT, EPT>(v, &mn, &mx, &hs);
+        const int shift = max(0, bit_length64(mx - mn) - 11);
+        int bin1;
+        T = hist_select_pivot<kThrNT, EPT>(v, mn, shift, m, &hs, nullptr, &bin1);
     }
     if (threadIdx.x == 0) {
         thresh[row] = T;
@@ -162,9 +171,27 @@ __device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* 
     return na;
 }
 
+constexpr int kMaxBucket = 32;
+
+// Writes rank r's block (expanded to `expand` tokens) into the output row.
+__device__ __forceinline__ void write_rank(int32_t* orow, int r, uint64_t c, int expand) {
+    const int base = (int)composite_index(c) * expand;
+    for (int t = 0; t < expand; ++t) orow[r * expand + t] = base + t;
+}
+
+// One row per workgroup.  Candidate path: the row's candidates are loaded
+// into registers as composites; a histogram descent finds the pivot of the
+// top kb; the selected composites are scattered into LDS grouped by their
+// top-level bin (bins are ordered, so a bin's group starts at the number of
+// selected composites in higher bins) and each takes its rank inside the
+// group by counting larger members.  A group larger than kMaxBucket (heavy
+// clustering or ties) switches the row to a bitonic sort of the selected set.
 template <int CAPL>
 __global__ __launch_bounds__(kFinNT) void fused_final_kernel(FinalArgs A) {
+    constexpr int EPT = CAPL / kFinNT;
     __shared__ uint64_t s_a[CAPL];
+    __shared__ uint32_t s_start[kSelBins];
+    __shared__ HistScratch hs;
     __shared__ KthScratch ks;
     __shared__ int s_pend;
     const int row = blockIdx.x;
@@ -172,25 +199,74 @@ __global__ __launch_bounds__(kFinNT) void fused_final_kernel(FinalArgs A) {
     const int kb = A.kb;
     const int nsel = min(kb, V);
     const int n = A.cand_count[row];
-    int have;
-    if (n >= nsel && n <= A.cand_cap) {
-        const uint64_t* c = A.cand + (int64_t)row * A.cand_cap;
-        // (score bits, key) entries -> composites
-        for (int i = threadIdx.x; i < n; i += kFinNT) {
-            const uint64_t e = c[i];
-            s_a[i] = compose(order_key(__uint_as_float((uint32_t)(e >> 32))), (uint32_t)e);
-        }
-        __syncthreads();
-        have = n;
-        if (n > kb) {
-            const uint64_t t = lds_kth_largest<kFinNT>(s_a, n, kb, &ks);
-            have = lds_compact_ge<kFinNT, CAPL / kFinNT>(s_a, n, t, ks.wsum);
-        }
-    } else {
-        have = recompute_row_topk<CAPL>(A, row, V, s_a, &ks, &s_pend);
-    }
-    lds_sort_desc<kFinNT>(s_a, have);
     int32_t* orow = A.out + (int64_t)row * A.out_len;
+    if (n >= nsel && n <= A.cand_cap) {
+        if (nsel > 0) {
+            const uint64_t* c = A.cand + (int64_t)row * A.cand_cap;
+            uint64_t v[EPT];
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                const int i = e * kFinNT + (int)threadIdx.x;
+                uint64_t x = 0ull;
+                if (i < n) {
+                    const uint64_t en = c[i];  // (score bits, key)
+                    x = compose(order_key(__uint_as_float((uint32_t)(en >> 32))), (uint32_t)en);
+                }
+                v[e] = x;
+            }
+            uint64_t mn, mx;
+            block_minmax_nonzero<kFinNT, EPT>(v, &mn, &mx, &hs);
+            const int shift1 = max(0, bit_length64(mx - mn) - 11);
+            uint64_t pivot = mn;
+            if (nsel < n) {
+                int bin1;
+                pivot = hist_select_pivot<kFinNT, EPT>(v, mn, shift1, nsel, &hs, s_start, &bin1);
+            } else {
+                int above, cnt;  // every candidate is selected; only the bin starts are needed
+                (void)hist_level<kFinNT, EPT>(v, mn, shift1, 64, 0ull, n, &hs, s_start, &above, &cnt);
+            }
+            for (int i = threadIdx.x; i < kSelBins; i += kFinNT) hs.hist[i] = 0u;
+            if (threadIdx.x == 0) hs.flag = 0;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                if (v[e] && v[e] >= pivot) {
+                    const uint32_t b1 = (uint32_t)((v[e] - mn) >> shift1);
+                    s_a[s_start[b1] + atomicAdd(&hs.hist[b1], 1u)] = v[e];
+                }
+            }
+            __syncthreads();
+            int rank[EPT];
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                rank[e] = -1;
+                if (v[e] && v[e] >= pivot) {
+                    const uint32_t b1 = (uint32_t)((v[e] - mn) >> shift1);
+                    const int st = (int)s_start[b1], cnt = (int)hs.hist[b1];
+                    if (cnt > kMaxBucket) {
+                        hs.flag = 1;
+                    } else {
+                        int r = 0;
+                        for (int i = st; i < st + cnt; ++i) r += s_a[i] > v[e] ? 1 : 0;
+                        rank[e] = st + r;
+                    }
+                }
+            }
+            __syncthreads();
+            if (hs.flag) {
+                lds_sort_desc<kFinNT>(s_a, nsel);
+                for (int r = threadIdx.x; r < nsel; r += kFinNT) write_rank(orow, r, s_a[r], A.expand);
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPT; ++e)
+                    if (rank[e] >= 0) write_rank(orow, rank[e], v[e], A.expand);
+            }
+        }
+        for (int i = nsel * A.expand + (int)threadIdx.x; i < A.out_len; i += kFinNT) orow[i] = -1;
+        return;
+    }
+    const int have = recompute_row_topk<CAPL>(A, row, V, s_a, &ks, &s_pend);
+    lds_sort_desc<kFinNT>(s_a, have);
     for (int i = threadIdx.x; i < A.out_len; i += kFinNT) {
         const int rank = i / A.expand, t = i - rank * A.expand;
         int v = -1;

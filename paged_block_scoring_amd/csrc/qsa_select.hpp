@@ -127,4 +127,136 @@ __device__ int lds_compact_ge(uint64_t* a, int n, uint64_t t, int* wsum) {
     return total;
 }
 
+// ---------------------------------------------------------------------------
+// Register-resident histogram selection.  Each of the NT threads holds EPT
+// composites in registers (0 marks an empty slot; real composites are never
+// 0).  Values are binned relative to `base` (the smallest value) with 2048
+// bins per level: the top level spans the whole value range, each further
+// level splits one bin of the level above.  Composites are distinct, so the
+// descent ends at the latest when a bin is one value wide.
+
+constexpr int kSelBins = 2048;
+
+struct HistScratch {
+    uint32_t hist[kSelBins];
+    uint64_t wmin[16], wmax[16];
+    int wsum[16];
+    int bin, above, cnt;
+    int flag;
+};
+
+__device__ __forceinline__ int bit_length64(uint64_t x) { return x ? 64 - __clzll((long long)x) : 0; }
+
+// Block-wide smallest and largest nonzero value (both 0 if there is none).
+// Contains barriers.
+template <int NT, int EPT>
+__device__ void block_minmax_nonzero(const uint64_t (&v)[EPT], uint64_t* mn, uint64_t* mx, HistScratch* s) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t a = ~0ull, b = 0ull;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+        if (v[e]) {
+            a = v[e] < a ? v[e] : a;
+            b = v[e] > b ? v[e] : b;
+        }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint64_t x = __shfl_xor(a, o, 64), y = __shfl_xor(b, o, 64);
+        a = x < a ? x : a;
+        b = y > b ? y : b;
+    }
+    if (lane == 0) {
+        s->wmin[wave] = a;
+        s->wmax[wave] = b;
+    }
+    __syncthreads();
+    a = ~0ull;
+    b = 0ull;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        a = s->wmin[w] < a ? s->wmin[w] : a;
+        b = s->wmax[w] > b ? s->wmax[w] : b;
+    }
+    __syncthreads();
+    *mn = b ? a : 0ull;
+    *mx = b;
+}
+
+// One histogram level.  Participants are the nonzero values whose offset
+// d = v - base satisfies d >> pshift == prefix (every value when pshift is
+// 64); their digit is (d >> shift) mod 2^(pshift - shift), pshift - shift <=
+// 11.  Finds the bin holding the need-th largest participant (1 <= need <=
+// participants) and returns it, with *above = participants in higher bins and
+// *cnt = participants in that bin.  If `start` is given, start[bin] receives
+// the number of participants in bins above `bin`, for every bin.  Contains
+// barriers.
+template <int NT, int EPT>
+__device__ int hist_level(const uint64_t (&v)[EPT], uint64_t base, int shift, int pshift, uint64_t prefix, int need,
+                          HistScratch* s, uint32_t* start, int* above, int* cnt) {
+    constexpr int BPT = kSelBins / NT;
+    static_assert(BPT * NT == kSelBins, "bins per thread");
+    const int t = threadIdx.x;
+    for (int i = t; i < kSelBins; i += NT) s->hist[i] = 0u;
+    __syncthreads();
+    const uint64_t dmask = (pshift - shift >= 64) ? ~0ull : ((1ull << (pshift - shift)) - 1ull);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        if (!v[e]) continue;
+        const uint64_t d = v[e] - base;
+        if (pshift < 64 && (d >> pshift) != prefix) continue;
+        atomicAdd(&s->hist[(uint32_t)((d >> shift) & dmask)], 1u);
+    }
+    __syncthreads();
+    // thread t owns bins kSelBins-1-BPT*t .. kSelBins-BPT*(t+1), high to low
+    uint32_t c[BPT];
+    int local = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        c[j] = s->hist[kSelBins - 1 - BPT * t - j];
+        local += (int)c[j];
+    }
+    int total;
+    int run = block_inclusive_scan<NT>(local, s->wsum, &total) - local;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        const int bin = kSelBins - 1 - BPT * t - j;
+        if (start) start[bin] = (uint32_t)run;
+        if (run < need && run + (int)c[j] >= need) {
+            s->bin = bin;
+            s->above = run;
+            s->cnt = (int)c[j];
+        }
+        run += (int)c[j];
+    }
+    __syncthreads();
+    const int b = s->bin;
+    *above = s->above;
+    *cnt = s->cnt;
+    __syncthreads();
+    return b;
+}
+
+// Smallest pivot P such that exactly k of the values are >= P (1 <= k <= n,
+// n = number of nonzero values, values distinct).  base/shift1 describe the
+// top level (base = smallest value, top-level digit = (v - base) >> shift1 <
+// 2048); start1[] receives the top level's per-bin "participants above"
+// counts and *bin1 the top-level bin of the k-th largest.  Contains barriers.
+template <int NT, int EPT>
+__device__ uint64_t hist_select_pivot(const uint64_t (&v)[EPT], uint64_t base, int shift1, int k, HistScratch* s,
+                                      uint32_t* start1, int* bin1) {
+    int above, cnt;
+    uint64_t prefix = (uint64_t)hist_level<NT, EPT>(v, base, shift1, 64, 0ull, k, s, start1, &above, &cnt);
+    *bin1 = (int)prefix;
+    int need = k - above;
+    int cur = shift1;
+    while (cnt != need) {
+        const int ns = cur > 11 ? cur - 11 : 0;
+        const int b = hist_level<NT, EPT>(v, base, ns, cur, prefix, need, s, nullptr, &above, &cnt);
+        prefix = (prefix << (cur - ns)) | (uint64_t)b;
+        cur = ns;
+        need -= above;
+    }
+    return base + (prefix << cur);
+}
+
 }  // namespace qsa

@@ -29,6 +29,7 @@
 //     how fast.
 #include <cmath>
 
+#include "qsa.h"
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
 #include "qsa_select.hpp"
@@ -49,8 +50,9 @@ __device__ __forceinline__ int row_visible_count(const VisibleSource& v, int r) 
 constexpr int kThrNT = 256;
 constexpr int kMaxSamples = 4096;
 
-// Threshold of one row: a composite T with exactly m sample composites >= T
-// (found by a histogram descent; T itself need not be a sample).
+// Threshold of one row: the score whose order key is the m-th largest sample
+// order key (found by a histogram descent), so at least m samples reach it.
+// Stored as a composite whose high word is that key.
 __global__ __launch_bounds__(kThrNT) void sample_threshold_kernel(const float* __restrict__ samp, int64_t ld_s,
                                                                   VisibleSource vis, int32_t stride, int32_t m,
                                                                   int32_t force_fallback,
@@ -64,17 +66,14 @@ __global__ __launch_bounds__(kThrNT) void sample_threshold_kernel(const float* _
     uint64_t T = ~0ull;  // decodes to a NaN threshold score: nothing passes
     if (ns >= m && !force_fallback) {
         const float* srow = samp + (int64_t)row * ld_s;
-        uint64_t v[EPT];
+        uint32_t k[EPT];
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const int i = e * kThrNT + (int)threadIdx.x;
-            v[e] = i < ns ? compose(order_key(srow[i]), (uint32_t)(i * stride)) : 0ull;
+            k[e] = (e * kThrNT < ns && i < ns) ? order_key(srow[i]) : 0u;
         }
-        uint64_t mn, mx;
-        block_minmax_nonzero<kThrNT, EPT>(v, &mn, &mx, &hs);
-        const int shift = max(0, bit_length64(mx - mn) - 11);
-        int bin1;
-        T = hist_select_pivot<kThrNT, EPT>(v, mn, shift, m, &hs, nullptr, &bin1);
+        const Descent d = hist_descent32<kThrNT, EPT>(k, ns, m, &hs, nullptr);
+        T = (uint64_t)d.pivot << 32;
     }
     if (threadIdx.x == 0) {
         thresh[row] = T;
@@ -109,8 +108,7 @@ __device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* 
     const PagedArgs& p = A.a;
     const int kb = A.kb;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int ch = (CAPL - kb) / (32 * kFinWaves) * (32 * kFinWaves);
-    if (ch > 2048) ch = 2048;
+    const int ch = (CAPL - kb) / (32 * kFinWaves) * (32 * kFinWaves);
     const int req = p.row_req ? p.row_req[row] : 0;
     const int32_t* ptrow = p.page_table + (int64_t)req * p.pt_stride;
     const _Float16* qrow = p.q + (int64_t)row * kHeads * kHeadDim;
@@ -172,100 +170,114 @@ __device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* 
 }
 
 constexpr int kMaxBucket = 32;
+constexpr int kRecChunk = 512;  // keys scored per round by the recompute path
 
 // Writes rank r's block (expanded to `expand` tokens) into the output row.
-__device__ __forceinline__ void write_rank(int32_t* orow, int r, uint64_t c, int expand) {
-    const int base = (int)composite_index(c) * expand;
+__device__ __forceinline__ void write_rank(int32_t* orow, int r, uint32_t idx, int expand) {
+    const int base = (int)idx * expand;
     for (int t = 0; t < expand; ++t) orow[r * expand + t] = base + t;
 }
 
 // One row per workgroup.  Candidate path: the row's candidates are loaded
-// into registers as composites; a histogram descent finds the pivot of the
-// top kb; the selected composites are scattered into LDS grouped by their
-// top-level bin (bins are ordered, so a bin's group starts at the number of
-// selected composites in higher bins) and each takes its rank inside the
-// group by counting larger members.  A group larger than kMaxBucket (heavy
-// clustering or ties) switches the row to a bitonic sort of the selected set.
-template <int CAPL>
+// into registers as (order key, index); a histogram descent over the order
+// keys finds the cut of the top kb (ties at the cut are broken by a second
+// descent over inverted indices); the selected entries are scattered into LDS
+// grouped by their top-level bin (bins are ordered, so a group starts at the
+// number of selected entries in higher bins) and each takes its rank inside
+// the group by counting larger members.  A group larger than kMaxBucket
+// (heavy clustering or ties) switches the row to a bitonic sort of the
+// selected set.  Rows whose candidate list is unusable take the recompute
+// path.
+template <int KBMAX, int CAPC>
 __global__ __launch_bounds__(kFinNT) void fused_final_kernel(FinalArgs A) {
-    constexpr int EPT = CAPL / kFinNT;
-    __shared__ uint64_t s_a[CAPL];
+    constexpr int EPT = CAPC / kFinNT;
+    __shared__ uint64_t s_a[KBMAX];
     __shared__ uint32_t s_start[kSelBins];
     __shared__ HistScratch hs;
-    __shared__ KthScratch ks;
-    __shared__ int s_pend;
     const int row = blockIdx.x;
     const int V = row_visible_count(A.vis, row);
     const int kb = A.kb;
     const int nsel = min(kb, V);
     const int n = A.cand_count[row];
     int32_t* orow = A.out + (int64_t)row * A.out_len;
-    if (n >= nsel && n <= A.cand_cap) {
+    if (n < nsel || n > A.cand_cap) return;  // fused_recompute_kernel's row
+    {
         if (nsel > 0) {
             const uint64_t* c = A.cand + (int64_t)row * A.cand_cap;
-            uint64_t v[EPT];
+            uint32_t k[EPT], idx[EPT];
 #pragma unroll
             for (int e = 0; e < EPT; ++e) {
                 const int i = e * kFinNT + (int)threadIdx.x;
-                uint64_t x = 0ull;
-                if (i < n) {
+                k[e] = 0u;
+                idx[e] = 0u;
+                if (e * kFinNT < n && i < n) {
                     const uint64_t en = c[i];  // (score bits, key)
-                    x = compose(order_key(__uint_as_float((uint32_t)(en >> 32))), (uint32_t)en);
+                    k[e] = order_key(__uint_as_float((uint32_t)(en >> 32)));
+                    idx[e] = (uint32_t)en;
                 }
-                v[e] = x;
             }
-            uint64_t mn, mx;
-            block_minmax_nonzero<kFinNT, EPT>(v, &mn, &mx, &hs);
-            const int shift1 = max(0, bit_length64(mx - mn) - 11);
-            uint64_t pivot = mn;
-            if (nsel < n) {
-                int bin1;
-                pivot = hist_select_pivot<kFinNT, EPT>(v, mn, shift1, nsel, &hs, s_start, &bin1);
-            } else {
-                int above, cnt;  // every candidate is selected; only the bin starts are needed
-                (void)hist_level<kFinNT, EPT>(v, mn, shift1, 64, 0ull, n, &hs, s_start, &above, &cnt);
+            // selection: sel(e) = k > pivot, or k == pivot and (exact or ~idx >= jpiv)
+            const Descent d = hist_descent32<kFinNT, EPT>(k, n, nsel, &hs, s_start);
+            uint32_t jpiv = 0u;
+            if (!d.exact) {
+                uint32_t t[EPT];
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) t[e] = (e * kFinNT < n && k[e] && k[e] == d.pivot) ? ~idx[e] : 0u;
+                jpiv = hist_descent32<kFinNT, EPT>(t, n, nsel - d.above, &hs, nullptr).pivot;
             }
             for (int i = threadIdx.x; i < kSelBins; i += kFinNT) hs.hist[i] = 0u;
             if (threadIdx.x == 0) hs.flag = 0;
             __syncthreads();
 #pragma unroll
             for (int e = 0; e < EPT; ++e) {
-                if (v[e] && v[e] >= pivot) {
-                    const uint32_t b1 = (uint32_t)((v[e] - mn) >> shift1);
-                    s_a[s_start[b1] + atomicAdd(&hs.hist[b1], 1u)] = v[e];
+                const bool sel = e * kFinNT < n && k[e] &&
+                                 (k[e] > d.pivot || (k[e] == d.pivot && (d.exact || ~idx[e] >= jpiv)));
+                if (sel) {
+                    const uint32_t b1 = (k[e] - d.base) >> d.shift1;
+                    s_a[s_start[b1] + atomicAdd(&hs.hist[b1], 1u)] = compose(k[e], idx[e]);
                 }
             }
             __syncthreads();
-            int rank[EPT];
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                rank[e] = -1;
-                if (v[e] && v[e] >= pivot) {
-                    const uint32_t b1 = (uint32_t)((v[e] - mn) >> shift1);
-                    const int st = (int)s_start[b1], cnt = (int)hs.hist[b1];
-                    if (cnt > kMaxBucket) {
-                        hs.flag = 1;
-                    } else {
-                        int r = 0;
-                        for (int i = st; i < st + cnt; ++i) r += s_a[i] > v[e] ? 1 : 0;
-                        rank[e] = st + r;
-                    }
+            // rank inside the bin group; a crowded group defers the row to the
+            // sort below (ranks written here are exact either way)
+            for (int p = threadIdx.x; p < nsel; p += kFinNT) {
+                const uint64_t me = s_a[p];
+                const uint32_t b1 = ((uint32_t)(me >> 32) - d.base) >> d.shift1;
+                const int st = (int)s_start[b1], cnt = (int)hs.hist[b1];
+                if (cnt > kMaxBucket) {
+                    hs.flag = 1;
+                } else {
+                    int r = 0;
+                    for (int i = st; i < st + cnt; ++i) r += s_a[i] > me ? 1 : 0;
+                    write_rank(orow, st + r, composite_index(me), A.expand);
                 }
             }
             __syncthreads();
             if (hs.flag) {
                 lds_sort_desc<kFinNT>(s_a, nsel);
-                for (int r = threadIdx.x; r < nsel; r += kFinNT) write_rank(orow, r, s_a[r], A.expand);
-            } else {
-#pragma unroll
-                for (int e = 0; e < EPT; ++e)
-                    if (rank[e] >= 0) write_rank(orow, rank[e], v[e], A.expand);
+                for (int r = threadIdx.x; r < nsel; r += kFinNT) write_rank(orow, r, composite_index(s_a[r]), A.expand);
             }
         }
         for (int i = nsel * A.expand + (int)threadIdx.x; i < A.out_len; i += kFinNT) orow[i] = -1;
-        return;
     }
-    const int have = recompute_row_topk<CAPL>(A, row, V, s_a, &ks, &s_pend);
+}
+
+// The rows whose candidate list is unusable (too short: the threshold was
+// too high; too long: it was too low or its score has many ties; or the
+// sampling pass left the row out): exact top-kb by recomputation.
+template <int KBMAX>
+__global__ __launch_bounds__(kFinNT) void fused_recompute_kernel(FinalArgs A) {
+    constexpr int LA = KBMAX + kRecChunk;
+    __shared__ uint64_t s_a[LA];
+    __shared__ KthScratch ks;
+    __shared__ int s_pend;
+    const int row = blockIdx.x;
+    const int V = row_visible_count(A.vis, row);
+    const int nsel = min(A.kb, V);
+    const int n = A.cand_count[row];
+    if (n >= nsel && n <= A.cand_cap) return;  // fused_final_kernel's row
+    int32_t* orow = A.out + (int64_t)row * A.out_len;
+    const int have = recompute_row_topk<LA>(A, row, V, s_a, &ks, &s_pend);
     lds_sort_desc<kFinNT>(s_a, have);
     for (int i = threadIdx.x; i < A.out_len; i += kFinNT) {
         const int rank = i / A.expand, t = i - rank * A.expand;
@@ -314,10 +326,14 @@ hipError_t launch_fused_final(const PagedArgs& a, const VisibleSource& vis, cons
     A.expand = expand;
     A.out_len = out_len;
     A.out = out;
-    if (f.capl == 4096)
-        fused_final_kernel<4096><<<dim3((unsigned)a.rows), kFinNT, 0, stream>>>(A);
-    else
-        fused_final_kernel<8192><<<dim3((unsigned)a.rows), kFinNT, 0, stream>>>(A);
+    const dim3 grid((unsigned)a.rows);
+    if (f.capl == 4096) {
+        fused_final_kernel<1024, 4096><<<grid, kFinNT, 0, stream>>>(A);
+        fused_recompute_kernel<1024><<<grid, kFinNT, 0, stream>>>(A);
+    } else {
+        fused_final_kernel<QSA_MAX_SELECT, 8192><<<grid, kFinNT, 0, stream>>>(A);
+        fused_recompute_kernel<QSA_MAX_SELECT><<<grid, kFinNT, 0, stream>>>(A);
+    }
     return hipGetLastError();
 }
 

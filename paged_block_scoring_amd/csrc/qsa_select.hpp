@@ -128,83 +128,84 @@ __device__ int lds_compact_ge(uint64_t* a, int n, uint64_t t, int* wsum) {
 }
 
 // ---------------------------------------------------------------------------
-// Register-resident histogram selection.  Each of the NT threads holds EPT
-// composites in registers (0 marks an empty slot; real composites are never
-// 0).  Values are binned relative to `base` (the smallest value) with 2048
-// bins per level: the top level spans the whole value range, each further
-// level splits one bin of the level above.  Composites are distinct, so the
-// descent ends at the latest when a bin is one value wide.
+// Register-resident histogram selection on 32-bit keys.  Each of the NT
+// threads holds EPT keys in registers, key e being element e*NT + threadIdx.x;
+// 0 marks an empty slot (order keys of finite scores are never 0, nor are
+// inverted indices).  Keys are binned relative to `base` (the smallest key)
+// with kSelBins bins per level: the top level spans the whole key range, each
+// further level splits one bin of the level above, until the bin holding the
+// wanted rank is exactly filled or one key wide.
 
-constexpr int kSelBins = 2048;
+constexpr int kSelBits = 10;
+constexpr int kSelBins = 1 << kSelBits;
 
 struct HistScratch {
     uint32_t hist[kSelBins];
-    uint64_t wmin[16], wmax[16];
+    uint32_t wmin[16], wmax[16];
     int wsum[16];
     int bin, above, cnt;
     int flag;
 };
 
-__device__ __forceinline__ int bit_length64(uint64_t x) { return x ? 64 - __clzll((long long)x) : 0; }
+__device__ __forceinline__ int bit_length32(uint32_t x) { return x ? 32 - __clz((int)x) : 0; }
 
-// Block-wide smallest and largest nonzero value (both 0 if there is none).
-// Contains barriers.
+// Block-wide smallest and largest nonzero key (both 0 if there is none).
+// Slots e with e*NT >= nmax are skipped.  Contains barriers.
 template <int NT, int EPT>
-__device__ void block_minmax_nonzero(const uint64_t (&v)[EPT], uint64_t* mn, uint64_t* mx, HistScratch* s) {
+__device__ void block_minmax_u32(const uint32_t (&k)[EPT], int nmax, uint32_t* mn, uint32_t* mx, HistScratch* s) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint64_t a = ~0ull, b = 0ull;
+    uint32_t a = 0xFFFFFFFFu, b = 0u;
 #pragma unroll
     for (int e = 0; e < EPT; ++e)
-        if (v[e]) {
-            a = v[e] < a ? v[e] : a;
-            b = v[e] > b ? v[e] : b;
+        if (e * NT < nmax && k[e]) {
+            a = min(a, k[e]);
+            b = max(b, k[e]);
         }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
-        const uint64_t x = __shfl_xor(a, o, 64), y = __shfl_xor(b, o, 64);
-        a = x < a ? x : a;
-        b = y > b ? y : b;
+        a = min(a, (uint32_t)__shfl_xor((int)a, o, 64));
+        b = max(b, (uint32_t)__shfl_xor((int)b, o, 64));
     }
     if (lane == 0) {
         s->wmin[wave] = a;
         s->wmax[wave] = b;
     }
     __syncthreads();
-    a = ~0ull;
-    b = 0ull;
+    a = 0xFFFFFFFFu;
+    b = 0u;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) {
-        a = s->wmin[w] < a ? s->wmin[w] : a;
-        b = s->wmax[w] > b ? s->wmax[w] : b;
+        a = min(a, s->wmin[w]);
+        b = max(b, s->wmax[w]);
     }
     __syncthreads();
-    *mn = b ? a : 0ull;
+    *mn = b ? a : 0u;
     *mx = b;
 }
 
-// One histogram level.  Participants are the nonzero values whose offset
-// d = v - base satisfies d >> pshift == prefix (every value when pshift is
-// 64); their digit is (d >> shift) mod 2^(pshift - shift), pshift - shift <=
-// 11.  Finds the bin holding the need-th largest participant (1 <= need <=
-// participants) and returns it, with *above = participants in higher bins and
-// *cnt = participants in that bin.  If `start` is given, start[bin] receives
-// the number of participants in bins above `bin`, for every bin.  Contains
+// One histogram level.  Participants are the nonzero keys whose offset d =
+// k - base satisfies d >> pshift == prefix (every key when pshift is 32);
+// their digit is (d >> shift) mod 2^(pshift - shift) (< kSelBins).  Finds the
+// bin holding the need-th largest participant (1 <= need <= participants) and
+// returns it, with *above = participants in higher bins and *cnt =
+// participants in that bin.  If `start` is given, start[bin] receives the
+// number of participants in bins above `bin`, for every bin.  Contains
 // barriers.
 template <int NT, int EPT>
-__device__ int hist_level(const uint64_t (&v)[EPT], uint64_t base, int shift, int pshift, uint64_t prefix, int need,
-                          HistScratch* s, uint32_t* start, int* above, int* cnt) {
+__device__ uint32_t hist_level32(const uint32_t (&k)[EPT], int nmax, uint32_t base, int shift, int pshift,
+                                 uint32_t prefix, int need, HistScratch* s, uint32_t* start, int* above, int* cnt) {
     constexpr int BPT = kSelBins / NT;
     static_assert(BPT * NT == kSelBins, "bins per thread");
     const int t = threadIdx.x;
     for (int i = t; i < kSelBins; i += NT) s->hist[i] = 0u;
     __syncthreads();
-    const uint64_t dmask = (pshift - shift >= 64) ? ~0ull : ((1ull << (pshift - shift)) - 1ull);
+    const uint32_t dmask = pshift - shift >= 32 ? 0xFFFFFFFFu : ((1u << (pshift - shift)) - 1u);
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-        if (!v[e]) continue;
-        const uint64_t d = v[e] - base;
-        if (pshift < 64 && (d >> pshift) != prefix) continue;
-        atomicAdd(&s->hist[(uint32_t)((d >> shift) & dmask)], 1u);
+        if (e * NT >= nmax || !k[e]) continue;
+        const uint32_t d = k[e] - base;
+        if (pshift < 32 && (d >> pshift) != prefix) continue;
+        atomicAdd(&s->hist[(d >> shift) & dmask], 1u);
     }
     __syncthreads();
     // thread t owns bins kSelBins-1-BPT*t .. kSelBins-BPT*(t+1), high to low
@@ -229,34 +230,52 @@ __device__ int hist_level(const uint64_t (&v)[EPT], uint64_t base, int shift, in
         run += (int)c[j];
     }
     __syncthreads();
-    const int b = s->bin;
+    const uint32_t b = (uint32_t)s->bin;
     *above = s->above;
     *cnt = s->cnt;
     __syncthreads();
     return b;
 }
 
-// Smallest pivot P such that exactly k of the values are >= P (1 <= k <= n,
-// n = number of nonzero values, values distinct).  base/shift1 describe the
-// top level (base = smallest value, top-level digit = (v - base) >> shift1 <
-// 2048); start1[] receives the top level's per-bin "participants above"
-// counts and *bin1 the top-level bin of the k-th largest.  Contains barriers.
+// Result of a histogram descent for the need-th largest key.
+struct Descent {
+    uint32_t pivot;  // keys >= pivot: `need` of them if exact, else more (ties at pivot)
+    bool exact;
+    int above;       // keys > pivot when !exact (all of them selected)
+    uint32_t base;   // smallest key and top-level shift: top-level bin = (k - base) >> shift1
+    int shift1;
+};
+
+// Descends to the need-th largest of the nonzero keys (1 <= need <= their
+// number).  Either some bin is exactly filled -- then exactly `need` keys are
+// >= pivot -- or the descent reaches a single key value with more copies than
+// needed: pivot is that value, `above` keys are larger.  start1 (optional)
+// receives the top level's "keys in higher bins" counts.  Contains barriers.
 template <int NT, int EPT>
-__device__ uint64_t hist_select_pivot(const uint64_t (&v)[EPT], uint64_t base, int shift1, int k, HistScratch* s,
-                                      uint32_t* start1, int* bin1) {
+__device__ Descent hist_descent32(const uint32_t (&k)[EPT], int nmax, int need, HistScratch* s, uint32_t* start1) {
+    Descent r;
+    uint32_t mn, mx;
+    block_minmax_u32<NT, EPT>(k, nmax, &mn, &mx, s);
+    const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
+    r.base = mn;
+    r.shift1 = shift1;
     int above, cnt;
-    uint64_t prefix = (uint64_t)hist_level<NT, EPT>(v, base, shift1, 64, 0ull, k, s, start1, &above, &cnt);
-    *bin1 = (int)prefix;
-    int need = k - above;
+    uint32_t prefix = hist_level32<NT, EPT>(k, nmax, mn, shift1, 32, 0u, need, s, start1, &above, &cnt);
+    int total_above = above;
+    int nd = need - above;
     int cur = shift1;
-    while (cnt != need) {
-        const int ns = cur > 11 ? cur - 11 : 0;
-        const int b = hist_level<NT, EPT>(v, base, ns, cur, prefix, need, s, nullptr, &above, &cnt);
-        prefix = (prefix << (cur - ns)) | (uint64_t)b;
+    while (cnt != nd && cur > 0) {
+        const int ns = cur > kSelBits ? cur - kSelBits : 0;
+        const uint32_t b = hist_level32<NT, EPT>(k, nmax, mn, ns, cur, prefix, nd, s, nullptr, &above, &cnt);
+        prefix = (prefix << (cur - ns)) | b;
         cur = ns;
-        need -= above;
+        nd -= above;
+        total_above += above;
     }
-    return base + (prefix << cur);
+    r.pivot = mn + (prefix << cur);
+    r.exact = cnt == nd;
+    r.above = total_above;
+    return r;
 }
 
 }  // namespace qsa

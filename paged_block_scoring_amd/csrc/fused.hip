@@ -98,13 +98,14 @@ constexpr int kFinWaves = kFinNT / 64;
 
 // Exact top-kb of one row by recomputation: each wave scores 32 keys at a
 // time straight from the cache with the same MFMA sequences as the tiled
-// scorer, with the row in MFMA row slot 0 and zero query fragments elsewhere
-// (default form: MFMA row 0 is the row, heads in K; relu form: rows 0..3 are
-// the four heads).  Composites above the running cutoff are appended in
+// scorer, with zero query fragments outside the row (default form: keys as
+// MFMA rows, the row as column 0, heads in K; relu form: the row's four heads
+// as MFMA rows 0..3, keys as columns).  Composites above the running cutoff are appended in
 // LDS, and the buffer is cut back to its kb largest whenever it exceeds kb.
 // Leaves the selected composites (unsorted) in a[0 .. return value).
 template <int CAPL>
-__device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* a, KthScratch* ks, int* s_pend) {
+__device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* a, KthScratch* ks, int* s_pend,
+                                  float* s_rs) {
     const PagedArgs& p = A.a;
     const int kb = A.kb;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -140,16 +141,26 @@ __device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* 
                 }
                 sc = combine_relu_heads(acc[0], acc[1], acc[2], acc[3]);
             } else {
+                // keys as MFMA rows, the row as column 0
 #pragma unroll
                 for (int t = 0; t < kHeads * kSlices; ++t) {
                     half8 qv = {};
                     const int s = t >> 2, h = t & 3;
                     if (m == 0) qv = *reinterpret_cast<const half8*>(qrow + h * kHeadDim + 16 * s + 8 * g);
-                    acc = mfma32(qv, kb8[s], acc);
+                    acc = mfma32(kb8[s], qv, acc);
                 }
-                sc = acc[0];
+                // lanes 0 and 32 hold the 32 scores (element v: key 8*(v/4) + 4*g + v%4);
+                // hand key m's score to lane m through LDS
+                float* rs = s_rs + 32 * wave;
+                if (m == 0) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) rs[8 * (v >> 2) + 4 * g + (v & 3)] = acc[v];
+                }
+                __builtin_amdgcn_wave_barrier();
+                sc = rs[m];
+                __builtin_amdgcn_wave_barrier();
             }
-            // lanes 0..31 hold MFMA row 0 (the row's score) for key j0 + lane
+            // lanes 0..31 now hold the row's score of key j0 + lane
             if (g == 0 && j < cend) {
                 const uint64_t comp = compose(order_key(sc), (uint32_t)j);
                 if (comp > cut) a[na + atomicAdd(s_pend, 1)] = comp;
@@ -271,13 +282,14 @@ __global__ __launch_bounds__(kFinNT) void fused_recompute_kernel(FinalArgs A) {
     __shared__ uint64_t s_a[LA];
     __shared__ KthScratch ks;
     __shared__ int s_pend;
+    __shared__ float s_rs[32 * kFinWaves];
     const int row = blockIdx.x;
     const int V = row_visible_count(A.vis, row);
     const int nsel = min(A.kb, V);
     const int n = A.cand_count[row];
     if (n >= nsel && n <= A.cand_cap) return;  // fused_final_kernel's row
     int32_t* orow = A.out + (int64_t)row * A.out_len;
-    const int have = recompute_row_topk<LA>(A, row, V, s_a, &ks, &s_pend);
+    const int have = recompute_row_topk<LA>(A, row, V, s_a, &ks, &s_pend, s_rs);
     lds_sort_desc<kFinNT>(s_a, have);
     for (int i = threadIdx.x; i < A.out_len; i += kFinNT) {
         const int rank = i / A.expand, t = i - rank * A.expand;

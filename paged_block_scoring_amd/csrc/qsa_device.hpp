@@ -8,11 +8,12 @@
 // both operands, and the 32x32 output puts rows 8*(v/4) + 4*(l/32) + (v%4) of
 // column l%32 in accumulator element v of lane l.  Accumulation is fp32 from
 // +0 in the order given.
-//   default form (heads in K): MFMA row = query row (32 per tile); a chain
-//     of 32 MFMAs, step t = (slice t/4, head t%4), accumulates the whole
-//     score q_0.k + q_1.k + q_2.k + q_3.k in one sum: the A operand of step t
-//     is head t%4 of the query, the B operand slice t/4 of the key.  Element v
-//     of a lane is the score of row 8*(v/4) + 4*(lane/32) + v%4.
+//   default form (heads in K): the keys are the MFMA rows and the query rows
+//     its columns; a chain of 32 MFMAs, step t = (slice t/4, head t%4), with
+//     A = slice t/4 of the key and B = head t%4 of the query accumulates the
+//     whole score q_0.k + q_1.k + q_2.k + q_3.k in one sum.  Element v of
+//     lane l is the score of query column l%32 and key row
+//     8*(v/4) + 4*(l/32) + v%4.
 //   relu form (per head): MFMA row m = 4*row + head (8 query rows x 4 heads);
 //     a chain of 8 MFMAs over the slices gives every head's dot, elements
 //     4o'..4o'+3 are the four heads of one (row, key), and the score is

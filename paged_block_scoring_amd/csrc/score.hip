@@ -28,8 +28,8 @@ hipError_t launch_form(ScoreKernelArgs A, int32_t cus, int32_t wg_per_cu, int64_
 
 template <Epi EPI>
 hipError_t launch_epi(const ScoreKernelArgs& A, int32_t cus, hipStream_t stream) {
-    if (A.a.relu) return launch_form<true, EPI>(A, cus, 2, 256, stream);
-    return launch_form<false, EPI>(A, cus, 2, 256, stream);
+    if (A.a.relu) return launch_form<true, EPI>(A, cus, 2, kStepKeys, stream);
+    return launch_form<false, EPI>(A, cus, 2, kStepKeys, stream);
 }
 
 }  // namespace

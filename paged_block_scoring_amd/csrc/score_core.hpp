@@ -27,18 +27,23 @@
 // MFMA chains are interleaved).  The MFMA arrangements are the canonical ones
 // of qsa_device.hpp.
 //
-// Epilogue.  A 32-key column tile leaves each wave 32 (or 16) rows x 32
-// scores spread over the MFMA output layout.  The wave transposes them, 16
-// rows at a time, through a small LDS buffer of its own so that each lane
-// holds 8 consecutive keys of one row (lanes 4r..4r+3 share row r):
-//   Store  -- out[row*ld + i] = score with two 16-byte stores per lane
-//             (two-pass arm, sampling pass);
+// Epilogue.  Each lane ends a 32-key column tile holding scores of a single
+// row:
+//   default form -- the MFMA produces the key x row tile, so lane l holds
+//     row l%32 of the wave and 16 consecutive keys;
+//   relu form -- the head-combined scores are spread over rows, so the wave
+//     transposes them through a small LDS buffer of its own until lane l
+//     holds row l/4 and 8 consecutive keys.
+// Then
+//   Store  -- out[row*ld + i] = score with 16-byte stores (two-pass arm,
+//             sampling pass); the default form first transposes through LDS
+//             so that each store instruction writes whole 128-byte row runs;
 //   Filter -- keep (score, key) if score >= the row's threshold score: one
-//             compare per score against a per-lane threshold; a quad prefix
-//             sum gives each kept entry its slot in the row's LDS staging list
-//             (score bits, key), which the wave moves to the row's global
-//             list -- one atomic per row -- when it would overflow and when
-//             the workgroup leaves the tile.  No other synchronisation.
+//             compare per score against a per-lane threshold; a prefix sum
+//             over the row's lanes gives each kept entry its slot in the
+//             row's LDS staging list (score bits, key), which the wave moves
+//             to the row's global list -- one atomic per row -- when it would
+//             overflow and when the workgroup leaves the tile.
 // Rows of different requests in one tile are processed in successive passes.
 #pragma once
 
@@ -53,9 +58,8 @@ constexpr int kSub = 2;                // 32-key column tiles per LDS stage
 constexpr int kStepKeys = 32 * kSub;   // keys per LDS stage
 constexpr int kMaxPiece = 1024;        // logical keys per piece (slot-table size)
 constexpr int kLCap = 32;              // per-row LDS staging slots of the Filter epilogue (>= 32)
-constexpr int kMaxTileRows = 128;      // rows per tile, largest form
 constexpr int kXcds = 8;               // XCDs of an MI355X (256 CUs = 8 x 32)
-constexpr int kTrStride = 36;          // floats per row of the transpose buffer (32 + 4: conflict-free reads)
+constexpr int kTrStride = 36;          // floats per row of the relu transpose buffer (32 + 4: conflict-free reads)
 
 struct ScoreKernelArgs {
     PagedArgs a;
@@ -82,33 +86,37 @@ struct ScoreShape {
 };
 static_assert(ScoreShape::NLOAD == 4, "each thread stages 4 consecutive keys per stage");
 
-// The two MFMA arrangements (qsa_device.hpp), as seen by the tiled kernel.
-// A lane's MFMA outputs for a 32-key column tile come in rounds of 8 scores
-// that cover 16 rows of the wave; out_row(o) is the row (within the round) of
-// output o in lane half 0, and lane half 1 adds HALF.
+// The two MFMA arrangements (qsa_device.hpp) as seen by the tiled kernel.
 template <bool RELU>
 struct Form;
-// default form: heads in K; MFMA row = query row (32 per wave); output
-// element v of the 16 is row 8*(v/4) + 4*(lane/32) + v%4, i.e. round v/8
+// default form: heads in K, keys as the MFMA rows and the wave's 32 query
+// rows as its columns.  Lane l's accumulator element v is MFMA row
+// 8*(v/4) + 4*(l/32) + v%4; the stage keeps key sigma(m) = 16*((m/4)%2) +
+// 4*(m/8) + m%4 of each 32-key column tile in LDS row m, so that element v is
+// key 16*(l/32) + v: every lane holds 16 consecutive keys of row l%32.
 template <>
 struct Form<false> {
     static constexpr int RPW = 32;                 // rows per wave
     static constexpr int TILE = 4 * RPW;           // rows per tile
     static constexpr int NQ = kHeads * kSlices;    // query fragments per lane: (slice, head)
-    static constexpr int ROUNDS = 2;
-    static constexpr int HALF = 4;
-    __device__ static constexpr int out_row(int o) { return 8 * (o >> 2) + (o & 3); }
+    __device__ static int lane_row(int lane) { return lane & 31; }
+    // LDS row of key n of a stage (the inverse of sigma within each column tile)
+    __device__ static int stage_row(int n) {
+        const int k = n & 31;
+        return (n & ~31) | (8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3));
+    }
 };
-// relu form: heads in M; two MFMA tiles of 8 rows x 4 heads per wave; the
-// head-combined outputs o = 4*mt + g are rows 8*mt + 2*g (+1 for lane half 1)
+// relu form: heads in M, two MFMA tiles of 8 rows x 4 heads per wave; the
+// head-combined outputs o = 4*mt + g are rows 8*mt + 2*g (+1 for lane half
+// 1), transposed to lane l = row l/4, keys 8*(l%4) .. 8*(l%4)+7
 template <>
 struct Form<true> {
     static constexpr int RPW = 16;
     static constexpr int TILE = 4 * RPW;
     static constexpr int NQ = 2 * kSlices;
-    static constexpr int ROUNDS = 1;
-    static constexpr int HALF = 1;
     __device__ static constexpr int out_row(int o) { return 8 * (o >> 2) + 2 * (o & 3); }
+    __device__ static int lane_row(int lane) { return lane >> 2; }
+    __device__ static int stage_row(int n) { return n; }
 };
 
 // Quad (lanes 4k..4k+3) exclusive prefix sum of x; *total gets the quad sum.
@@ -125,29 +133,37 @@ __device__ __forceinline__ int quad_exclusive_sum(int x, int* total) {
     return incl - x;
 }
 
-// Moves this wave's staged entries of tile rows (one row per quad, `row` =
-// its global row) to the rows' global candidate lists: the quad's first lane
-// reserves space with one atomic, the quad copies.  Wave-local.
-__device__ __forceinline__ void flush_staged(const ScoreKernelArgs& A, const uint64_t* lb, int row, int& cnt) {
+// Moves the staged entries of one row per lane group (the `gsize` lanes that
+// share `row`; `leader` is the group's member 0) to the rows' global
+// candidate lists: the leader reserves space with one atomic, the group
+// copies.  Wave-local.
+__device__ __forceinline__ void flush_staged(const ScoreKernelArgs& A, const uint64_t* lb, int row, int& cnt,
+                                             int leader, int member, int gsize) {
     int base = 0;
-    if ((threadIdx.x & 3) == 0 && cnt > 0) base = atomicAdd(&A.cand_count[row], cnt);
-    base = __builtin_amdgcn_mov_dpp(base, 0x00, 0xF, 0xF, false);  // quad_perm(0,0,0,0)
+    if (member == 0 && cnt > 0) base = atomicAdd(&A.cand_count[row], cnt);
+    base = __shfl(base, leader, 64);
     uint64_t* dst = A.cand + (int64_t)row * A.cand_cap;
-    for (int i = threadIdx.x & 3; i < cnt; i += 4)
+    for (int i = member; i < cnt; i += gsize)
         if (base + i < A.cand_cap) dst[base + i] = lb[i];
     cnt = 0;
+}
+
+__device__ __forceinline__ uint64_t cand_entry(float score, int key) {
+    return ((uint64_t)__float_as_uint(score) << 32) | (uint32_t)key;
 }
 
 template <bool RELU, Epi EPI>
 __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKernelArgs A) {
     using S = ScoreShape;
     using F = Form<RELU>;
-    constexpr int NT = S::NT, TILE = F::TILE, RPW = F::RPW, ROUNDS = F::ROUNDS;
+    constexpr int NT = S::NT, TILE = F::TILE, RPW = F::RPW;
     constexpr bool FILTER = EPI == Epi::Filter;
 
     __shared__ __attribute__((aligned(16))) unsigned char s_keys[2][kStepKeys * kKeyBytes];
     __shared__ __attribute__((aligned(16))) uint32_t s_slot[kMaxPiece];
-    __shared__ __attribute__((aligned(16))) float s_tr[S::WAVES][16 * kTrStride];
+    // per-wave transpose buffer: relu form (16 rows), default-form Store (32 rows)
+    constexpr int TR_ROWS = RELU ? 16 : (FILTER ? 0 : 32);
+    __shared__ __attribute__((aligned(16))) float s_tr[TR_ROWS ? S::WAVES : 1][TR_ROWS ? TR_ROWS * kTrStride : 4];
     __shared__ int32_t s_req[TILE], s_lv[TILE], s_todo[TILE], s_lim[TILE];
     __shared__ float s_fT[FILTER ? TILE : 1];
     __shared__ uint64_t s_lbuf[FILTER ? TILE * kLCap : 1];
@@ -167,27 +183,20 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
 
     // staging: this thread's 4 consecutive keys of a stage and its chunk
     const int pk = 4 * (tid >> 4), pc = tid & 15;
-    // transposed epilogue: this lane's rows of the wave (rr + 16*round) and
-    // its 8 keys of a column tile
-    const int rr = lane >> 2, cq = lane & 3;
-    int trow[ROUNDS];
-#pragma unroll
-    for (int h = 0; h < ROUNDS; ++h) trow[h] = wave * RPW + 16 * h + rr;
-    float* const tw = s_tr[wave];
+    // epilogue: the tile row this lane works on, and its lane group
+    const int erow = wave * RPW + F::lane_row(lane);
+    const int g_leader = RELU ? (lane & ~3) : (lane & 31);
+    const int g_member = RELU ? (lane & 3) : (lane >> 5);
+    constexpr int g_size = RELU ? 4 : 2;
 
     // every slot-table entry always holds a valid cache slot, so the prefetch
     // may read entries past the end of a pass's table
     for (int i = tid; i < kMaxPiece; i += NT) s_slot[i] = 0u;
 
     half8 qa[F::NQ];
-    float fT_r[ROUNDS];  // threshold scores of this lane's rows (Filter)
-    int cnt_r[ROUNDS];   // staged entries of this lane's rows (Filter)
-#pragma unroll
-    for (int h = 0; h < ROUNDS; ++h) {
-        fT_r[h] = 0.0f;
-        cnt_r[h] = 0;
-    }
-    int tile_r0 = -1;    // first row of the tile held in registers
+    float fT_r = 0.0f;  // threshold score of this lane's row (Filter)
+    int cnt_r = 0;      // staged entries of this lane's row (Filter)
+    int tile_r0 = -1;   // first row of the tile held in registers
 
     while (p < pend) {
         const int tile = (int)(p / span);
@@ -197,10 +206,8 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
         p += len;
         const int r0 = tile * TILE;
         const bool new_tile = r0 != tile_r0;
-        if (FILTER && new_tile && tile_r0 >= 0) {
-#pragma unroll
-            for (int h = 0; h < ROUNDS; ++h) flush_staged(A, s_lbuf + trow[h] * kLCap, tile_r0 + trow[h], cnt_r[h]);
-        }
+        if (FILTER && new_tile && tile_r0 >= 0)
+            flush_staged(A, s_lbuf + erow * kLCap, tile_r0 + erow, cnt_r, g_leader, g_member, g_size);
 
         for (int t = tid; t < TILE; t += NT) {
             const int r = r0 + t;
@@ -227,11 +234,11 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
             for (int t = 0; t < F::NQ; ++t) {
                 const int m = lane & 31;
                 int row, h, s;
-                if (RELU) {  // MFMA tile t/8: rows 8*(t/8) + m/4, head m%4; slice t%8
+                if (RELU) {  // A operand: MFMA tile t/8 rows 8*(t/8) + m/4, head m%4; slice t%8
                     row = wave * RPW + (t / kSlices) * 8 + (m >> 2);
                     h = m & 3;
                     s = t % kSlices;
-                } else {     // MFMA row m = row m; step t = (slice t/4, head t%4)
+                } else {     // B operand: column m = row m; step t = (slice t/4, head t%4)
                     row = wave * RPW + m;
                     h = t & 3;
                     s = t >> 2;
@@ -245,10 +252,7 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
             }
         }
         __syncthreads();
-        if (FILTER && new_tile) {
-#pragma unroll
-            for (int h = 0; h < ROUNDS; ++h) fT_r[h] = s_fT[trow[h]];
-        }
+        if (FILTER && new_tile) fT_r = s_fT[erow];
         tile_r0 = r0;
 
         for (;;) {
@@ -289,17 +293,12 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                 const int pg = min(max(ptrow[lp], 0), a.num_pages - 1);
                 s_slot[i] = (uint32_t)pg * (uint32_t)a.kpp + (uint32_t)slot;
             }
-            // this lane's row bounds, and the smallest over the wave's rows:
+            // this lane's row bound, and the smallest over the wave's rows:
             // column tiles entirely below it need no per-row mask
-            int lim_r[ROUNDS];
-            int wlim = 0x7FFFFFFF;
+            const int lim_r = s_lim[erow];
+            int wlim = lim_r;
 #pragma unroll
-            for (int h = 0; h < ROUNDS; ++h) {
-                lim_r[h] = s_lim[trow[h]];
-                wlim = min(wlim, lim_r[h]);
-            }
-#pragma unroll
-            for (int o = 4; o < 64; o <<= 1) wlim = min(wlim, __shfl_xor(wlim, o, 64));
+            for (int o = 1; o < 64; o <<= 1) wlim = min(wlim, __shfl_xor(wlim, o, 64));
             wlim = __builtin_amdgcn_readfirstlane(wlim);
             __syncthreads();
 
@@ -316,7 +315,7 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                     pf[i] = *reinterpret_cast<const u32x4*>(kc + (size_t)sl[i] * kHeadDim + pc * 8);
 #pragma unroll
                 for (int i = 0; i < S::NLOAD; ++i)
-                    *reinterpret_cast<u32x4*>(s_keys[0] + lds_key_chunk(pk + i, pc)) = pf[i];
+                    *reinterpret_cast<u32x4*>(s_keys[0] + lds_key_chunk(F::stage_row(pk + i), pc)) = pf[i];
             }
             int buf = 0;
             for (int j0 = c0; j0 < cend; j0 += kStepKeys) {
@@ -332,7 +331,6 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                 // keep the prefetch issued here, ahead of the MFMAs that hide it
                 __builtin_amdgcn_sched_barrier(0);
 
-                float sc[kSub][ROUNDS][8];
                 if (RELU) {
                     float16v acc[kSub][2];
 #pragma unroll
@@ -351,14 +349,67 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                                 acc[st][mt] = mfma32(qa[mt * kSlices + s], kbs[st], acc[st][mt]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
+                    float sc[kSub][8];
 #pragma unroll
                     for (int st = 0; st < kSub; ++st)
 #pragma unroll
                         for (int o = 0; o < 8; ++o) {
                             const int mt = o >> 2, g = o & 3;
-                            sc[st][0][o] = combine_relu_heads(acc[st][mt][4 * g], acc[st][mt][4 * g + 1],
-                                                              acc[st][mt][4 * g + 2], acc[st][mt][4 * g + 3]);
+                            sc[st][o] = combine_relu_heads(acc[st][mt][4 * g], acc[st][mt][4 * g + 1],
+                                                           acc[st][mt][4 * g + 2], acc[st][mt][4 * g + 3]);
                         }
+                    // stage the prefetched tile in the idle buffer (after the
+                    // last step this fills a buffer no wave reads any more:
+                    // every wave has passed this step's barrier)
+#pragma unroll
+                    for (int i = 0; i < S::NLOAD; ++i)
+                        *reinterpret_cast<u32x4*>(s_keys[buf ^ 1] + lds_key_chunk(F::stage_row(pk + i), pc)) = pf[i];
+
+                    float* const tw = s_tr[wave];
+                    const int rr = lane >> 2, cq = lane & 3;
+#pragma unroll
+                    for (int st = 0; st < kSub; ++st) {
+                        // transpose: lane (row rr, keys 8cq..8cq+7) of this column tile
+#pragma unroll
+                        for (int o = 0; o < 8; ++o)
+                            tw[(Form<true>::out_row(o) + (lane >> 5)) * kTrStride + (lane & 31)] = sc[st][o];
+                        __builtin_amdgcn_wave_barrier();
+                        const float4v v0 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq);
+                        const float4v v1 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq + 4);
+                        __builtin_amdgcn_wave_barrier();
+                        const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                        const int key0 = j0 + 32 * st + 8 * cq;
+                        const bool full = j0 + 32 * (st + 1) <= wlim;
+                        if (!FILTER) {
+                            float* dst = A.out + (int64_t)(r0 + erow) * A.ld + key0;
+                            if (full && A.vec_store) {
+                                *reinterpret_cast<float4v*>(dst) = v0;
+                                *reinterpret_cast<float4v*>(dst + 4) = v1;
+                            } else {
+#pragma unroll
+                                for (int i = 0; i < 8; ++i)
+                                    if (full || key0 + i < lim_r) dst[i] = v[i];
+                            }
+                        } else {
+                            bool kp[8];
+                            int n = 0;
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                kp[i] = v[i] >= fT_r && (full || key0 + i < lim_r);
+                                n += kp[i] ? 1 : 0;
+                            }
+                            int tot;
+                            const int excl = quad_exclusive_sum(n, &tot);
+                            uint64_t* lb = s_lbuf + erow * kLCap;
+                            if (__any(cnt_r + tot > kLCap))
+                                flush_staged(A, lb, r0 + erow, cnt_r, g_leader, g_member, g_size);
+                            int slot = cnt_r + excl;
+#pragma unroll
+                            for (int i = 0; i < 8; ++i)
+                                if (kp[i]) lb[slot++] = cand_entry(v[i], key0 + i);
+                            cnt_r += tot;
+                        }
+                    }
                 } else {
                     float16v acc[kSub];
 #pragma unroll
@@ -373,65 +424,67 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
 #pragma unroll
                         for (int h = 0; h < kHeads; ++h)
 #pragma unroll
-                            for (int st = 0; st < kSub; ++st) acc[st] = mfma32(qa[kHeads * s + h], kbs[st], acc[st]);
+                            for (int st = 0; st < kSub; ++st) acc[st] = mfma32(kbs[st], qa[kHeads * s + h], acc[st]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
+                    // stage the prefetched tile in the idle buffer (see above)
 #pragma unroll
-                    for (int st = 0; st < kSub; ++st)
-#pragma unroll
-                        for (int h = 0; h < ROUNDS; ++h)
-#pragma unroll
-                            for (int o = 0; o < 8; ++o) sc[st][h][o] = acc[st][8 * h + o];
-                }
-                // stage the prefetched tile in the idle buffer (after the last
-                // step this fills a buffer no wave reads any more: every wave
-                // has passed this step's barrier)
-#pragma unroll
-                for (int i = 0; i < S::NLOAD; ++i)
-                    *reinterpret_cast<u32x4*>(s_keys[buf ^ 1] + lds_key_chunk(pk + i, pc)) = pf[i];
+                    for (int i = 0; i < S::NLOAD; ++i)
+                        *reinterpret_cast<u32x4*>(s_keys[buf ^ 1] + lds_key_chunk(F::stage_row(pk + i), pc)) = pf[i];
 
 #pragma unroll
-                for (int st = 0; st < kSub; ++st) {
-                    const int key0 = j0 + 32 * st + 8 * cq;
-                    const bool full = j0 + 32 * (st + 1) <= wlim;
-#pragma unroll
-                    for (int h = 0; h < ROUNDS; ++h) {
-                        // transpose: lane (row rr, keys 8cq..8cq+7) of this round
-                        const int wr = F::HALF * (lane >> 5);
-#pragma unroll
-                        for (int o = 0; o < 8; ++o) tw[(wr + F::out_row(o)) * kTrStride + (lane & 31)] = sc[st][h][o];
-                        __builtin_amdgcn_wave_barrier();
-                        const float4v v0 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq);
-                        const float4v v1 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq + 4);
-                        __builtin_amdgcn_wave_barrier();
-                        const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    for (int st = 0; st < kSub; ++st) {
+                        // element v: key kb + v of row erow
+                        const int kb = j0 + 32 * st + 16 * (lane >> 5);
+                        const bool full = j0 + 32 * (st + 1) <= wlim;
                         if (!FILTER) {
-                            float* dst = A.out + (int64_t)(r0 + trow[h]) * A.ld + key0;
-                            if (full && A.vec_store) {
-                                *reinterpret_cast<float4v*>(dst) = v0;
-                                *reinterpret_cast<float4v*>(dst + 4) = v1;
-                            } else {
+                            // transpose through LDS so that 8 consecutive lanes store
+                            // 32 consecutive keys (128 bytes) of one row: lane l then
+                            // holds keys 4*(l%8) .. +3 of rows l/8 + 8i, i = 0..3
+                            float* const tw = s_tr[wave];
 #pragma unroll
-                                for (int i = 0; i < 8; ++i)
-                                    if (full || key0 + i < lim_r[h]) dst[i] = v[i];
+                            for (int j = 0; j < 4; ++j)
+                                *reinterpret_cast<float4v*>(tw + (lane & 31) * kTrStride + 16 * (lane >> 5) + 4 * j) =
+                                    float4v{acc[st][4 * j], acc[st][4 * j + 1], acc[st][4 * j + 2], acc[st][4 * j + 3]};
+                            __builtin_amdgcn_wave_barrier();
+                            float4v w[4];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                w[i] = *reinterpret_cast<const float4v*>(tw + ((lane >> 3) + 8 * i) * kTrStride + 4 * (lane & 7));
+                            __builtin_amdgcn_wave_barrier();
+                            const int key0 = j0 + 32 * st + 4 * (lane & 7);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int trow = wave * RPW + (lane >> 3) + 8 * i;
+                                float* dst = A.out + (int64_t)(r0 + trow) * A.ld + key0;
+                                if (full && A.vec_store) {
+                                    *reinterpret_cast<float4v*>(dst) = w[i];
+                                } else {
+                                    const int lim = s_lim[trow];
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e)
+                                        if (full || key0 + e < lim) dst[e] = w[i][e];
+                                }
                             }
                         } else {
-                            bool kp[8];
+                            bool kp[16];
                             int n = 0;
 #pragma unroll
-                            for (int i = 0; i < 8; ++i) {
-                                kp[i] = v[i] >= fT_r[h] && (full || key0 + i < lim_r[h]);
-                                n += kp[i] ? 1 : 0;
+                            for (int v = 0; v < 16; ++v) {
+                                kp[v] = acc[st][v] >= fT_r && (full || kb + v < lim_r);
+                                n += kp[v] ? 1 : 0;
                             }
-                            int tot;
-                            const int excl = quad_exclusive_sum(n, &tot);
-                            uint64_t* lb = s_lbuf + trow[h] * kLCap;
-                            if (__any(cnt_r[h] + tot > kLCap)) flush_staged(A, lb, r0 + trow[h], cnt_r[h]);
-                            int slot = cnt_r[h] + excl;
+                            // the row's two lanes (l and l ^ 32) hold keys kb..kb+15 and kb+16..kb+31
+                            const auto nn = __builtin_amdgcn_permlane32_swap(n, n, false, false);
+                            const int n_lo = (int)nn[0], tot = (int)nn[0] + (int)nn[1];
+                            uint64_t* lb = s_lbuf + erow * kLCap;
+                            if (__any(cnt_r + tot > kLCap))
+                                flush_staged(A, lb, r0 + erow, cnt_r, g_leader, g_member, g_size);
+                            int slot = cnt_r + ((lane >> 5) ? n_lo : 0);
 #pragma unroll
-                            for (int i = 0; i < 8; ++i)
-                                if (kp[i]) lb[slot++] = ((uint64_t)__float_as_uint(v[i]) << 32) | (uint32_t)(key0 + i);
-                            cnt_r[h] += tot;
+                            for (int v = 0; v < 16; ++v)
+                                if (kp[v]) lb[slot++] = cand_entry(acc[st][v], kb + v);
+                            cnt_r += tot;
                         }
                     }
                 }
@@ -442,10 +495,8 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
         }
         __syncthreads();
     }
-    if (FILTER && tile_r0 >= 0) {
-#pragma unroll
-        for (int h = 0; h < ROUNDS; ++h) flush_staged(A, s_lbuf + trow[h] * kLCap, tile_r0 + trow[h], cnt_r[h]);
-    }
+    if (FILTER && tile_r0 >= 0)
+        flush_staged(A, s_lbuf + erow * kLCap, tile_r0 + erow, cnt_r, g_leader, g_member, g_size);
 }
 
 }  // namespace qsa

@@ -467,13 +467,12 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                                 }
                             }
                         } else {
-                            bool kp[16];
-                            int n = 0;
+                            // bit v: element v passes the threshold (and is visible)
+                            uint32_t bits = 0u;
 #pragma unroll
-                            for (int v = 0; v < 16; ++v) {
-                                kp[v] = acc[st][v] >= fT_r && (full || kb + v < lim_r);
-                                n += kp[v] ? 1 : 0;
-                            }
+                            for (int v = 0; v < 16; ++v) bits |= (acc[st][v] >= fT_r ? 1u : 0u) << v;
+                            if (!full) bits &= (1u << min(max(lim_r - kb, 0), 16)) - 1u;
+                            const int n = __popc(bits);
                             // the row's two lanes (l and l ^ 32) hold keys kb..kb+15 and kb+16..kb+31
                             const auto nn = __builtin_amdgcn_permlane32_swap(n, n, false, false);
                             const int n_lo = (int)nn[0], tot = (int)nn[0] + (int)nn[1];
@@ -483,7 +482,7 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                             int slot = cnt_r + ((lane >> 5) ? n_lo : 0);
 #pragma unroll
                             for (int v = 0; v < 16; ++v)
-                                if (kp[v]) lb[slot++] = cand_entry(acc[st][v], kb + v);
+                                if ((bits >> v) & 1u) lb[slot++] = cand_entry(acc[st][v], kb + v);
                             cnt_r += tot;
                         }
                     }

@@ -467,22 +467,43 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                                 }
                             }
                         } else {
-                            // bit v: element v passes the threshold (and is visible)
-                            uint32_t bits = 0u;
+                            // element v (key kb + v) is kept if it reaches the threshold (and,
+                            // on a column tile that crosses a bound, is visible); the full and
+                            // the bounded tile each get their own straight-line code
+                            const int nv = full ? 16 : min(max(lim_r - kb, 0), 16);
+                            int n = 0;
+                            if (full) {
 #pragma unroll
-                            for (int v = 0; v < 16; ++v) bits |= (acc[st][v] >= fT_r ? 1u : 0u) << v;
-                            if (!full) bits &= (1u << min(max(lim_r - kb, 0), 16)) - 1u;
-                            const int n = __popc(bits);
+                                for (int v = 0; v < 16; ++v) n += acc[st][v] >= fT_r ? 1 : 0;
+                            } else {
+#pragma unroll
+                                for (int v = 0; v < 16; ++v) n += (acc[st][v] >= fT_r && v < nv) ? 1 : 0;
+                            }
                             // the row's two lanes (l and l ^ 32) hold keys kb..kb+15 and kb+16..kb+31
                             const auto nn = __builtin_amdgcn_permlane32_swap(n, n, false, false);
                             const int n_lo = (int)nn[0], tot = (int)nn[0] + (int)nn[1];
                             uint64_t* lb = s_lbuf + erow * kLCap;
                             if (__any(cnt_r + tot > kLCap))
                                 flush_staged(A, lb, r0 + erow, cnt_r, g_leader, g_member, g_size);
-                            int slot = cnt_r + ((lane >> 5) ? n_lo : 0);
+                            // entries as (key, score bits) word pairs
+                            uint32_t* lw = reinterpret_cast<uint32_t*>(lb) + 2 * (cnt_r + ((lane >> 5) ? n_lo : 0));
+                            if (full) {
 #pragma unroll
-                            for (int v = 0; v < 16; ++v)
-                                if ((bits >> v) & 1u) lb[slot++] = cand_entry(acc[st][v], kb + v);
+                                for (int v = 0; v < 16; ++v)
+                                    if (acc[st][v] >= fT_r) {
+                                        lw[0] = (uint32_t)(kb + v);
+                                        lw[1] = __float_as_uint(acc[st][v]);
+                                        lw += 2;
+                                    }
+                            } else {
+#pragma unroll
+                                for (int v = 0; v < 16; ++v)
+                                    if (acc[st][v] >= fT_r && v < nv) {
+                                        lw[0] = (uint32_t)(kb + v);
+                                        lw[1] = __float_as_uint(acc[st][v]);
+                                        lw += 2;
+                                    }
+                            }
                             cnt_r += tot;
                         }
                     }

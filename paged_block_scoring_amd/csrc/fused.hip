@@ -99,7 +99,7 @@ constexpr int kFinWaves = kFinNT / 64;
 // Exact top-kb of one row by recomputation: each wave scores 32 keys at a
 // time straight from the cache with the same MFMA sequences as the tiled
 // scorer, with zero query fragments outside the row (default form: keys as
-// MFMA rows, the row as column 0, heads in K; relu form: the row's four heads
+// MFMA rows, the row's head sum as column 0; relu form: the row's four heads
 // as MFMA rows 0..3, keys as columns).  Composites above the running cutoff are appended in
 // LDS, and the buffer is cut back to its kb largest whenever it exceeds kb.
 // Leaves the selected composites (unsorted) in a[0 .. return value).
@@ -141,13 +141,19 @@ __device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* 
                 }
                 sc = combine_relu_heads(acc[0], acc[1], acc[2], acc[3]);
             } else {
-                // keys as MFMA rows, the row as column 0
+                // keys as MFMA rows, the row's head sum (hi, lo) as column 0
 #pragma unroll
-                for (int t = 0; t < kHeads * kSlices; ++t) {
-                    half8 qv = {};
-                    const int s = t >> 2, h = t & 3;
-                    if (m == 0) qv = *reinterpret_cast<const half8*>(qrow + h * kHeadDim + 16 * s + 8 * g);
-                    acc = mfma32(kb8[s], qv, acc);
+                for (int s = 0; s < kSlices; ++s) {
+                    half8 hi = {}, lo = {};
+                    if (m == 0) {
+                        half8 h[kHeads];
+#pragma unroll
+                        for (int hh = 0; hh < kHeads; ++hh)
+                            h[hh] = *reinterpret_cast<const half8*>(qrow + hh * kHeadDim + 16 * s + 8 * g);
+                        head_sum_split(h[0], h[1], h[2], h[3], hi, lo);
+                    }
+                    acc = mfma32(kb8[s], hi, acc);
+                    acc = mfma32(kb8[s], lo, acc);
                 }
                 // lanes 0 and 32 hold the 32 scores (element v: key 8*(v/4) + 4*g + v%4);
                 // hand key m's score to lane m through LDS

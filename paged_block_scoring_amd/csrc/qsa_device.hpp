@@ -8,11 +8,15 @@
 // both operands, and the 32x32 output puts rows 8*(v/4) + 4*(l/32) + (v%4) of
 // column l%32 in accumulator element v of lane l.  Accumulation is fp32 from
 // +0 in the order given.
-//   default form (heads in K): the keys are the MFMA rows and the query rows
-//     its columns; a chain of 32 MFMAs, step t = (slice t/4, head t%4), with
-//     A = slice t/4 of the key and B = head t%4 of the query accumulates the
-//     whole score q_0.k + q_1.k + q_2.k + q_3.k in one sum.  Element v of
-//     lane l is the score of query column l%32 and key row
+//   default form (head sum in K): the score is linear in the query heads,
+//     sum_h q_h.k = (sum_h q_h).k, so each query row is first reduced to the
+//     fp32 head sum u = ((q_0 + q_1) + q_2) + q_3 (exact fp16 -> fp32 adds),
+//     carried as the fp16 pair hi = fp16(u), lo = fp16(u - hi), which
+//     represents u to a relative 2^-22 (exactly for small integers).  The
+//     keys are the MFMA rows and the query rows its columns; a chain of 16
+//     MFMAs, step t = (slice t/2, part t%2), with A = slice t/2 of the key and
+//     B = slice t/2 of hi (t even) or lo (t odd), accumulates the score in one
+//     sum.  Element v of lane l is the score of query column l%32 and key row
 //     8*(v/4) + 4*(l/32) + v%4.
 //   relu form (per head): MFMA row m = 4*row + head (8 query rows x 4 heads);
 //     a chain of 8 MFMAs over the slices gives every head's dot, elements
@@ -79,6 +83,18 @@ __device__ __forceinline__ uint32_t composite_index(uint64_t c) {
 
 __device__ __forceinline__ float16v mfma32(half8 a, half8 b, float16v c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// hi/lo fp16 pair of the fp32 head sum of 8 query dims (default form).
+__device__ __forceinline__ void head_sum_split(const half8& q0, const half8& q1, const half8& q2, const half8& q3,
+                                               half8& hi, half8& lo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float u = (((float)q0[i] + (float)q1[i]) + (float)q2[i]) + (float)q3[i];
+        const _Float16 h = (_Float16)u;
+        hi[i] = h;
+        lo[i] = (_Float16)(u - (float)h);
+    }
 }
 
 // The four head dots of one (row, key) -> score (relu form).

@@ -89,8 +89,8 @@ static_assert(ScoreShape::NLOAD == 4, "each thread stages 4 consecutive keys per
 // The two MFMA arrangements (qsa_device.hpp) as seen by the tiled kernel.
 template <bool RELU>
 struct Form;
-// default form: heads in K, keys as the MFMA rows and the wave's 32 query
-// rows as its columns.  Lane l's accumulator element v is MFMA row
+// default form: head sum in K, keys as the MFMA rows and the wave's 32
+// query rows as its columns.  Lane l's accumulator element v is MFMA row
 // 8*(v/4) + 4*(l/32) + v%4; the stage keeps key sigma(m) = 16*((m/4)%2) +
 // 4*(m/8) + m%4 of each 32-key column tile in LDS row m, so that element v is
 // key 16*(l/32) + v: every lane holds 16 consecutive keys of row l%32.
@@ -98,7 +98,7 @@ template <>
 struct Form<false> {
     static constexpr int RPW = 32;                 // rows per wave
     static constexpr int TILE = 4 * RPW;           // rows per tile
-    static constexpr int NQ = kHeads * kSlices;    // query fragments per lane: (slice, head)
+    static constexpr int NQ = 2 * kSlices;         // query fragments per lane: (slice, hi/lo)
     __device__ static int lane_row(int lane) { return lane & 31; }
     // LDS row of key n of a stage (the inverse of sigma within each column tile)
     __device__ static int stage_row(int n) {
@@ -230,25 +230,33 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
         }
         if (new_tile) {
             // query fragments of this wave's rows
+            if (RELU) {
 #pragma unroll
-            for (int t = 0; t < F::NQ; ++t) {
-                const int m = lane & 31;
-                int row, h, s;
-                if (RELU) {  // A operand: MFMA tile t/8 rows 8*(t/8) + m/4, head m%4; slice t%8
-                    row = wave * RPW + (t / kSlices) * 8 + (m >> 2);
-                    h = m & 3;
-                    s = t % kSlices;
-                } else {     // B operand: column m = row m; step t = (slice t/4, head t%4)
-                    row = wave * RPW + m;
-                    h = t & 3;
-                    s = t >> 2;
+                for (int t = 0; t < F::NQ; ++t) {
+                    // A operand: MFMA tile t/8 rows 8*(t/8) + m/4, head m%4; slice t%8
+                    const int m = lane & 31;
+                    const int row = r0 + wave * RPW + (t / kSlices) * 8 + (m >> 2);
+                    half8 v = {};
+                    if (row < a.rows)
+                        v = *reinterpret_cast<const half8*>(a.q + ((int64_t)row * kHeads + (m & 3)) * kHeadDim +
+                                                            16 * (t % kSlices) + 8 * (lane >> 5));
+                    qa[t] = v;
                 }
-                row += r0;
-                half8 v = {};
-                if (row < a.rows)
-                    v = *reinterpret_cast<const half8*>(a.q + ((int64_t)row * kHeads + h) * kHeadDim + 16 * s +
-                                                        8 * (lane >> 5));
-                qa[t] = v;
+            } else {
+                // B operand: column m = row m; step t = (slice t/2, hi/lo t%2)
+                const int row = r0 + wave * RPW + (lane & 31);
+#pragma unroll
+                for (int s = 0; s < kSlices; ++s) {
+                    half8 h[kHeads];
+#pragma unroll
+                    for (int hh = 0; hh < kHeads; ++hh) {
+                        h[hh] = half8{};
+                        if (row < a.rows)
+                            h[hh] = *reinterpret_cast<const half8*>(a.q + ((int64_t)row * kHeads + hh) * kHeadDim +
+                                                                    16 * s + 8 * (lane >> 5));
+                    }
+                    head_sum_split(h[0], h[1], h[2], h[3], qa[2 * s], qa[2 * s + 1]);
+                }
             }
         }
         __syncthreads();
@@ -422,9 +430,9 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                             kbs[st] = *reinterpret_cast<const half8*>(
                                 sk + lds_key_chunk(32 * st + (lane & 31), 2 * s + (lane >> 5)));
 #pragma unroll
-                        for (int h = 0; h < kHeads; ++h)
+                        for (int t = 2 * s; t < 2 * s + 2; ++t)
 #pragma unroll
-                            for (int st = 0; st < kSub; ++st) acc[st] = mfma32(kbs[st], qa[kHeads * s + h], acc[st]);
+                            for (int st = 0; st < kSub; ++st) acc[st] = mfma32(kbs[st], qa[t], acc[st]);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     // stage the prefetched tile in the idle buffer (see above)

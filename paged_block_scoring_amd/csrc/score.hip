@@ -8,28 +8,28 @@ namespace qsa {
 namespace {
 
 // Even shares of each XCD's (tile, key) positions, in whole stages: about
-// `wg_per_cu` workgroups per compute unit, but no share below `min_seg`
-// positions (a multiple of kStepKeys).
+// the form's resident workgroups per compute unit, but no share below
+// `min_seg` positions.
 template <bool RELU, Epi EPI>
-hipError_t launch_form(ScoreKernelArgs A, int32_t cus, int32_t wg_per_cu, int64_t min_seg, hipStream_t stream) {
-    using S = ScoreShape;
+hipError_t launch_form(ScoreKernelArgs A, int32_t cus, int64_t min_seg, hipStream_t stream) {
+    constexpr int64_t g = Stage<RELU>::STEP;
     A.tiles = (A.a.rows + Form<RELU>::TILE - 1) / Form<RELU>::TILE;
-    const int64_t stripe = ((int64_t)(A.lmax + kXcds - 1) / kXcds + kStepKeys - 1) / kStepKeys * kStepKeys;
+    const int64_t stripe = ((int64_t)(A.lmax + kXcds - 1) / kXcds + g - 1) / g * g;
     A.xcd_keys = (int32_t)stripe;
     const int64_t positions = (int64_t)A.tiles * stripe;
-    int64_t per_xcd = (int64_t)(cus / kXcds > 0 ? cus / kXcds : 1) * wg_per_cu;
-    int64_t seg = ((positions + per_xcd - 1) / per_xcd + kStepKeys - 1) / kStepKeys * kStepKeys;
-    if (seg < min_seg) seg = min_seg;
+    int64_t per_xcd = (int64_t)(cus / kXcds > 0 ? cus / kXcds : 1) * Form<RELU>::WG_PER_CU;
+    int64_t seg = ((positions + per_xcd - 1) / per_xcd + g - 1) / g * g;
+    if (seg < min_seg) seg = (min_seg + g - 1) / g * g;
     per_xcd = (positions + seg - 1) / seg;
     A.seg_len = seg;
-    score_tiles_kernel<RELU, EPI><<<dim3((unsigned)(kXcds * per_xcd)), S::NT, 0, stream>>>(A);
+    score_tiles_kernel<RELU, EPI><<<dim3((unsigned)(kXcds * per_xcd)), ScoreShape::NT, 0, stream>>>(A);
     return hipGetLastError();
 }
 
 template <Epi EPI>
 hipError_t launch_epi(const ScoreKernelArgs& A, int32_t cus, hipStream_t stream) {
-    if (A.a.relu) return launch_form<true, EPI>(A, cus, 2, kStepKeys, stream);
-    return launch_form<false, EPI>(A, cus, 2, kStepKeys, stream);
+    if (A.a.relu) return launch_form<true, EPI>(A, cus, 64, stream);
+    return launch_form<false, EPI>(A, cus, 64, stream);
 }
 
 }  // namespace

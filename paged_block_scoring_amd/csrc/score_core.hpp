@@ -47,6 +47,8 @@
 // Rows of different requests in one tile are processed in successive passes.
 #pragma once
 
+#include <type_traits>
+
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
 
@@ -54,9 +56,6 @@ namespace qsa {
 
 enum class Epi { Store, Filter };
 
-constexpr int kSub = 2;                // 32-key column tiles per LDS stage
-constexpr int kStepKeys = 32 * kSub;   // keys per LDS stage
-constexpr int kMaxPiece = 1024;        // logical keys per piece (slot-table size)
 constexpr int kLCap = 32;              // per-row LDS staging slots of the Filter epilogue (>= 32)
 constexpr int kXcds = 8;               // XCDs of an MI355X (256 CUs = 8 x 32)
 constexpr int kTrStride = 36;          // floats per row of the relu transpose buffer (32 + 4: conflict-free reads)
@@ -66,8 +65,8 @@ struct ScoreKernelArgs {
     int32_t stride;    // logical key i is key stride*i
     int32_t lmax;      // logical keys of the longest row: ceil(max_visible / stride)
     int32_t tiles;     // ceil(rows / rows per tile)
-    int32_t xcd_keys;  // logical keys per XCD stripe (a multiple of kStepKeys)
-    int64_t seg_len;   // (tile, key) positions per workgroup (a multiple of kStepKeys)
+    int32_t xcd_keys;  // logical keys per XCD stripe (a multiple of the stage size)
+    int64_t seg_len;   // (tile, key) positions per workgroup (a multiple of the stage size)
     // Store
     float* out;
     int64_t ld;
@@ -82,9 +81,7 @@ struct ScoreKernelArgs {
 struct ScoreShape {
     static constexpr int WAVES = 4;
     static constexpr int NT = 64 * WAVES;
-    static constexpr int NLOAD = kStepKeys * kChunksPerKey / NT;     // 16-byte pieces per thread per stage
 };
-static_assert(ScoreShape::NLOAD == 4, "each thread stages 4 consecutive keys per stage");
 
 // The two MFMA arrangements (qsa_device.hpp) as seen by the tiled kernel.
 template <bool RELU>
@@ -99,6 +96,9 @@ struct Form<false> {
     static constexpr int RPW = 32;                 // rows per wave
     static constexpr int TILE = 4 * RPW;           // rows per tile
     static constexpr int NQ = 2 * kSlices;         // query fragments per lane: (slice, hi/lo)
+    static constexpr int SUB = 1;                  // 32-key column tiles per LDS stage
+    static constexpr int MAXPIECE = 1024;          // logical keys per piece (slot-table size)
+    static constexpr int WG_PER_CU = 2;            // resident workgroups per compute unit
     __device__ static int lane_row(int lane) { return lane & 31; }
     // LDS row of key n of a stage (the inverse of sigma within each column tile)
     __device__ static int stage_row(int n) {
@@ -114,9 +114,21 @@ struct Form<true> {
     static constexpr int RPW = 16;
     static constexpr int TILE = 4 * RPW;
     static constexpr int NQ = 2 * kSlices;
+    static constexpr int SUB = 2;
+    static constexpr int MAXPIECE = 1024;
+    static constexpr int WG_PER_CU = 2;
     __device__ static constexpr int out_row(int o) { return 8 * (o >> 2) + 2 * (o & 3); }
     __device__ static int lane_row(int lane) { return lane >> 2; }
     __device__ static int stage_row(int n) { return n; }
+};
+
+// Stage geometry of a form: STEP keys per LDS stage, NLOAD 16-byte pieces
+// (consecutive keys) per thread per stage.
+template <bool RELU>
+struct Stage {
+    static constexpr int STEP = 32 * Form<RELU>::SUB;
+    static constexpr int NLOAD = STEP * kChunksPerKey / ScoreShape::NT;
+    static_assert(NLOAD * ScoreShape::NT == STEP * kChunksPerKey, "whole keys per thread");
 };
 
 // Quad (lanes 4k..4k+3) exclusive prefix sum of x; *total gets the quad sum.
@@ -153,17 +165,18 @@ __device__ __forceinline__ uint64_t cand_entry(float score, int key) {
 }
 
 template <bool RELU, Epi EPI>
-__global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKernelArgs A) {
-    using S = ScoreShape;
+__global__ __launch_bounds__(ScoreShape::NT, Form<RELU>::WG_PER_CU) void score_tiles_kernel(ScoreKernelArgs A) {
     using F = Form<RELU>;
-    constexpr int NT = S::NT, TILE = F::TILE, RPW = F::RPW;
+    constexpr int NT = ScoreShape::NT, TILE = F::TILE, RPW = F::RPW;
+    constexpr int kSub = F::SUB, kStepKeys = Stage<RELU>::STEP, NLOAD = Stage<RELU>::NLOAD;
+    constexpr int kMaxPiece = F::MAXPIECE;
     constexpr bool FILTER = EPI == Epi::Filter;
 
     __shared__ __attribute__((aligned(16))) unsigned char s_keys[2][kStepKeys * kKeyBytes];
     __shared__ __attribute__((aligned(16))) uint32_t s_slot[kMaxPiece];
     // per-wave transpose buffer: relu form (16 rows), default-form Store (32 rows)
     constexpr int TR_ROWS = RELU ? 16 : (FILTER ? 0 : 32);
-    __shared__ __attribute__((aligned(16))) float s_tr[TR_ROWS ? S::WAVES : 1][TR_ROWS ? TR_ROWS * kTrStride : 4];
+    __shared__ __attribute__((aligned(16))) float s_tr[TR_ROWS ? ScoreShape::WAVES : 1][TR_ROWS ? TR_ROWS * kTrStride : 4];
     __shared__ int32_t s_req[TILE], s_lv[TILE], s_todo[TILE], s_lim[TILE];
     __shared__ float s_fT[FILTER ? TILE : 1];
     __shared__ uint64_t s_lbuf[FILTER ? TILE * kLCap : 1];
@@ -181,8 +194,8 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
     int64_t p = (int64_t)loc * A.seg_len;
     const int64_t pend = min(p + A.seg_len, total);
 
-    // staging: this thread's 4 consecutive keys of a stage and its chunk
-    const int pk = 4 * (tid >> 4), pc = tid & 15;
+    // staging: this thread's NLOAD consecutive keys of a stage and its chunk
+    const int pk = NLOAD * (tid >> 4), pc = tid & 15;
     // epilogue: the tile row this lane works on, and its lane group
     const int erow = wave * RPW + F::lane_row(lane);
     const int g_leader = RELU ? (lane & ~3) : (lane & 31);
@@ -315,14 +328,15 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
             // buffer -> epilogue.  The epilogue's global stores are issued
             // after the wait, so they drain during the next step's MFMAs.
             const _Float16* kc = a.kcache;
-            u32x4 pf[S::NLOAD];
+            u32x4 pf[NLOAD];
+            using SlotVec = typename std::conditional<NLOAD == 4, u32x4, u32x2>::type;
             {
-                const u32x4 sl = *reinterpret_cast<const u32x4*>(&s_slot[pk]);
+                const SlotVec sl = *reinterpret_cast<const SlotVec*>(&s_slot[pk]);
 #pragma unroll
-                for (int i = 0; i < S::NLOAD; ++i)
+                for (int i = 0; i < NLOAD; ++i)
                     pf[i] = *reinterpret_cast<const u32x4*>(kc + (size_t)sl[i] * kHeadDim + pc * 8);
 #pragma unroll
-                for (int i = 0; i < S::NLOAD; ++i)
+                for (int i = 0; i < NLOAD; ++i)
                     *reinterpret_cast<u32x4*>(s_keys[0] + lds_key_chunk(F::stage_row(pk + i), pc)) = pf[i];
             }
             int buf = 0;
@@ -330,10 +344,10 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                 __syncthreads();
                 const unsigned char* sk = s_keys[buf];
                 {
-                    const int li = min(j0 + kStepKeys - c0 + pk, kMaxPiece - 4);
-                    const u32x4 sl = *reinterpret_cast<const u32x4*>(&s_slot[li]);
+                    const int li = min(j0 + kStepKeys - c0 + pk, kMaxPiece - NLOAD);
+                    const SlotVec sl = *reinterpret_cast<const SlotVec*>(&s_slot[li]);
 #pragma unroll
-                    for (int i = 0; i < S::NLOAD; ++i)
+                    for (int i = 0; i < NLOAD; ++i)
                         pf[i] = *reinterpret_cast<const u32x4*>(kc + (size_t)sl[i] * kHeadDim + pc * 8);
                 }
                 // keep the prefetch issued here, ahead of the MFMAs that hide it
@@ -370,7 +384,7 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                     // last step this fills a buffer no wave reads any more:
                     // every wave has passed this step's barrier)
 #pragma unroll
-                    for (int i = 0; i < S::NLOAD; ++i)
+                    for (int i = 0; i < NLOAD; ++i)
                         *reinterpret_cast<u32x4*>(s_keys[buf ^ 1] + lds_key_chunk(F::stage_row(pk + i), pc)) = pf[i];
 
                     float* const tw = s_tr[wave];
@@ -437,7 +451,7 @@ __global__ __launch_bounds__(ScoreShape::NT, 2) void score_tiles_kernel(ScoreKer
                     __builtin_amdgcn_sched_barrier(0);
                     // stage the prefetched tile in the idle buffer (see above)
 #pragma unroll
-                    for (int i = 0; i < S::NLOAD; ++i)
+                    for (int i = 0; i < NLOAD; ++i)
                         *reinterpret_cast<u32x4*>(s_keys[buf ^ 1] + lds_key_chunk(F::stage_row(pk + i), pc)) = pf[i];
 
 #pragma unroll

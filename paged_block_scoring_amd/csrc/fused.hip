@@ -50,9 +50,10 @@ __device__ __forceinline__ int row_visible_count(const VisibleSource& v, int r) 
 constexpr int kThrNT = 256;
 constexpr int kMaxSamples = 4096;
 
-// Threshold of one row: the score whose order key is the m-th largest sample
-// order key (found by a histogram descent), so at least m samples reach it.
-// Stored as a composite whose high word is that key.
+// Threshold of one row: the samples are binned linearly by value between
+// their minimum and maximum (the bin index is monotone in the value); T is
+// the smallest sample of the bin holding the m-th largest, so at least m
+// samples are >= T.  Stored as a composite whose high word is T's order key.
 __global__ __launch_bounds__(kThrNT) void sample_threshold_kernel(const float* __restrict__ samp, int64_t ld_s,
                                                                   VisibleSource vis, int32_t stride, int32_t m,
                                                                   int32_t force_fallback,
@@ -60,20 +61,81 @@ __global__ __launch_bounds__(kThrNT) void sample_threshold_kernel(const float* _
                                                                   int32_t* __restrict__ cand_count) {
     constexpr int EPT = kMaxSamples / kThrNT;
     __shared__ HistScratch hs;
+    __shared__ float s_f[2 * (kThrNT / 64)];
     const int row = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int V = row_visible_count(vis, row);
     const int ns = (V + stride - 1) / stride;
     uint64_t T = ~0ull;  // decodes to a NaN threshold score: nothing passes
     if (ns >= m && !force_fallback) {
         const float* srow = samp + (int64_t)row * ld_s;
-        uint32_t k[EPT];
+        float x[EPT];
+        float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const int i = e * kThrNT + (int)threadIdx.x;
-            k[e] = (e * kThrNT < ns && i < ns) ? order_key(srow[i]) : 0u;
+            x[e] = 0.0f;
+            if (e * kThrNT < ns && i < ns) {
+                x[e] = srow[i];
+                lo = fminf(lo, x[e]);
+                hi = fmaxf(hi, x[e]);
+            }
         }
-        const Descent d = hist_descent32<kThrNT, EPT>(k, ns, m, &hs, nullptr);
-        T = (uint64_t)d.pivot << 32;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            lo = fminf(lo, __shfl_xor(lo, o, 64));
+            hi = fmaxf(hi, __shfl_xor(hi, o, 64));
+        }
+        if (lane == 0) {
+            s_f[wave] = lo;
+            s_f[kThrNT / 64 + wave] = hi;
+        }
+        for (int i = threadIdx.x; i < kSelBins; i += kThrNT) hs.hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kThrNT / 64; ++w) {
+            lo = fminf(lo, s_f[w]);
+            hi = fmaxf(hi, s_f[kThrNT / 64 + w]);
+        }
+        float t = lo;
+        const float scale = (float)kSelBins / (hi - lo);
+        if (hi > lo && scale < __builtin_huge_valf()) {  // (block-uniform)
+            auto bin = [&](float v) { return min((int)((v - lo) * scale), kSelBins - 1); };
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                if (e * kThrNT < ns && e * kThrNT + (int)threadIdx.x < ns) atomicAdd(&hs.hist[bin(x[e])], 1u);
+            __syncthreads();
+            // thread u owns bins kSelBins-1-BPT*u .. (high to low); find the bin of the m-th largest
+            constexpr int BPT = kSelBins / kThrNT;
+            uint32_t c[BPT];
+            int local = 0;
+#pragma unroll
+            for (int j = 0; j < BPT; ++j) {
+                c[j] = hs.hist[kSelBins - 1 - BPT * (int)threadIdx.x - j];
+                local += (int)c[j];
+            }
+            int tot;
+            int run = block_inclusive_scan<kThrNT>(local, hs.wsum, &tot) - local;
+#pragma unroll
+            for (int j = 0; j < BPT; ++j) {
+                if (run < m && run + (int)c[j] >= m) hs.bin = kSelBins - 1 - BPT * (int)threadIdx.x - j;
+                run += (int)c[j];
+            }
+            __syncthreads();
+            const int b = hs.bin;
+            float tm = __builtin_huge_valf();
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                if (e * kThrNT < ns && e * kThrNT + (int)threadIdx.x < ns && bin(x[e]) == b) tm = fminf(tm, x[e]);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) tm = fminf(tm, __shfl_xor(tm, o, 64));
+            if (lane == 0) s_f[wave] = tm;
+            __syncthreads();
+            t = s_f[0];
+#pragma unroll
+            for (int w = 1; w < kThrNT / 64; ++w) t = fminf(t, s_f[w]);
+        }
+        T = (uint64_t)order_key(t) << 32;
     }
     if (threadIdx.x == 0) {
         thresh[row] = T;
@@ -189,9 +251,16 @@ __device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* 
 constexpr int kMaxBucket = 32;
 constexpr int kRecChunk = 512;  // keys scored per round by the recompute path
 
-// Writes rank r's block (expanded to `expand` tokens) into the output row.
-__device__ __forceinline__ void write_rank(int32_t* orow, int r, uint32_t idx, int expand) {
+// Writes rank r's block (expanded to `expand` tokens) into the output row
+// (one 16-byte store for the usual 4-token blocks; out_len is then a
+// multiple of 4 and the row 16-byte aligned).
+__device__ __forceinline__ void write_rank(int32_t* orow, int r, uint32_t idx, int expand, bool vec4) {
     const int base = (int)idx * expand;
+    if (vec4) {
+        typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<i32x4*>(orow + 4 * r) = i32x4{base, base + 1, base + 2, base + 3};
+        return;
+    }
     for (int t = 0; t < expand; ++t) orow[r * expand + t] = base + t;
 }
 
@@ -217,6 +286,7 @@ __global__ __launch_bounds__(kFinNT) void fused_final_kernel(FinalArgs A) {
     const int nsel = min(kb, V);
     const int n = A.cand_count[row];
     int32_t* orow = A.out + (int64_t)row * A.out_len;
+    const bool vec4 = A.expand == 4 && (A.out_len & 3) == 0 && (reinterpret_cast<uintptr_t>(A.out) & 15) == 0;
     if (n < nsel || n > A.cand_cap) return;  // fused_recompute_kernel's row
     {
         if (nsel > 0) {
@@ -266,13 +336,13 @@ __global__ __launch_bounds__(kFinNT) void fused_final_kernel(FinalArgs A) {
                 } else {
                     int r = 0;
                     for (int i = st; i < st + cnt; ++i) r += s_a[i] > me ? 1 : 0;
-                    write_rank(orow, st + r, composite_index(me), A.expand);
+                    write_rank(orow, st + r, composite_index(me), A.expand, vec4);
                 }
             }
             __syncthreads();
             if (hs.flag) {
                 lds_sort_desc<kFinNT>(s_a, nsel);
-                for (int r = threadIdx.x; r < nsel; r += kFinNT) write_rank(orow, r, composite_index(s_a[r]), A.expand);
+                for (int r = threadIdx.x; r < nsel; r += kFinNT) write_rank(orow, r, composite_index(s_a[r]), A.expand, vec4);
             }
         }
         for (int i = nsel * A.expand + (int)threadIdx.x; i < A.out_len; i += kFinNT) orow[i] = -1;

@@ -265,19 +265,20 @@ __device__ __forceinline__ void write_rank(int32_t* orow, int r, uint32_t idx, i
 }
 
 // One row per workgroup.  Candidate path: the row's candidates are loaded
-// into registers as (order key, index); a histogram descent over the order
-// keys finds the cut of the top kb (ties at the cut are broken by a second
-// descent over inverted indices); the selected entries are scattered into LDS
-// grouped by their top-level bin (bins are ordered, so a group starts at the
-// number of selected entries in higher bins) and each takes its rank inside
-// the group by counting larger members.  A group larger than kMaxBucket
-// (heavy clustering or ties) switches the row to a bitonic sort of the
-// selected set.  Rows whose candidate list is unusable take the recompute
-// path.
+// into registers as (order key, index) and binned by order key over their
+// range (kSelBins ordered bins); with start[bin] = entries in higher bins,
+// every entry of a bin at or above the bin b holding the kb-th largest is
+// scattered into LDS at start[bin] + (its arrival in the bin) and ranks
+// itself inside its bin by counting larger members: ranks below min(kb, V)
+// are the selection, already in rank order.  A bin at or above b with more
+// than kMaxBucket entries (heavy clustering or ties) switches the row to an
+// exact histogram descent (ties at the cut broken by a second descent over
+// inverted indices) and a bitonic sort of the selected set.  Rows whose
+// candidate list is unusable take the recompute path.
 template <int KBMAX, int CAPC>
 __global__ __launch_bounds__(kFinNT) void fused_final_kernel(FinalArgs A) {
     constexpr int EPT = CAPC / kFinNT;
-    __shared__ uint64_t s_a[KBMAX];
+    __shared__ uint64_t s_a[KBMAX + kMaxBucket];
     __shared__ uint32_t s_start[kSelBins];
     __shared__ HistScratch hs;
     const int row = blockIdx.x;
@@ -303,44 +304,63 @@ __global__ __launch_bounds__(kFinNT) void fused_final_kernel(FinalArgs A) {
                     idx[e] = (uint32_t)en;
                 }
             }
-            // selection: sel(e) = k > pivot, or k == pivot and (exact or ~idx >= jpiv)
-            const Descent d = hist_descent32<kFinNT, EPT>(k, n, nsel, &hs, s_start);
-            uint32_t jpiv = 0u;
-            if (!d.exact) {
-                uint32_t t[EPT];
+            // one histogram level over the order keys: the bin b holding the
+            // kb-th largest; every entry of a bin >= b is scattered into LDS at
+            // start[bin] + (its arrival in the bin) and ranks itself inside its
+            // bin; ranks below nsel are the selection
+            uint32_t mn, mx;
+            block_minmax_u32<kFinNT, EPT>(k, n, &mn, &mx, &hs);
+            const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
+            int above, cnt;
+            const int b = (int)hist_level32<kFinNT, EPT>(k, n, mn, shift1, 32, 0u, nsel, &hs, s_start, &above, &cnt);
+            bool slow = cnt > kMaxBucket;
+            if (!slow) {
+                for (int i = threadIdx.x; i < kSelBins; i += kFinNT) hs.hist[i] = 0u;
+                if (threadIdx.x == 0) hs.flag = 0;
+                __syncthreads();
 #pragma unroll
-                for (int e = 0; e < EPT; ++e) t[e] = (e * kFinNT < n && k[e] && k[e] == d.pivot) ? ~idx[e] : 0u;
-                jpiv = hist_descent32<kFinNT, EPT>(t, n, nsel - d.above, &hs, nullptr).pivot;
-            }
-            for (int i = threadIdx.x; i < kSelBins; i += kFinNT) hs.hist[i] = 0u;
-            if (threadIdx.x == 0) hs.flag = 0;
-            __syncthreads();
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                const bool sel = e * kFinNT < n && k[e] &&
-                                 (k[e] > d.pivot || (k[e] == d.pivot && (d.exact || ~idx[e] >= jpiv)));
-                if (sel) {
-                    const uint32_t b1 = (k[e] - d.base) >> d.shift1;
-                    s_a[s_start[b1] + atomicAdd(&hs.hist[b1], 1u)] = compose(k[e], idx[e]);
+                for (int e = 0; e < EPT; ++e) {
+                    if (e * kFinNT < n && k[e]) {
+                        const uint32_t bn = (k[e] - mn) >> shift1;
+                        if ((int)bn >= b) s_a[s_start[bn] + atomicAdd(&hs.hist[bn], 1u)] = compose(k[e], idx[e]);
+                    }
                 }
-            }
-            __syncthreads();
-            // rank inside the bin group; a crowded group defers the row to the
-            // sort below (ranks written here are exact either way)
-            for (int p = threadIdx.x; p < nsel; p += kFinNT) {
-                const uint64_t me = s_a[p];
-                const uint32_t b1 = ((uint32_t)(me >> 32) - d.base) >> d.shift1;
-                const int st = (int)s_start[b1], cnt = (int)hs.hist[b1];
-                if (cnt > kMaxBucket) {
-                    hs.flag = 1;
-                } else {
+                __syncthreads();
+                for (int p = threadIdx.x; p < above + cnt; p += kFinNT) {
+                    const uint64_t me = s_a[p];
+                    const uint32_t bn = ((uint32_t)(me >> 32) - mn) >> shift1;
+                    const int st = (int)s_start[bn], cn = (int)hs.hist[bn];
+                    if (cn > kMaxBucket) {
+                        hs.flag = 1;  // a crowded bin above b: the row takes the sort below
+                        continue;
+                    }
                     int r = 0;
-                    for (int i = st; i < st + cnt; ++i) r += s_a[i] > me ? 1 : 0;
-                    write_rank(orow, st + r, composite_index(me), A.expand, vec4);
+                    for (int i = st; i < st + cn; ++i) r += s_a[i] > me ? 1 : 0;
+                    if (st + r < nsel) write_rank(orow, st + r, composite_index(me), A.expand, vec4);
                 }
+                __syncthreads();
+                slow = hs.flag != 0;
             }
-            __syncthreads();
-            if (hs.flag) {
+            if (slow) {
+                // exact pivot by a histogram descent (ties at the cut broken by a
+                // second descent over inverted indices), then a bitonic sort
+                const Descent d = hist_descent32<kFinNT, EPT>(k, n, nsel, &hs, nullptr);
+                uint32_t jpiv = 0u;
+                if (!d.exact) {
+                    uint32_t t[EPT];
+#pragma unroll
+                    for (int e = 0; e < EPT; ++e) t[e] = (e * kFinNT < n && k[e] && k[e] == d.pivot) ? ~idx[e] : 0u;
+                    jpiv = hist_descent32<kFinNT, EPT>(t, n, nsel - d.above, &hs, nullptr).pivot;
+                }
+                if (threadIdx.x == 0) hs.cnt = 0;
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) {
+                    const bool sel = e * kFinNT < n && k[e] &&
+                                     (k[e] > d.pivot || (k[e] == d.pivot && (d.exact || ~idx[e] >= jpiv)));
+                    if (sel) s_a[atomicAdd(&hs.cnt, 1)] = compose(k[e], idx[e]);
+                }
+                __syncthreads();
                 lds_sort_desc<kFinNT>(s_a, nsel);
                 for (int r = threadIdx.x; r < nsel; r += kFinNT) write_rank(orow, r, composite_index(s_a[r]), A.expand, vec4);
             }

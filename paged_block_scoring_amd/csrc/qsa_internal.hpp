@@ -28,6 +28,13 @@ struct PagedArgs {
 // Scorer: writes scores[r*ld + j] for j < V_r.
 hipError_t launch_score_paged(const PagedArgs& a, float* scores, int64_t ld, hipStream_t stream);
 
+// Rows per window of the few-rows-per-request scorer: the rows per request
+// rounded up to a power of two, at most 32 (8 in the relu form).
+int32_t group_rows_for(int32_t rows, int32_t num_reqs, bool relu);
+
+// Few-rows-per-request scorer (score_group.hip): same scores as the tiled one.
+hipError_t launch_score_group(const PagedArgs& a, float* out, int64_t ld, hipStream_t stream);
+
 // Scorer over logical keys i (key stride*i): out[r*ld + i] for i < ceil(V_r/stride).
 hipError_t launch_score_store(const PagedArgs& a, int32_t stride, float* out, int64_t ld, int32_t cus,
                               hipStream_t stream);

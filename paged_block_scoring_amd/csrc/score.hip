@@ -1,6 +1,9 @@
 // score.hip -- launchers of the tiled scoring kernel (score_core.hpp): the
 // materialising scorer behind qsa_score_paged and the two-pass arm, the
 // strided sampling pass and the filtering pass of the fused arm.
+#include <stdlib.h>
+#include <string.h>
+
 #include "qsa_internal.hpp"
 #include "score_core.hpp"
 
@@ -47,7 +50,20 @@ hipError_t launch_score_store(const PagedArgs& a, int32_t stride, float* out, in
     return launch_epi<Epi::Store>(A, cus, stream);
 }
 
+// The tiled scorer shares each staged key among a tile's rows; with fewer than
+// 32 rows per request on average those rows mostly belong to different
+// requests, and the windowed scorer, which streams every key once per window,
+// takes over.
+static bool use_group_scorer(const PagedArgs& a) {
+    const char* f = getenv("QSA_FORCE_SCORER");
+    if (f && strcmp(f, "tiles") == 0) return false;
+    if (f && strcmp(f, "groups") == 0) return true;
+    const int32_t reqs = a.num_reqs > 0 ? a.num_reqs : 1;
+    return a.rows / reqs < 32;
+}
+
 hipError_t launch_score_paged(const PagedArgs& a, float* scores, int64_t ld, hipStream_t stream) {
+    if (use_group_scorer(a)) return launch_score_group(a, scores, ld, stream);
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     return launch_score_store(a, 1, scores, ld, cus, stream);

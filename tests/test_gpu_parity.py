@@ -166,6 +166,42 @@ def test_reduced(oracle_mod, name, integer, flags):
     full_parity(oracle_mod, w, flags, integer or name == "tie_stress_96", paths=PATHS)
 
 
+@contextlib.contextmanager
+def force_scorer(name):
+    """Pick the scorer behind qsa_score_paged and the two-pass arm: "tiles"
+    (rows of a tile share staged keys) or "groups" (each wave streams the keys
+    of a small row window)."""
+    old = os.environ.get("QSA_FORCE_SCORER")
+    os.environ["QSA_FORCE_SCORER"] = name
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("QSA_FORCE_SCORER", None)
+        else:
+            os.environ["QSA_FORCE_SCORER"] = old
+
+
+@pytest.mark.parametrize("flags", [0, RELU])
+@pytest.mark.parametrize("name", ["kernel_shape_80", "mixed_small", "decode_small", "three_reqs_40"])
+def test_scorers_bit_identical(oracle_mod, name, flags):
+    """Both scorers run the same MFMA chain on the same operands, so their
+    scores must agree to the bit (windows of 32 / 8 rows here straddle request
+    boundaries and end in ragged tails)."""
+    w = REDUCED[name](False)
+    d = to_dev(w)
+    V = visible(oracle_mod, w)
+    with force_scorer("tiles"):
+        a = gpu_scores(d, w, flags)
+    with force_scorer("groups"):
+        b = gpu_scores(d, w, flags)
+    for r in range(w.rows):
+        assert np.array_equal(a[r, :V[r]].view(np.uint32), b[r, :V[r]].view(np.uint32)), f"row {r}"
+    with force_scorer("groups"), force_path("two_pass"):
+        out = gpu_select(d, w, flags)
+    assert np.array_equal(out, expected_from_scores(oracle_mod, a, V, w.k, w.compress_ratio, flags))
+
+
 def test_out_keys_reduced(oracle_mod):
     w = W.kernel_shape(rows=40, ctx=30_000)
     d = to_dev(w)

@@ -194,7 +194,7 @@ def time_calls(fn, steps, warmup, torch):
 
 
 KERNELS = {
-    "fused": ["sample_scorer", "sample_threshold", "filter_scorer", "final_select"],
+    "fused": ["qsum_prep", "sample_scorer", "sample_threshold", "filter_scorer", "final_select"],
     "two_pass": ["scorer", "topk_rows"],
 }
 

@@ -150,22 +150,28 @@ qsa::PagedArgs make_paged(const void* q, const void* kcache, const int32_t* page
 // Two-pass arm: fp32 scores [rows][ld] in the workspace, then the selector.
 int64_t two_pass_ld(int32_t max_visible) { return ceil_div(max_visible > 0 ? max_visible : 1, 64) * 64; }
 
-size_t two_pass_bytes(int32_t rows, int32_t max_visible) {
-    return (size_t)rows * (size_t)two_pass_ld(max_visible) * sizeof(float);
-}
-
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// scores, then the prepared query head sums
+size_t two_pass_scores_bytes(int32_t rows, int32_t max_visible) {
+    return align256((size_t)rows * (size_t)two_pass_ld(max_visible) * sizeof(float));
+}
+size_t two_pass_bytes(int32_t rows, int32_t max_visible) {
+    return two_pass_scores_bytes(rows, max_visible) + qsa::qsum_bytes(rows);
+}
 
 // Fused arm: sample scores, per-row threshold and candidate count, candidate lists.
 struct FusedLayout {
     qsa::FusedPlan plan;
-    size_t off_samp, off_thresh, off_count, off_cand, total;
+    size_t off_qsum, off_samp, off_thresh, off_count, off_cand, total;
 };
 
 FusedLayout fused_layout(int32_t rows, int32_t max_visible, int32_t kb) {
     FusedLayout L;
     L.plan = qsa::plan_fused(max_visible, kb);
     size_t o = 0;
+    L.off_qsum = o;
+    o = align256(o + qsa::qsum_bytes(rows));
     L.off_samp = o;
     o = align256(o + (size_t)rows * (size_t)L.plan.ld_s * sizeof(float));
     L.off_thresh = o;
@@ -239,7 +245,7 @@ QSA_EXPORT qsa_status qsa_score_paged(const void* q, const void* kcache, const i
     if ((st = check_device(&dev)) != QSA_OK) return st;
     qsa::PagedArgs a = make_paged(q, kcache, page_table, pt_stride, num_pages, num_reqs, row_req, pos, rows,
                                   page_size, compress_ratio, max_visible, flags);
-    HIP_CHECK(qsa::launch_score_paged(a, scores, ld_scores, static_cast<hipStream_t>(stream)));
+    HIP_CHECK(qsa::launch_score_paged(a, nullptr, scores, ld_scores, static_cast<hipStream_t>(stream)));
     return QSA_OK;
 }
 
@@ -341,13 +347,16 @@ QSA_EXPORT qsa_status qsa_select_paged_tokens(const void* q, const void* kcache,
         uint64_t* thresh = reinterpret_cast<uint64_t*>(w + L.off_thresh);
         int32_t* count = reinterpret_cast<int32_t*>(w + L.off_count);
         uint64_t* cand = reinterpret_cast<uint64_t*>(w + L.off_cand);
+        _Float16* qsum = a.relu ? nullptr : reinterpret_cast<_Float16*>(w + L.off_qsum);
         const int cus = device_cus();
         HIP_CHECK(mark(s));
-        HIP_CHECK(qsa::launch_score_store(a, L.plan.stride, samp, L.plan.ld_s, cus, s));
+        if (qsum) HIP_CHECK(qsa::launch_qsum_prep(a, qsum, s));
+        HIP_CHECK(mark(s));
+        HIP_CHECK(qsa::launch_score_store(a, qsum, L.plan.stride, samp, L.plan.ld_s, cus, s));
         HIP_CHECK(mark(s));
         HIP_CHECK(qsa::launch_sample_threshold(samp, L.plan.ld_s, vs, L.plan, force_fallback(), thresh, count, rows, s));
         HIP_CHECK(mark(s));
-        HIP_CHECK(qsa::launch_score_filter(a, thresh, cand, count, L.plan.cand_cap, cus, s));
+        HIP_CHECK(qsa::launch_score_filter(a, qsum, thresh, cand, count, L.plan.cand_cap, cus, s));
         HIP_CHECK(mark(s));
         HIP_CHECK(qsa::launch_fused_final(a, vs, L.plan, cand, count, kb, expand, k, out, s));
         HIP_CHECK(mark(s));
@@ -358,7 +367,10 @@ QSA_EXPORT qsa_status qsa_select_paged_tokens(const void* q, const void* kcache,
     float* scores = static_cast<float*>(workspace);
     const int64_t ld = two_pass_ld(max_visible);
     HIP_CHECK(mark(s));
-    if (max_visible > 0) HIP_CHECK(qsa::launch_score_paged(a, scores, ld, s));
+    _Float16* qsum = a.relu ? nullptr
+                            : reinterpret_cast<_Float16*>(static_cast<unsigned char*>(workspace) +
+                                                          two_pass_scores_bytes(rows, max_visible));
+    if (max_visible > 0) HIP_CHECK(qsa::launch_score_paged(a, qsum, scores, ld, s));
     HIP_CHECK(mark(s));
     HIP_CHECK(qsa::launch_topk_rows(scores, ld, vs, rows, kb, expand, k, out, s));
     HIP_CHECK(mark(s));

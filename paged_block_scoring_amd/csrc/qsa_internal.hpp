@@ -25,8 +25,16 @@ struct PagedArgs {
     bool relu;
 };
 
-// Scorer: writes scores[r*ld + j] for j < V_r.
-hipError_t launch_score_paged(const PagedArgs& a, float* scores, int64_t ld, hipStream_t stream);
+// Head sums of the query rows (default form) in the MFMA fragment order of
+// the row-tiled scorer: qsum[((tile*4 + wave)*16 + t)*64 + lane] holds 8
+// fp16 values, t = 2*slice + (0: hi, 1: lo); zero for rows past the end.
+size_t qsum_bytes(int32_t rows);
+hipError_t launch_qsum_prep(const PagedArgs& a, _Float16* qsum, hipStream_t stream);
+
+// Scorer: writes scores[r*ld + j] for j < V_r.  qsum (default form) may be
+// null, in which case the scorer forms the head sums itself.
+hipError_t launch_score_paged(const PagedArgs& a, const _Float16* qsum, float* scores, int64_t ld,
+                              hipStream_t stream);
 
 // Rows per window of the few-rows-per-request scorer: the rows per request
 // rounded up to a power of two, at most 32 (8 in the relu form).
@@ -36,12 +44,12 @@ int32_t group_rows_for(int32_t rows, int32_t num_reqs, bool relu);
 hipError_t launch_score_group(const PagedArgs& a, float* out, int64_t ld, hipStream_t stream);
 
 // Scorer over logical keys i (key stride*i): out[r*ld + i] for i < ceil(V_r/stride).
-hipError_t launch_score_store(const PagedArgs& a, int32_t stride, float* out, int64_t ld, int32_t cus,
-                              hipStream_t stream);
+hipError_t launch_score_store(const PagedArgs& a, const _Float16* qsum, int32_t stride, float* out, int64_t ld,
+                              int32_t cus, hipStream_t stream);
 
 // Scorer that appends every composite >= thresh[r] to row r's candidate list.
-hipError_t launch_score_filter(const PagedArgs& a, const uint64_t* thresh, uint64_t* cand, int32_t* cand_count,
-                               int32_t cand_cap, int32_t cus, hipStream_t stream);
+hipError_t launch_score_filter(const PagedArgs& a, const _Float16* qsum, const uint64_t* thresh, uint64_t* cand,
+                               int32_t* cand_count, int32_t cand_cap, int32_t cus, hipStream_t stream);
 
 // Where a selector takes each row's candidate count from.
 struct VisibleSource {

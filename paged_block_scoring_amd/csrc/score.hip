@@ -29,19 +29,49 @@ hipError_t launch_form(ScoreKernelArgs A, int32_t cus, int64_t min_seg, hipStrea
     return hipGetLastError();
 }
 
+// Default form: the row-tiled scorer of score_rows.hpp, same share rule.
+template <Epi EPI>
+hipError_t launch_rows(const ScoreKernelArgs& K, int32_t cus, int64_t min_seg, hipStream_t stream) {
+    constexpr int64_t g = RowsShape::STEP;
+    RowsArgs A = {};
+    A.a = K.a;
+    A.qsum = K.qsum;
+    A.stride = K.stride;
+    A.lmax = K.lmax;
+    A.out = K.out;
+    A.ld = K.ld;
+    A.vec_store = K.vec_store;
+    A.thresh = K.thresh;
+    A.cand = K.cand;
+    A.cand_count = K.cand_count;
+    A.cand_cap = K.cand_cap;
+    A.tiles = (A.a.rows + RowsShape::TILE - 1) / RowsShape::TILE;
+    const int64_t stripe = ((int64_t)(A.lmax + kXcds - 1) / kXcds + g - 1) / g * g;
+    A.xcd_keys = (int32_t)stripe;
+    const int64_t positions = (int64_t)A.tiles * stripe;
+    int64_t per_xcd = (int64_t)(cus / kXcds > 0 ? cus / kXcds : 1) * 2;
+    int64_t seg = ((positions + per_xcd - 1) / per_xcd + g - 1) / g * g;
+    if (seg < min_seg) seg = (min_seg + g - 1) / g * g;
+    per_xcd = (positions + seg - 1) / seg;
+    A.seg_len = seg;
+    score_rows_kernel<EPI><<<dim3((unsigned)(kXcds * per_xcd)), RowsShape::NT, 0, stream>>>(A);
+    return hipGetLastError();
+}
+
 template <Epi EPI>
 hipError_t launch_epi(const ScoreKernelArgs& A, int32_t cus, hipStream_t stream) {
     if (A.a.relu) return launch_form<true, EPI>(A, cus, 64, stream);
-    return launch_form<false, EPI>(A, cus, 64, stream);
+    return launch_rows<EPI>(A, cus, 64, stream);
 }
 
 }  // namespace
 
-hipError_t launch_score_store(const PagedArgs& a, int32_t stride, float* out, int64_t ld, int32_t cus,
-                              hipStream_t stream) {
+hipError_t launch_score_store(const PagedArgs& a, const _Float16* qsum, int32_t stride, float* out, int64_t ld,
+                              int32_t cus, hipStream_t stream) {
     if (a.rows <= 0 || a.max_visible <= 0) return hipSuccess;
     ScoreKernelArgs A = {};
     A.a = a;
+    A.qsum = qsum;
     A.stride = stride;
     A.lmax = (a.max_visible + stride - 1) / stride;
     A.out = out;
@@ -62,18 +92,24 @@ static bool use_group_scorer(const PagedArgs& a) {
     return a.rows / reqs < 32;
 }
 
-hipError_t launch_score_paged(const PagedArgs& a, float* scores, int64_t ld, hipStream_t stream) {
+hipError_t launch_score_paged(const PagedArgs& a, const _Float16* qsum, float* scores, int64_t ld,
+                              hipStream_t stream) {
     if (use_group_scorer(a)) return launch_score_group(a, scores, ld, stream);
+    if (qsum && !a.relu) {
+        const hipError_t e = launch_qsum_prep(a, const_cast<_Float16*>(qsum), stream);
+        if (e != hipSuccess) return e;
+    }
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    return launch_score_store(a, 1, scores, ld, cus, stream);
+    return launch_score_store(a, qsum, 1, scores, ld, cus, stream);
 }
 
-hipError_t launch_score_filter(const PagedArgs& a, const uint64_t* thresh, uint64_t* cand, int32_t* cand_count,
-                               int32_t cand_cap, int32_t cus, hipStream_t stream) {
+hipError_t launch_score_filter(const PagedArgs& a, const _Float16* qsum, const uint64_t* thresh, uint64_t* cand,
+                               int32_t* cand_count, int32_t cand_cap, int32_t cus, hipStream_t stream) {
     if (a.rows <= 0 || a.max_visible <= 0) return hipSuccess;
     ScoreKernelArgs A = {};
     A.a = a;
+    A.qsum = qsum;
     A.stride = 1;
     A.lmax = a.max_visible;
     A.thresh = thresh;
@@ -81,6 +117,41 @@ hipError_t launch_score_filter(const PagedArgs& a, const uint64_t* thresh, uint6
     A.cand_count = cand_count;
     A.cand_cap = cand_cap;
     return launch_epi<Epi::Filter>(A, cus, stream);
+}
+
+// One thread per (tile, wave, slice, lane): the fp32 head sum of the 8 query
+// dims that lane supplies for that slice, as its fp16 hi/lo pair
+// (head_sum_split, the same arithmetic as the scorers' own), stored at steps
+// t = 2*slice and 2*slice + 1 of the fragment order.
+__global__ __launch_bounds__(256) void qsum_prep_kernel(const _Float16* __restrict__ q, int32_t rows,
+                                                        _Float16* __restrict__ qsum, int32_t n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int lane = i & 63, s = (i >> 6) & 7, wave = (i >> 9) & 3, tile = i >> 11;
+    const int row = tile * RowsShape::TILE + wave * RowsShape::RPW + (lane & 31);
+    half8 hi = {}, lo = {};
+    if (row < rows) {
+        const _Float16* qr = q + (int64_t)row * kHeads * kHeadDim + 16 * s + 8 * (lane >> 5);
+        head_sum_split(*reinterpret_cast<const half8*>(qr), *reinterpret_cast<const half8*>(qr + kHeadDim),
+                       *reinterpret_cast<const half8*>(qr + 2 * kHeadDim),
+                       *reinterpret_cast<const half8*>(qr + 3 * kHeadDim), hi, lo);
+    }
+    half8* out = reinterpret_cast<half8*>(qsum) + ((int64_t)tile * RowsShape::WAVES + wave) * 16 * 64 + lane;
+    out[64 * (2 * s)] = hi;
+    out[64 * (2 * s + 1)] = lo;
+}
+
+size_t qsum_bytes(int32_t rows) {
+    const int64_t tiles = (rows + RowsShape::TILE - 1) / RowsShape::TILE;
+    return (size_t)tiles * RowsShape::WAVES * 16 * 64 * sizeof(half8);
+}
+
+hipError_t launch_qsum_prep(const PagedArgs& a, _Float16* qsum, hipStream_t stream) {
+    if (a.rows <= 0) return hipSuccess;
+    const int64_t tiles = (a.rows + RowsShape::TILE - 1) / RowsShape::TILE;
+    const int32_t n = (int32_t)(tiles * RowsShape::WAVES * kSlices * 64);
+    qsum_prep_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, stream>>>(a.q, a.rows, qsum, n);
+    return hipGetLastError();
 }
 
 }  // namespace qsa

@@ -51,17 +51,15 @@
 
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
+#include "score_rows.hpp"
 
 namespace qsa {
 
-enum class Epi { Store, Filter };
-
 constexpr int kLCap = 32;              // per-row LDS staging slots of the Filter epilogue (>= 32)
-constexpr int kXcds = 8;               // XCDs of an MI355X (256 CUs = 8 x 32)
-constexpr int kTrStride = 36;          // floats per row of the relu transpose buffer (32 + 4: conflict-free reads)
 
 struct ScoreKernelArgs {
     PagedArgs a;
+    const _Float16* qsum;  // default form only: prepared head sums, or null
     int32_t stride;    // logical key i is key stride*i
     int32_t lmax;      // logical keys of the longest row: ceil(max_visible / stride)
     int32_t tiles;     // ceil(rows / rows per tile)
@@ -323,33 +321,42 @@ __global__ __launch_bounds__(ScoreShape::NT, Form<RELU>::WG_PER_CU) void score_t
             wlim = __builtin_amdgcn_readfirstlane(wlim);
             __syncthreads();
 
-            // Step: barrier (tile staged) -> issue the loads of the next tile
-            // -> MFMAs -> wait for the next tile and stage it in the other
-            // buffer -> epilogue.  The epilogue's global stores are issued
-            // after the wait, so they drain during the next step's MFMAs.
+            // Step i: barrier (stage i staged) -> issue the loads of stage i+2
+            // -> MFMAs on stage i -> wait for the loads of stage i+1 (issued
+            // one step earlier) and stage them in the other buffer ->
+            // epilogue.  Loads thus have two steps to arrive; the slot of
+            // stage i+3 is read from LDS during step i so that the next
+            // step's loads issue right after its barrier.  Two register sets
+            // alternate (the loop is unrolled by two).
             const _Float16* kc = a.kcache;
-            u32x4 pf[NLOAD];
             using SlotVec = typename std::conditional<NLOAD == 4, u32x4, u32x2>::type;
-            {
-                const SlotVec sl = *reinterpret_cast<const SlotVec*>(&s_slot[pk]);
+            auto slots_of = [&](int stage) {
+                const int li = min(stage * kStepKeys + pk, kMaxPiece - NLOAD);
+                return *reinterpret_cast<const SlotVec*>(&s_slot[li]);
+            };
+            auto issue = [&](const SlotVec& sl, u32x4 (&pf)[NLOAD]) {
 #pragma unroll
                 for (int i = 0; i < NLOAD; ++i)
                     pf[i] = *reinterpret_cast<const u32x4*>(kc + (size_t)sl[i] * kHeadDim + pc * 8);
+            };
+            auto stage_in = [&](int b, const u32x4 (&pf)[NLOAD]) {
 #pragma unroll
                 for (int i = 0; i < NLOAD; ++i)
-                    *reinterpret_cast<u32x4*>(s_keys[0] + lds_key_chunk(F::stage_row(pk + i), pc)) = pf[i];
-            }
-            int buf = 0;
-            for (int j0 = c0; j0 < cend; j0 += kStepKeys) {
+                    *reinterpret_cast<u32x4*>(s_keys[b] + lds_key_chunk(F::stage_row(pk + i), pc)) = pf[i];
+            };
+            u32x4 pfA[NLOAD], pfB[NLOAD];
+            issue(slots_of(0), pfA);
+            stage_in(0, pfA);
+            issue(slots_of(1), pfA);
+            SlotVec sl_next = slots_of(2);
+            const int nsteps = (cend - c0 + kStepKeys - 1) / kStepKeys;
+            auto step = [&](int si, const u32x4 (&pf_wait)[NLOAD], u32x4 (&pf_issue)[NLOAD]) {
+                const int j0 = c0 + si * kStepKeys;
+                const int buf = si & 1;
                 __syncthreads();
                 const unsigned char* sk = s_keys[buf];
-                {
-                    const int li = min(j0 + kStepKeys - c0 + pk, kMaxPiece - NLOAD);
-                    const SlotVec sl = *reinterpret_cast<const SlotVec*>(&s_slot[li]);
-#pragma unroll
-                    for (int i = 0; i < NLOAD; ++i)
-                        pf[i] = *reinterpret_cast<const u32x4*>(kc + (size_t)sl[i] * kHeadDim + pc * 8);
-                }
+                issue(sl_next, pf_issue);
+                sl_next = slots_of(si + 3);
                 // keep the prefetch issued here, ahead of the MFMAs that hide it
                 __builtin_amdgcn_sched_barrier(0);
 
@@ -383,9 +390,7 @@ __global__ __launch_bounds__(ScoreShape::NT, Form<RELU>::WG_PER_CU) void score_t
                     // stage the prefetched tile in the idle buffer (after the
                     // last step this fills a buffer no wave reads any more:
                     // every wave has passed this step's barrier)
-#pragma unroll
-                    for (int i = 0; i < NLOAD; ++i)
-                        *reinterpret_cast<u32x4*>(s_keys[buf ^ 1] + lds_key_chunk(F::stage_row(pk + i), pc)) = pf[i];
+                    stage_in(buf ^ 1, pf_wait);
 
                     float* const tw = s_tr[wave];
                     const int rr = lane >> 2, cq = lane & 3;
@@ -433,26 +438,27 @@ __global__ __launch_bounds__(ScoreShape::NT, Form<RELU>::WG_PER_CU) void score_t
                         }
                     }
                 } else {
+                    // every key fragment of the stage is read before the chain starts
+                    half8 kbs[kSub][kSlices];
+#pragma unroll
+                    for (int st = 0; st < kSub; ++st)
+#pragma unroll
+                        for (int s = 0; s < kSlices; ++s)
+                            kbs[st][s] = *reinterpret_cast<const half8*>(
+                                sk + lds_key_chunk(32 * st + (lane & 31), 2 * s + (lane >> 5)));
+                    __builtin_amdgcn_sched_barrier(0);
                     float16v acc[kSub];
 #pragma unroll
                     for (int st = 0; st < kSub; ++st) acc[st] = float16v{};
 #pragma unroll
-                    for (int s = 0; s < kSlices; ++s) {
-                        half8 kbs[kSub];
-#pragma unroll
-                        for (int st = 0; st < kSub; ++st)
-                            kbs[st] = *reinterpret_cast<const half8*>(
-                                sk + lds_key_chunk(32 * st + (lane & 31), 2 * s + (lane >> 5)));
+                    for (int s = 0; s < kSlices; ++s)
 #pragma unroll
                         for (int t = 2 * s; t < 2 * s + 2; ++t)
 #pragma unroll
-                            for (int st = 0; st < kSub; ++st) acc[st] = mfma32(kbs[st], qa[t], acc[st]);
-                    }
+                            for (int st = 0; st < kSub; ++st) acc[st] = mfma32(kbs[st][s], qa[t], acc[st]);
                     __builtin_amdgcn_sched_barrier(0);
                     // stage the prefetched tile in the idle buffer (see above)
-#pragma unroll
-                    for (int i = 0; i < NLOAD; ++i)
-                        *reinterpret_cast<u32x4*>(s_keys[buf ^ 1] + lds_key_chunk(F::stage_row(pk + i), pc)) = pf[i];
+                    stage_in(buf ^ 1, pf_wait);
 
 #pragma unroll
                     for (int st = 0; st < kSub; ++st) {
@@ -530,7 +536,10 @@ __global__ __launch_bounds__(ScoreShape::NT, Form<RELU>::WG_PER_CU) void score_t
                         }
                     }
                 }
-                buf ^= 1;
+            };
+            for (int si = 0; si < nsteps; si += 2) {
+                step(si, pfA, pfB);
+                if (si + 1 < nsteps) step(si + 1, pfB, pfA);
             }
             // every wave is done with this pass's s_lim before wave 0 rewrites it
             __syncthreads();

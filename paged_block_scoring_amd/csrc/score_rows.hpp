@@ -1,0 +1,428 @@
+// score_rows.hpp -- the tiled paged scorer of the default score form (the
+// plain head sum), used by the sampling and filtering passes of the fused arm
+// and by the materialising scorer.
+//
+// Sources: "[Perf][Qwen4Exp] Admit the cuBLAS QSA indexer and exact top-k on
+// Turing", sections "Purpose" (FP16 product with FP32 accumulation and an
+// epilogue; a paged scorer reading keys through the page table) and "Test
+// Plan" (4 index heads, head dim 128, compress ratio 4); "spec(MODEL-MM-QWEN4-
+// EXP) ...", section "The component deep-dives, and two corrections to the
+// above" (one key per ratio tokens shared by all heads; one score per query
+// token summed over heads).
+//
+// Work.  Rows are cut into tiles of 128 consecutive rows (4 waves of 32); the
+// logical keys (logical key i is key stride*i of the request; stride is 1
+// except for the sampling pass) are cut into 8 stripes, one per XCD.
+// Workgroup w runs on XCD w % 8 (the hardware's round-robin dispatch) and
+// owns a contiguous, equal share of that XCD's (tile, key) positions, so every
+// XCD streams only its stripe of keys (which stays in its L2) and every
+// workgroup does the same amount of work.  A share is processed as pieces of
+// one tile and at most kRowsPiece keys; rows of different requests in one
+// tile are processed in successive passes over the piece.
+//
+// A piece.  Each wave holds the head-sum query fragments (hi and lo halves,
+// qsa_device.hpp) of its 32 rows in registers: read from the prepared head
+// sums when the caller has them (coalesced), else formed from q.  A per-piece table in LDS
+// gives every logical key's slot in the cache.  Keys go through LDS 32 at a
+// time (8 KB, double-buffered, XOR-swizzled).  Step i: barrier -> issue the
+// global loads of stage i+2 into registers -> read the 8 key fragments of
+// stage i -> 16 MFMAs (keys as MFMA rows, the wave's rows as columns) ->
+// wait for the loads of stage i+1 (issued one step earlier) and write them to
+// the idle buffer -> epilogue.  Two register sets alternate, so a load has two
+// steps to arrive; the slot of stage i+3 is read during step i.  The LDS row
+// of key n of a stage is sigma^-1(n) (see Form), which makes lane l's
+// accumulator element v the score of row l%32 and key 16*(l/32) + v.
+//
+// Epilogues.
+//   Store  -- out[row*ld + i] = score: the wave transposes its 32 x 32 tile
+//             through LDS so that 8 consecutive lanes store 32 consecutive
+//             keys (128 bytes) of one row with 16-byte stores;
+//   Filter -- keep (key, score) if score >= the row's threshold score.  Each
+//             lane keeps its own list in LDS (kLaneCap entries).  A step
+//             compares the lane's 16 scores (the ballot of each compare is the
+//             exec mask of that score's append) and counts them; a lane whose
+//             list would overflow makes the wave move every lane's list to the
+//             rows' global candidate lists (one atomic per lane), as does
+//             leaving a tile.  The appends themselves run without branches:
+//             exec is set to the score's ballot around one LDS store.
+#pragma once
+
+#include "qsa_device.hpp"
+#include "qsa_internal.hpp"
+
+namespace qsa {
+
+enum class Epi { Store, Filter };
+
+constexpr int kXcds = 8;         // XCDs of an MI355X (256 CUs = 8 x 32)
+constexpr int kTrStride = 36;    // floats per row of a transpose buffer (32 + 4: conflict-free reads)
+constexpr int kRowsPiece = 2048; // logical keys per piece (slot-table entries)
+constexpr int kLaneCap = 24;     // entries of a lane's LDS candidate list (>= 16)
+
+struct RowsArgs {
+    PagedArgs a;
+    const _Float16* qsum;  // head sums in fragment order (qsa_internal.hpp), or null
+    int32_t stride;    // logical key i is key stride*i
+    int32_t lmax;      // logical keys of the longest row: ceil(max_visible / stride)
+    int32_t tiles;     // ceil(rows / 128)
+    int32_t xcd_keys;  // logical keys per XCD stripe (a multiple of 32)
+    int64_t seg_len;   // (tile, key) positions per workgroup (a multiple of 32)
+    // Store
+    float* out;
+    int64_t ld;
+    int32_t vec_store;  // out and ld allow 16-byte stores
+    // Filter
+    const uint64_t* thresh;  // [rows] threshold composite; only its score is used
+    uint64_t* cand;          // [rows][cand_cap] entries (score bits << 32 | key)
+    int32_t* cand_count;     // [rows]
+    int32_t cand_cap;
+};
+
+struct RowsShape {
+    static constexpr int WAVES = 4;
+    static constexpr int NT = 64 * WAVES;
+    static constexpr int RPW = 32;               // rows per wave
+    static constexpr int TILE = WAVES * RPW;     // rows per tile
+    static constexpr int STEP = 32;              // keys per stage
+    static constexpr int NLOAD = STEP * kChunksPerKey / NT;  // 16-byte pieces per thread per stage
+    static_assert(NLOAD == 2, "two consecutive keys per thread");
+    // LDS row of key n of a stage: sigma^-1, sigma(m) = 16*((m/4)%2) + 4*(m/8) + m%4
+    __device__ static int stage_row(int n) {
+        const int k = n & 31;
+        return (n & ~31) | (8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3));
+    }
+};
+
+// n += the number of masks among m0..m7 that hold this lane (one add with
+// carry-in per mask).  The masks come from VALU compares, and a VALU-written
+// SGPR read as a carry needs two wait states: the block starts with them.
+__device__ __forceinline__ void count_masks8(const uint64_t (&m)[16], int o, int& n) {
+    uint64_t junk;
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_addc_co_u32_e64 %[n], %[j], %[n], 0, %[m0]\n\t"
+        "v_addc_co_u32_e64 %[n], %[j], %[n], 0, %[m1]\n\t"
+        "v_addc_co_u32_e64 %[n], %[j], %[n], 0, %[m2]\n\t"
+        "v_addc_co_u32_e64 %[n], %[j], %[n], 0, %[m3]\n\t"
+        "v_addc_co_u32_e64 %[n], %[j], %[n], 0, %[m4]\n\t"
+        "v_addc_co_u32_e64 %[n], %[j], %[n], 0, %[m5]\n\t"
+        "v_addc_co_u32_e64 %[n], %[j], %[n], 0, %[m6]\n\t"
+        "v_addc_co_u32_e64 %[n], %[j], %[n], 0, %[m7]"
+        : [n] "+v"(n), [j] "=&s"(junk)
+        : [m0] "s"(m[o]), [m1] "s"(m[o + 1]), [m2] "s"(m[o + 2]), [m3] "s"(m[o + 3]), [m4] "s"(m[o + 4]),
+          [m5] "s"(m[o + 5]), [m6] "s"(m[o + 6]), [m7] "s"(m[o + 7]));
+}
+
+// Appends (key kb+v, score sv) for v = o..o+7 at LDS byte address addr
+// (advanced by 8 per entry) in the lanes of mask m[v]: exec is set to m[v]
+// around each entry's store, so lanes outside it neither store nor advance,
+// without a branch.  The caller runs with a full exec, which is restored.
+__device__ __forceinline__ void append_masks8(const uint64_t (&m)[16], const float16v& sc, int o, int kb,
+                                              uint32_t& addr) {
+    int tk;
+#define QSA_APPEND_ONE(V)                                      \
+    "s_mov_b64 exec, %[m" #V "]\n\t"                           \
+    "v_add_u32 %[tk], " #V ", %[kb]\n\t"                       \
+    "ds_write2_b32 %[ad], %[tk], %[s" #V "] offset1:1\n\t"     \
+    "v_add_u32 %[ad], 8, %[ad]\n\t"
+    asm volatile(
+        QSA_APPEND_ONE(0) QSA_APPEND_ONE(1) QSA_APPEND_ONE(2) QSA_APPEND_ONE(3)
+        QSA_APPEND_ONE(4) QSA_APPEND_ONE(5) QSA_APPEND_ONE(6) QSA_APPEND_ONE(7)
+        "s_mov_b64 exec, -1"
+        : [ad] "+v"(addr), [tk] "=&v"(tk)
+        : [kb] "v"(kb + o), [m0] "s"(m[o]), [m1] "s"(m[o + 1]), [m2] "s"(m[o + 2]), [m3] "s"(m[o + 3]),
+          [m4] "s"(m[o + 4]), [m5] "s"(m[o + 5]), [m6] "s"(m[o + 6]), [m7] "s"(m[o + 7]), [s0] "v"(sc[o]),
+          [s1] "v"(sc[o + 1]), [s2] "v"(sc[o + 2]), [s3] "v"(sc[o + 3]), [s4] "v"(sc[o + 4]),
+          [s5] "v"(sc[o + 5]), [s6] "v"(sc[o + 6]), [s7] "v"(sc[o + 7])
+        : "memory");
+#undef QSA_APPEND_ONE
+}
+
+template <Epi EPI>
+__global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A) {
+    using S = RowsShape;
+    constexpr int NT = S::NT, TILE = S::TILE, RPW = S::RPW, STEP = S::STEP, NLOAD = S::NLOAD;
+    constexpr bool FILTER = EPI == Epi::Filter;
+
+    __shared__ __attribute__((aligned(16))) unsigned char s_keys[2][STEP * kKeyBytes];
+    __shared__ __attribute__((aligned(16))) uint32_t s_slot[kRowsPiece];
+    __shared__ __attribute__((aligned(16))) float s_tr[FILTER ? 1 : S::WAVES][FILTER ? 4 : RPW * kTrStride];
+    __shared__ __attribute__((aligned(16))) uint2 s_list[FILTER ? NT * kLaneCap : 1];
+    __shared__ int32_t s_req[TILE], s_lv[TILE], s_todo[TILE], s_lim[TILE];
+    __shared__ float s_fT[FILTER ? TILE : 1];
+    __shared__ int32_t s_act, s_vmax;
+
+    const PagedArgs& a = A.a;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int xcd = blockIdx.x % kXcds, loc = blockIdx.x / kXcds;
+    const int xk0 = xcd * A.xcd_keys;
+    // keys of this XCD's stripe, padded to whole stages so that every piece
+    // starts on a stage boundary (keys past the end are invisible to every row)
+    const int span = min(A.xcd_keys, (A.lmax - xk0 + STEP - 1) / STEP * STEP);
+    if (span <= 0) return;
+    const int64_t total = (int64_t)A.tiles * span;
+    int64_t p = (int64_t)loc * A.seg_len;
+    const int64_t pend = min(p + A.seg_len, total);
+
+    // staging: this thread's NLOAD consecutive keys of a stage and its chunk
+    const int pk = NLOAD * (tid >> 4), pc = tid & 15;
+    // epilogue: the tile row of this lane
+    const int erow = wave * RPW + (lane & 31);
+
+    // every slot-table entry always holds a valid cache slot, so the prefetch
+    // may read entries past the end of a pass's table
+    for (int i = tid; i < kRowsPiece; i += NT) s_slot[i] = 0u;
+
+    half8 qa[2 * kSlices];
+    float fT = 0.0f;  // threshold score of this lane's row (Filter)
+    int cnt = 0;      // entries in this lane's list (Filter)
+    const uint32_t list0 =
+        (uint32_t)reinterpret_cast<uintptr_t>(static_cast<void*>(&s_list[0])) + (uint32_t)(tid * kLaneCap * 8);
+    int tile_r0 = -1;  // first row of the tile held in registers
+
+    // moves every lane's list to its row's global candidate list (one atomic
+    // per lane; the list is read from LDS 16 bytes at a time)
+    auto flush = [&](int row) {
+        int base = 0;
+        if (cnt > 0) base = atomicAdd(&A.cand_count[row], cnt);
+        const int lim = min(cnt, A.cand_cap - base);
+        uint64_t* dst = A.cand + (int64_t)row * A.cand_cap + base;
+        const u32x4* src = reinterpret_cast<const u32x4*>(&s_list[tid * kLaneCap]);
+        u32x4 e[kLaneCap / 2];
+#pragma unroll
+        for (int i = 0; i < kLaneCap / 2; ++i) e[i] = src[i];
+#pragma unroll
+        for (int i = 0; i < kLaneCap / 2; ++i) {
+            if (2 * i < lim) dst[2 * i] = ((uint64_t)e[i][1] << 32) | e[i][0];
+            if (2 * i + 1 < lim) dst[2 * i + 1] = ((uint64_t)e[i][3] << 32) | e[i][2];
+        }
+        cnt = 0;
+    };
+    // the single-request case builds a piece's slot table while its rows load
+    const bool one_req = a.num_reqs == 1;
+    auto build_slots = [&](int act, int k0, int k1) {
+        const int32_t* ptrow = a.page_table + (int64_t)act * a.pt_stride;
+        for (int i = tid; i < k1 - k0; i += NT) {
+            const int j = (k0 + i) * A.stride;
+            const int lp = j / a.kpp;
+            const int slot = j - lp * a.kpp;
+            const int pg = min(max(ptrow[lp], 0), a.num_pages - 1);
+            s_slot[i] = (uint32_t)pg * (uint32_t)a.kpp + (uint32_t)slot;
+        }
+    };
+
+    while (p < pend) {
+        const int tile = (int)(p / span);
+        const int off = (int)(p - (int64_t)tile * span);
+        const int len = (int)min<int64_t>(min<int64_t>((int64_t)(span - off), pend - p), (int64_t)kRowsPiece);
+        const int c0 = xk0 + off, c1 = c0 + len;
+        p += len;
+        const int r0 = tile * TILE;
+        const bool new_tile = r0 != tile_r0;
+        if (FILTER && new_tile && tile_r0 >= 0) flush(tile_r0 + erow);
+
+        // the tile's rows (threads < 128): loads first, so that the query and
+        // page-table loads below overlap them
+        int req = -1, ps = 0;
+        uint64_t th = 0ull;
+        const int rr = r0 + tid;
+        if (tid < TILE) {
+            const int rc = rr < a.rows ? rr : a.rows - 1;
+            req = a.row_req ? a.row_req[rc] : 0;
+            ps = a.pos[rc];
+            if (FILTER && new_tile) th = A.thresh[rc];
+        }
+        if (new_tile && A.qsum) {
+            // prepared head sums: 16 coalesced 16-byte loads per lane
+            const half8* qs = reinterpret_cast<const half8*>(A.qsum) + ((int64_t)tile * S::WAVES + wave) * 16 * 64 + lane;
+#pragma unroll
+            for (int t = 0; t < 2 * kSlices; ++t) qa[t] = qs[64 * t];
+        } else if (new_tile) {
+            // B operand: column m = row m; step t of the chain = (slice t/2, hi/lo t%2)
+            const int row = r0 + wave * RPW + (lane & 31);
+            const int rowc = row < a.rows ? row : a.rows - 1;
+#pragma unroll
+            for (int s = 0; s < kSlices; ++s) {
+                half8 h[kHeads];
+#pragma unroll
+                for (int hh = 0; hh < kHeads; ++hh) {
+                    const half8 v = *reinterpret_cast<const half8*>(a.q + ((int64_t)rowc * kHeads + hh) * kHeadDim +
+                                                                    16 * s + 8 * (lane >> 5));
+                    h[hh] = row < a.rows ? v : half8{};
+                }
+                head_sum_split(h[0], h[1], h[2], h[3], qa[2 * s], qa[2 * s + 1]);
+            }
+        }
+        if (one_req) build_slots(0, c0, c1);
+        if (tid < TILE) {
+            int lv = 0;
+            if (rr >= a.rows || req < 0 || req >= a.num_reqs) {
+                req = -1;
+            } else {
+                const int v = visible_keys(ps, a.cr, a.max_visible);
+                lv = (v + A.stride - 1) / A.stride;
+            }
+            s_req[tid] = req;
+            s_lv[tid] = lv;
+            s_todo[tid] = (req >= 0 && lv > c0) ? 1 : 0;
+            // the threshold composite's score (an all-ones composite decodes
+            // to NaN, which no score reaches)
+            if (FILTER && new_tile) s_fT[tid] = req >= 0 ? key_to_float((uint32_t)(th >> 32)) : 0.0f;
+        }
+        __syncthreads();
+        if (FILTER && new_tile) fT = s_fT[erow];
+        tile_r0 = r0;
+
+        for (;;) {
+            // one pass per request present among the tile's pending rows
+            // (smallest request id first): wave 0 elects it and marks the rows
+            if (wave == 0) {
+                int best = 0x7FFFFFFF;
+                for (int t = lane; t < TILE; t += 64)
+                    if (s_todo[t]) best = min(best, s_req[t]);
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o, 64));
+                int vmax = 0;
+                for (int t = lane; t < TILE; t += 64) {
+                    const bool on = s_todo[t] && s_req[t] == best;
+                    s_lim[t] = on ? min(s_lv[t], c1) : 0;
+                    if (on) {
+                        s_todo[t] = 0;
+                        vmax = max(vmax, s_lv[t]);
+                    }
+                }
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) vmax = max(vmax, __shfl_xor(vmax, o, 64));
+                if (lane == 0) {
+                    s_act = best == 0x7FFFFFFF ? -1 : best;
+                    s_vmax = vmax;
+                }
+            }
+            __syncthreads();
+            const int act = s_act;
+            if (act < 0) break;
+            const int cend = min(c1, s_vmax);
+
+            if (!one_req) build_slots(act, c0, cend);
+            // this lane's row bound, and the smallest over the wave's rows:
+            // column tiles entirely below it need no per-row mask
+            const int lim_r = s_lim[erow];
+            int wlim = lim_r;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) wlim = min(wlim, __shfl_xor(wlim, o, 64));
+            wlim = __builtin_amdgcn_readfirstlane(wlim);
+            __syncthreads();
+
+            const _Float16* kc = a.kcache;
+            auto slots_of = [&](int stage) {
+                const int li = min(stage * STEP + pk, kRowsPiece - NLOAD);
+                return *reinterpret_cast<const u32x2*>(&s_slot[li]);
+            };
+            auto issue = [&](const u32x2& sl, u32x4 (&pf)[NLOAD]) {
+#pragma unroll
+                for (int i = 0; i < NLOAD; ++i)
+                    pf[i] = *reinterpret_cast<const u32x4*>(kc + (size_t)sl[i] * kHeadDim + pc * 8);
+            };
+            auto stage_in = [&](int b, const u32x4 (&pf)[NLOAD]) {
+#pragma unroll
+                for (int i = 0; i < NLOAD; ++i)
+                    *reinterpret_cast<u32x4*>(s_keys[b] + lds_key_chunk(S::stage_row(pk + i), pc)) = pf[i];
+            };
+            // stages 0 and 1 load together; stage 0 goes to LDS, stage 1 is
+            // the first step's pending set
+            u32x4 pfA[NLOAD], pfB[NLOAD];
+            issue(slots_of(0), pfB);
+            issue(slots_of(1), pfA);
+            stage_in(0, pfB);
+            u32x2 sl_next = slots_of(2);
+            const int nsteps = (cend - c0 + STEP - 1) / STEP;
+
+            auto step = [&](int si, const u32x4 (&pf_wait)[NLOAD], u32x4 (&pf_issue)[NLOAD]) {
+                const int j0 = c0 + si * STEP;
+                const int buf = si & 1;
+                __syncthreads();
+                const unsigned char* sk = s_keys[buf];
+                issue(sl_next, pf_issue);
+                sl_next = slots_of(si + 3);
+                // keep the prefetch issued here, ahead of the MFMAs that hide it
+                __builtin_amdgcn_sched_barrier(0);
+                half8 kf[kSlices];
+#pragma unroll
+                for (int s = 0; s < kSlices; ++s)
+                    kf[s] = *reinterpret_cast<const half8*>(sk + lds_key_chunk(lane & 31, 2 * s + (lane >> 5)));
+                __builtin_amdgcn_sched_barrier(0);
+                float16v acc = {};
+#pragma unroll
+                for (int s = 0; s < kSlices; ++s) {
+                    acc = mfma32(kf[s], qa[2 * s], acc);
+                    acc = mfma32(kf[s], qa[2 * s + 1], acc);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // stage i+1 into the idle buffer (after the last step this fills a
+                // buffer no wave reads any more: every wave has passed this step's barrier)
+                stage_in(buf ^ 1, pf_wait);
+
+                // element v: key kb + v of row erow
+                const int kb = j0 + 16 * (lane >> 5);
+                const bool full = j0 + STEP <= wlim;
+                if (!FILTER) {
+                    // transpose so that lane l holds keys 4*(l%8) .. +3 of rows l/8 + 8i
+                    float* const tw = s_tr[wave];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        *reinterpret_cast<float4v*>(tw + (lane & 31) * kTrStride + 16 * (lane >> 5) + 4 * j) =
+                            float4v{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+                    __builtin_amdgcn_wave_barrier();
+                    float4v w[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        w[i] = *reinterpret_cast<const float4v*>(tw + ((lane >> 3) + 8 * i) * kTrStride + 4 * (lane & 7));
+                    __builtin_amdgcn_wave_barrier();
+                    const int key0 = j0 + 4 * (lane & 7);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int trow = wave * RPW + (lane >> 3) + 8 * i;
+                        float* dst = A.out + (int64_t)(r0 + trow) * A.ld + key0;
+                        if (full && A.vec_store) {
+                            *reinterpret_cast<float4v*>(dst) = w[i];
+                        } else {
+                            const int lim = s_lim[trow];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (full || key0 + e < lim) dst[e] = w[i][e];
+                        }
+                    }
+                } else {
+                    // a column tile that crosses a row bound: scores past it cannot pass
+                    if (!full) {
+                        const int nv = min(max(lim_r - kb, 0), 16);
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            if (v >= nv) acc[v] = -__builtin_huge_valf();
+                    }
+                    uint64_t m[16];
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) m[v] = __builtin_amdgcn_ballot_w64(acc[v] >= fT);
+                    int n = 0;
+                    count_masks8(m, 0, n);
+                    count_masks8(m, 8, n);
+                    if (__any(cnt + n > kLaneCap)) flush(r0 + erow);
+                    uint32_t ad = list0 + (uint32_t)(cnt * 8);
+                    append_masks8(m, acc, 0, kb, ad);
+                    append_masks8(m, acc, 8, kb, ad);
+                    cnt += n;
+                }
+            };
+            for (int si = 0; si < nsteps; si += 2) {
+                step(si, pfA, pfB);
+                if (si + 1 < nsteps) step(si + 1, pfB, pfA);
+            }
+            // every wave is done with this pass's s_lim before wave 0 rewrites it
+            __syncthreads();
+        }
+        __syncthreads();
+    }
+    if (FILTER && tile_r0 >= 0) flush(tile_r0 + erow);
+}
+
+}  // namespace qsa

@@ -68,15 +68,17 @@ def parse():
 
 # kernel name in the bench -> (substrings of the demangled symbol, source files)
 KERNEL_SOURCES = {
-    "filter_scorer": (("score_tiles_kernel", "(qsa::Epi)1"),
-                      ["paged_block_scoring_amd/csrc/score_core.hpp", "paged_block_scoring_amd/csrc/score.hip",
+    "qsum_prep": (("qsum_prep_kernel",), ["paged_block_scoring_amd/csrc/score.hip"]),
+    "filter_scorer": (("score_rows_kernel", "(qsa::Epi)1"),
+                      ["paged_block_scoring_amd/csrc/score_rows.hpp", "paged_block_scoring_amd/csrc/score.hip",
                        "paged_block_scoring_amd/csrc/qsa_device.hpp"]),
-    "sample_scorer": (("score_tiles_kernel", "(qsa::Epi)0"),
-                      ["paged_block_scoring_amd/csrc/score_core.hpp", "paged_block_scoring_amd/csrc/score.hip",
+    "sample_scorer": (("score_rows_kernel", "(qsa::Epi)0"),
+                      ["paged_block_scoring_amd/csrc/score_rows.hpp", "paged_block_scoring_amd/csrc/score.hip",
                        "paged_block_scoring_amd/csrc/qsa_device.hpp"]),
-    "scorer": (("score_tiles_kernel", "(qsa::Epi)0"),
-               ["paged_block_scoring_amd/csrc/score_core.hpp", "paged_block_scoring_amd/csrc/score.hip",
-                "paged_block_scoring_amd/csrc/qsa_device.hpp"]),
+    # the two-pass arm's scorer: row-tiled for prefill chunks, windowed for decode
+    "scorer": (("score_",),
+               ["paged_block_scoring_amd/csrc/score_rows.hpp", "paged_block_scoring_amd/csrc/score_group.hip",
+                "paged_block_scoring_amd/csrc/score.hip", "paged_block_scoring_amd/csrc/qsa_device.hpp"]),
     "sample_threshold": (("sample_threshold_kernel",),
                          ["paged_block_scoring_amd/csrc/fused.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
     "final_select": (("fused_final_kernel",),
@@ -267,6 +269,10 @@ def main():
         sampled = int(((vis + stride - 1) // stride).sum())
         units["filter_scorer"] = ("mfma", flops_full, PEAK_MFMA_F16_TFLOPS, "TFLOP/s")
         units["sample_scorer"] = ("mfma", FLOPS_PER_ROW_KEY * sampled, PEAK_MFMA_F16_TFLOPS, "TFLOP/s")
+    elif rows < 32 * w.num_reqs:
+        # few rows per request: every key streams from HBM for one row (256 B per key)
+        units["scorer"] = ("hbm", 256 * sum_v + 1024 * rows, PEAK_HBM_GBS, "GB/s")
+        units["topk_rows"] = ("hbm", 4 * sum_v + 4 * rows * k, PEAK_HBM_GBS, "GB/s")
     else:
         units["scorer"] = ("mfma", flops_full, PEAK_MFMA_F16_TFLOPS, "TFLOP/s")
         units["topk_rows"] = ("hbm", 4 * sum_v + 4 * rows * k, PEAK_HBM_GBS, "GB/s")

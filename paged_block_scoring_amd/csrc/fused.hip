@@ -71,15 +71,15 @@ __global__ __launch_bounds__(kThrNT) void sample_threshold_kernel(const float* _
         const float* srow = samp + (int64_t)row * ld_s;
         float x[EPT];
         float lo = __builtin_huge_valf(), hi = -__builtin_huge_valf();
+        // every load is issued before any is used: indices past the row's
+        // samples are clamped into its stride (ld_s >= ns) and masked after
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) x[e] = srow[min(e * kThrNT + (int)threadIdx.x, (int)ld_s - 1)];
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            const int i = e * kThrNT + (int)threadIdx.x;
-            x[e] = 0.0f;
-            if (e * kThrNT < ns && i < ns) {
-                x[e] = srow[i];
-                lo = fminf(lo, x[e]);
-                hi = fmaxf(hi, x[e]);
-            }
+            const bool in = e * kThrNT + (int)threadIdx.x < ns;
+            lo = in ? fminf(lo, x[e]) : lo;
+            hi = in ? fmaxf(hi, x[e]) : hi;
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
@@ -293,15 +293,28 @@ __global__ __launch_bounds__(kFinNT) void fused_final_kernel(FinalArgs A) {
         if (nsel > 0) {
             const uint64_t* c = A.cand + (int64_t)row * A.cand_cap;
             uint32_t k[EPT], idx[EPT];
+            // loads in groups of 4 slots, each group issued before any use
+            // (indices past n are clamped into the row's list and masked)
+            static_assert(EPT % 4 == 0, "slot groups of 4");
 #pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                const int i = e * kFinNT + (int)threadIdx.x;
-                k[e] = 0u;
-                idx[e] = 0u;
-                if (e * kFinNT < n && i < n) {
-                    const uint64_t en = c[i];  // (score bits, key)
-                    k[e] = order_key(__uint_as_float((uint32_t)(en >> 32)));
-                    idx[e] = (uint32_t)en;
+            for (int g = 0; g < EPT; g += 4) {
+#pragma unroll
+                for (int e = g; e < g + 4; ++e) {
+                    k[e] = 0u;
+                    idx[e] = 0u;
+                }
+                if (g * kFinNT < n) {
+                    uint64_t en[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        en[e] = c[min((g + e) * kFinNT + (int)threadIdx.x, A.cand_cap - 1)];  // (score bits, key)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if ((g + e) * kFinNT + (int)threadIdx.x < n) {
+                            k[g + e] = order_key(__uint_as_float((uint32_t)(en[e] >> 32)));
+                            idx[g + e] = (uint32_t)en[e];
+                        }
+                    }
                 }
             }
             // one histogram level over the order keys: the bin b holding the

@@ -46,6 +46,9 @@ hipError_t launch_rows(const ScoreKernelArgs& K, int32_t cus, int64_t min_seg, h
     A.cand_count = K.cand_count;
     A.cand_cap = K.cand_cap;
     A.tiles = (A.a.rows + RowsShape::TILE - 1) / RowsShape::TILE;
+    A.kpp_shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if ((1 << sh) == A.a.kpp) A.kpp_shift = sh;
     const int64_t stripe = ((int64_t)(A.lmax + kXcds - 1) / kXcds + g - 1) / g * g;
     A.xcd_keys = (int32_t)stripe;
     const int64_t positions = (int64_t)A.tiles * stripe;

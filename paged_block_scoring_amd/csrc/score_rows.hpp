@@ -44,7 +44,8 @@
 //             list would overflow makes the wave move every lane's list to the
 //             rows' global candidate lists (one atomic per lane), as does
 //             leaving a tile.  The appends themselves run without branches:
-//             exec is set to the score's ballot around one LDS store.
+//             exec is set to the score's ballot around one LDS store; they
+//             are issued in the gaps of the next stage's MFMA chain.
 #pragma once
 
 #include "qsa_device.hpp"
@@ -66,6 +67,7 @@ struct RowsArgs {
     int32_t lmax;      // logical keys of the longest row: ceil(max_visible / stride)
     int32_t tiles;     // ceil(rows / 128)
     int32_t xcd_keys;  // logical keys per XCD stripe (a multiple of 32)
+    int32_t kpp_shift; // log2(keys per page) when that is a power of two, else -1
     int64_t seg_len;   // (tile, key) positions per workgroup (a multiple of 32)
     // Store
     float* out;
@@ -138,6 +140,66 @@ __device__ __forceinline__ void append_masks8(const uint64_t (&m)[16], const flo
 #undef QSA_APPEND_ONE
 }
 
+// A quarter (4 MFMAs, chain steps t = 4b..4b+3) of a 32-key stage's MFMA
+// chain, with 4 of the previous stage's appends (scores v = 4b..4b+3) placed
+// in the gaps the dependent chain leaves: after each MFMA the append's exec
+// is set to its ballot, the key formed, the entry stored, the address
+// advanced and exec restored.  Quarter 0 starts the chain from zero; quarter
+// 3 ends with the wait states an MFMA result needs before a VALU may read it
+// and also names every key fragment of the stage as an input, so that no
+// fragment register is reused (written) while an MFMA of the chain may still
+// read it.  Nothing else in a block touches the chain's accumulators.
+template <int B>
+__device__ __forceinline__ void mfma_quarter_appends(float16v& acc, const half8 (&kf)[8], const half8& k0,
+                                                     const half8& k1, const half8 (&qa)[16],
+                                                     const uint64_t (&m)[16], const float16v& ps, int pkb,
+                                                     uint32_t& pad) {
+    int tk;
+#define QSA_APP(V)                                          \
+    "s_mov_b64 exec, %[m" #V "]\n\t"                        \
+    "v_add_u32 %[tk], " #V ", %[kb]\n\t"                    \
+    "ds_write2_b32 %[ad], %[tk], %[s" #V "] offset1:1\n\t"  \
+    "v_add_u32 %[ad], 8, %[ad]\n\t"                         \
+    "s_mov_b64 exec, -1\n\t"
+#define QSA_OPS                                                                                      \
+    [k0] "v"(k0), [k1] "v"(k1), [q0] "v"(qa[4 * B]), [q1] "v"(qa[4 * B + 1]), [q2] "v"(qa[4 * B + 2]),  \
+        [q3] "v"(qa[4 * B + 3]), [m0] "s"(m[4 * B]), [m1] "s"(m[4 * B + 1]), [m2] "s"(m[4 * B + 2]),     \
+        [m3] "s"(m[4 * B + 3]), [s0] "v"(ps[4 * B]), [s1] "v"(ps[4 * B + 1]), [s2] "v"(ps[4 * B + 2]),   \
+        [s3] "v"(ps[4 * B + 3]), [kb] "v"(pkb + 4 * B)
+    if (B == 0) {
+        asm volatile(
+            "v_mfma_f32_32x32x16_f16 %[acc], %[k0], %[q0], 0\n\t" QSA_APP(0)
+            "v_mfma_f32_32x32x16_f16 %[acc], %[k0], %[q1], %[acc]\n\t" QSA_APP(1)
+            "v_mfma_f32_32x32x16_f16 %[acc], %[k1], %[q2], %[acc]\n\t" QSA_APP(2)
+            "v_mfma_f32_32x32x16_f16 %[acc], %[k1], %[q3], %[acc]\n\t" QSA_APP(3)
+            : [acc] "=&v"(acc), [ad] "+v"(pad), [tk] "=&v"(tk)
+            : QSA_OPS
+            : "memory");
+    } else if (B < 3) {
+        asm volatile(
+            "v_mfma_f32_32x32x16_f16 %[acc], %[k0], %[q0], %[acc]\n\t" QSA_APP(0)
+            "v_mfma_f32_32x32x16_f16 %[acc], %[k0], %[q1], %[acc]\n\t" QSA_APP(1)
+            "v_mfma_f32_32x32x16_f16 %[acc], %[k1], %[q2], %[acc]\n\t" QSA_APP(2)
+            "v_mfma_f32_32x32x16_f16 %[acc], %[k1], %[q3], %[acc]\n\t" QSA_APP(3)
+            : [acc] "+v"(acc), [ad] "+v"(pad), [tk] "=&v"(tk)
+            : QSA_OPS
+            : "memory");
+    } else {
+        asm volatile(
+            "v_mfma_f32_32x32x16_f16 %[acc], %[k0], %[q0], %[acc]\n\t" QSA_APP(0)
+            "v_mfma_f32_32x32x16_f16 %[acc], %[k0], %[q1], %[acc]\n\t" QSA_APP(1)
+            "v_mfma_f32_32x32x16_f16 %[acc], %[k1], %[q2], %[acc]\n\t" QSA_APP(2)
+            "v_mfma_f32_32x32x16_f16 %[acc], %[k1], %[q3], %[acc]\n\t" QSA_APP(3)
+            "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+            : [acc] "+v"(acc), [ad] "+v"(pad), [tk] "=&v"(tk)
+            : QSA_OPS, [f0] "v"(kf[0]), [f1] "v"(kf[1]), [f2] "v"(kf[2]), [f3] "v"(kf[3]), [f4] "v"(kf[4]),
+              [f5] "v"(kf[5])
+            : "memory");
+    }
+#undef QSA_OPS
+#undef QSA_APP
+}
+
 template <Epi EPI>
 __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A) {
     using S = RowsShape;
@@ -198,17 +260,18 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
         }
         cnt = 0;
     };
+    // cache slot of key j of request act (page id clamped into the cache)
+    auto slot_of = [&](int act, int j) {
+        const int32_t* ptrow = a.page_table + (int64_t)act * a.pt_stride;
+        const int lp = A.kpp_shift >= 0 ? (j >> A.kpp_shift) : j / a.kpp;
+        const int slot = j - lp * a.kpp;
+        const int pg = min(max(ptrow[lp], 0), a.num_pages - 1);
+        return (uint32_t)pg * (uint32_t)a.kpp + (uint32_t)slot;
+    };
     // the single-request case builds a piece's slot table while its rows load
     const bool one_req = a.num_reqs == 1;
     auto build_slots = [&](int act, int k0, int k1) {
-        const int32_t* ptrow = a.page_table + (int64_t)act * a.pt_stride;
-        for (int i = tid; i < k1 - k0; i += NT) {
-            const int j = (k0 + i) * A.stride;
-            const int lp = j / a.kpp;
-            const int slot = j - lp * a.kpp;
-            const int pg = min(max(ptrow[lp], 0), a.num_pages - 1);
-            s_slot[i] = (uint32_t)pg * (uint32_t)a.kpp + (uint32_t)slot;
-        }
+        for (int i = tid; i < k1 - k0; i += NT) s_slot[i] = slot_of(act, (k0 + i) * A.stride);
     };
 
     while (p < pend) {
@@ -337,7 +400,7 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
             u32x2 sl_next = slots_of(2);
             const int nsteps = (cend - c0 + STEP - 1) / STEP;
 
-            auto step = [&](int si, const u32x4 (&pf_wait)[NLOAD], u32x4 (&pf_issue)[NLOAD]) {
+            auto step_store = [&](int si, const u32x4 (&pf_wait)[NLOAD], u32x4 (&pf_issue)[NLOAD]) {
                 const int j0 = c0 + si * STEP;
                 const int buf = si & 1;
                 __syncthreads();
@@ -365,7 +428,7 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
                 // element v: key kb + v of row erow
                 const int kb = j0 + 16 * (lane >> 5);
                 const bool full = j0 + STEP <= wlim;
-                if (!FILTER) {
+                {
                     // transpose so that lane l holds keys 4*(l%8) .. +3 of rows l/8 + 8i
                     float* const tw = s_tr[wave];
 #pragma unroll
@@ -392,30 +455,81 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
                                 if (full || key0 + e < lim) dst[e] = w[i][e];
                         }
                     }
-                } else {
-                    // a column tile that crosses a row bound: scores past it cannot pass
-                    if (!full) {
-                        const int nv = min(max(lim_r - kb, 0), 16);
-#pragma unroll
-                        for (int v = 0; v < 16; ++v)
-                            if (v >= nv) acc[v] = -__builtin_huge_valf();
-                    }
-                    uint64_t m[16];
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) m[v] = __builtin_amdgcn_ballot_w64(acc[v] >= fT);
-                    int n = 0;
-                    count_masks8(m, 0, n);
-                    count_masks8(m, 8, n);
-                    if (__any(cnt + n > kLaneCap)) flush(r0 + erow);
-                    uint32_t ad = list0 + (uint32_t)(cnt * 8);
-                    append_masks8(m, acc, 0, kb, ad);
-                    append_masks8(m, acc, 8, kb, ad);
-                    cnt += n;
                 }
             };
-            for (int si = 0; si < nsteps; si += 2) {
-                step(si, pfA, pfB);
-                if (si + 1 < nsteps) step(si + 1, pfB, pfA);
+
+            // Filter: the appends of a stage ride in the next stage's MFMA chain.
+            // Two sets (scores, ballots, list address, key base) alternate: the
+            // step writes one and appends the other's entries.
+            auto step_filter = [&](int si, const u32x4 (&pf_wait)[NLOAD], u32x4 (&pf_issue)[NLOAD], float16v& acc,
+                                   uint64_t (&m)[16], uint32_t& ad, int& kbw, const float16v& pacc,
+                                   const uint64_t (&pm)[16], uint32_t pad, int pkb) {
+                const int j0 = c0 + si * STEP;
+                const int buf = si & 1;
+                __syncthreads();
+                const unsigned char* sk = s_keys[buf];
+                issue(sl_next, pf_issue);
+                sl_next = slots_of(si + 3);
+                __builtin_amdgcn_sched_barrier(0);
+                half8 kf[kSlices];
+#pragma unroll
+                for (int s = 0; s < kSlices; ++s)
+                    kf[s] = *reinterpret_cast<const half8*>(sk + lds_key_chunk(lane & 31, 2 * s + (lane >> 5)));
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_quarter_appends<0>(acc, kf, kf[0], kf[1], qa, pm, pacc, pkb, pad);
+                mfma_quarter_appends<1>(acc, kf, kf[2], kf[3], qa, pm, pacc, pkb, pad);
+                mfma_quarter_appends<2>(acc, kf, kf[4], kf[5], qa, pm, pacc, pkb, pad);
+                mfma_quarter_appends<3>(acc, kf, kf[6], kf[7], qa, pm, pacc, pkb, pad);
+                __builtin_amdgcn_sched_barrier(0);
+                stage_in(buf ^ 1, pf_wait);
+
+                // element v: key kb + v of row erow
+                const int kb = j0 + 16 * (lane >> 5);
+                // a column tile that crosses a row bound: scores past it cannot pass
+                if (j0 + STEP > wlim) {
+                    const int nv = min(max(lim_r - kb, 0), 16);
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (v >= nv) acc[v] = -__builtin_huge_valf();
+                }
+#pragma unroll
+                for (int v = 0; v < 16; ++v) m[v] = __builtin_amdgcn_ballot_w64(acc[v] >= fT);
+                int n = 0;
+                count_masks8(m, 0, n);
+                count_masks8(m, 8, n);
+                // the lists now hold every entry up to the previous stage
+                if (__any(cnt + n > kLaneCap)) flush(r0 + erow);
+                ad = list0 + (uint32_t)(cnt * 8);
+                kbw = kb;
+                cnt += n;
+            };
+
+            if (!FILTER) {
+                for (int si = 0; si < nsteps; si += 2) {
+                    step_store(si, pfA, pfB);
+                    if (si + 1 < nsteps) step_store(si + 1, pfB, pfA);
+                }
+            } else {
+                float16v accA, accB;
+                uint64_t mA[16], mB[16];
+                uint32_t adA = list0, adB = list0;
+                int kbA = 0, kbB = 0;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mB[v] = 0ull;  // nothing pending before the first stage
+                int si = 0;
+                for (; si + 1 < nsteps; si += 2) {
+                    step_filter(si, pfA, pfB, accA, mA, adA, kbA, accB, mB, adB, kbB);
+                    step_filter(si + 1, pfB, pfA, accB, mB, adB, kbB, accA, mA, adA, kbA);
+                }
+                // the last stage's entries
+                if (si < nsteps) {
+                    step_filter(si, pfA, pfB, accA, mA, adA, kbA, accB, mB, adB, kbB);
+                    append_masks8(mA, accA, 0, kbA, adA);
+                    append_masks8(mA, accA, 8, kbA, adA);
+                } else {
+                    append_masks8(mB, accB, 0, kbB, adB);
+                    append_masks8(mB, accB, 8, kbB, adB);
+                }
             }
             // every wave is done with this pass's s_lim before wave 0 rewrites it
             __syncthreads();

@@ -81,7 +81,7 @@ KERNEL_SOURCES = {
                 "paged_block_scoring_amd/csrc/score.hip", "paged_block_scoring_amd/csrc/qsa_device.hpp"]),
     "sample_threshold": (("sample_threshold_kernel",),
                          ["paged_block_scoring_amd/csrc/fused.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
-    "final_select": (("fused_final_kernel",),
+    "final_select": (("fused_select_kernel",),
                      ["paged_block_scoring_amd/csrc/fused.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
     "topk_rows": (("topk_rows_kernel",), ["paged_block_scoring_amd/csrc/topk.hip"]),
 }

@@ -148,6 +148,7 @@ struct FinalArgs {
     VisibleSource vis;
     const uint64_t* cand;
     const int32_t* cand_count;
+    const uint64_t* thresh;  // [rows] the filter's threshold composites (high word: order key of the score)
     int32_t cand_cap;
     int32_t kb;
     int32_t expand;
@@ -264,148 +265,205 @@ __device__ __forceinline__ void write_rank(int32_t* orow, int r, uint32_t idx, i
     for (int t = 0; t < expand; ++t) orow[r * expand + t] = base + t;
 }
 
-// One row per workgroup.  Candidate path: the row's candidates are loaded
-// into registers as (order key, index) and binned by order key over their
-// range (kSelBins ordered bins); with start[bin] = entries in higher bins,
-// every entry of a bin at or above the bin b holding the kb-th largest is
-// scattered into LDS at start[bin] + (its arrival in the bin) and ranks
-// itself inside its bin by counting larger members: ranks below min(kb, V)
-// are the selection, already in rank order.  A bin at or above b with more
-// than kMaxBucket entries (heavy clustering or ties) switches the row to an
-// exact histogram descent (ties at the cut broken by a second descent over
-// inverted indices) and a bitonic sort of the selected set.  Rows whose
-// candidate list is unusable take the recompute path.
+// LDS of the select kernel: the candidate path and the recompute path use
+// the same memory (a row takes one of them).
+template <int KBMAX>
+union SelectLds {
+    struct {
+        uint64_t a[KBMAX + kMaxBucket];
+        uint32_t start[kSelBins];
+        HistScratch hs;
+    } f;
+    struct {
+        uint64_t a[KBMAX + kRecChunk];
+        KthScratch ks;
+        int pend;
+        float rs[32 * kFinWaves];
+    } r;
+};
+
+// One row per workgroup.  The row's visible count, candidate count,
+// threshold and first 2,048 candidate slots are loaded at once (slots past
+// the count are clamped into the list and masked).
+// Candidate path: the candidates are held in registers as (order key,
+// index) and binned by order key between the threshold's key (no candidate
+// is below it) and their largest (kSelBins ordered bins); with start[bin] =
+// entries in higher bins, every entry of a bin at or above the bin b holding
+// the kb-th largest is scattered into LDS at start[bin] + (its arrival in the
+// bin) and ranks itself inside its bin by counting larger members: ranks
+// below min(kb, V) are the selection, already in rank order.  A bin at or
+// above b with more than kMaxBucket entries (heavy clustering or ties)
+// switches the row to an exact histogram descent (ties at the cut broken by
+// a second descent over inverted indices) and a bitonic sort of the
+// selected set.
+// Rows whose candidate list is unusable (too short: the threshold was too
+// high; too long: it was too low or its score has many ties; or the
+// sampling pass left the row out) take the recompute path: exact top-kb by
+// recomputation (recompute_row_topk), then a sort in LDS.
 template <int KBMAX, int CAPC>
-__global__ __launch_bounds__(kFinNT) void fused_final_kernel(FinalArgs A) {
+__global__ __launch_bounds__(kFinNT) void fused_select_kernel(FinalArgs A) {
     constexpr int EPT = CAPC / kFinNT;
-    __shared__ uint64_t s_a[KBMAX + kMaxBucket];
-    __shared__ uint32_t s_start[kSelBins];
-    __shared__ HistScratch hs;
+    static_assert(EPT % 4 == 0 && EPT >= 8, "slot groups of 4, two issued up front");
+    __shared__ SelectLds<KBMAX> L;
     const int row = blockIdx.x;
-    const int V = row_visible_count(A.vis, row);
+    const int tid = threadIdx.x;
     const int kb = A.kb;
-    const int nsel = min(kb, V);
-    const int n = A.cand_count[row];
     int32_t* orow = A.out + (int64_t)row * A.out_len;
     const bool vec4 = A.expand == 4 && (A.out_len & 3) == 0 && (reinterpret_cast<uintptr_t>(A.out) & 15) == 0;
-    if (n < nsel || n > A.cand_cap) return;  // fused_recompute_kernel's row
-    {
-        if (nsel > 0) {
-            const uint64_t* c = A.cand + (int64_t)row * A.cand_cap;
-            uint32_t k[EPT], idx[EPT];
-            // loads in groups of 4 slots, each group issued before any use
-            // (indices past n are clamped into the row's list and masked)
-            static_assert(EPT % 4 == 0, "slot groups of 4");
+
+    // everything the row needs first, in one round of loads
+    const uint64_t* c = A.cand + (int64_t)row * A.cand_cap;
+    uint64_t en[8];
 #pragma unroll
-            for (int g = 0; g < EPT; g += 4) {
+    for (int e = 0; e < 8; ++e) en[e] = c[min(e * kFinNT + tid, A.cand_cap - 1)];  // (score bits, key)
+    const int n = A.cand_count[row];
+    const uint32_t tkey = (uint32_t)(A.thresh[row] >> 32);
+    const int V = row_visible_count(A.vis, row);
+    const int nsel = min(kb, V);
+
+    if (n < nsel || n > A.cand_cap) {
+        const int have = recompute_row_topk<KBMAX + kRecChunk>(A, row, V, L.r.a, &L.r.ks, &L.r.pend, L.r.rs);
+        lds_sort_desc<kFinNT>(L.r.a, have);
+        for (int i = tid; i < A.out_len; i += kFinNT) {
+            const int rank = i / A.expand, t = i - rank * A.expand;
+            int v = -1;
+            if (rank < nsel) v = (int)composite_index(L.r.a[rank]) * A.expand + t;
+            orow[i] = v;
+        }
+        return;
+    }
+    uint64_t* const s_a = L.f.a;
+    uint32_t* const s_start = L.f.start;
+    HistScratch& hs = L.f.hs;
+    if (nsel > 0) {
+        uint32_t k[EPT], idx[EPT];
 #pragma unroll
-                for (int e = g; e < g + 4; ++e) {
-                    k[e] = 0u;
-                    idx[e] = 0u;
-                }
-                if (g * kFinNT < n) {
-                    uint64_t en[4];
+        for (int e = 0; e < 8; ++e) {
+            const bool in = e * kFinNT + tid < n;
+            k[e] = in ? order_key(__uint_as_float((uint32_t)(en[e] >> 32))) : 0u;
+            idx[e] = in ? (uint32_t)en[e] : 0u;
+        }
+        // the rest of a long list, 4 slots per group
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        en[e] = c[min((g + e) * kFinNT + (int)threadIdx.x, A.cand_cap - 1)];  // (score bits, key)
+        for (int g = 8; g < EPT; g += 4) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if ((g + e) * kFinNT + (int)threadIdx.x < n) {
-                            k[g + e] = order_key(__uint_as_float((uint32_t)(en[e] >> 32)));
-                            idx[g + e] = (uint32_t)en[e];
-                        }
-                    }
-                }
+            for (int e = g; e < g + 4; ++e) {
+                k[e] = 0u;
+                idx[e] = 0u;
             }
-            // one histogram level over the order keys: the bin b holding the
-            // kb-th largest; every entry of a bin >= b is scattered into LDS at
-            // start[bin] + (its arrival in the bin) and ranks itself inside its
-            // bin; ranks below nsel are the selection
-            uint32_t mn, mx;
-            block_minmax_u32<kFinNT, EPT>(k, n, &mn, &mx, &hs);
-            const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
-            int above, cnt;
-            const int b = (int)hist_level32<kFinNT, EPT>(k, n, mn, shift1, 32, 0u, nsel, &hs, s_start, &above, &cnt);
-            bool slow = cnt > kMaxBucket;
-            if (!slow) {
-                for (int i = threadIdx.x; i < kSelBins; i += kFinNT) hs.hist[i] = 0u;
-                if (threadIdx.x == 0) hs.flag = 0;
-                __syncthreads();
+            if (g * kFinNT < n) {
+                uint64_t ex[4];
 #pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    if (e * kFinNT < n && k[e]) {
-                        const uint32_t bn = (k[e] - mn) >> shift1;
-                        if ((int)bn >= b) s_a[s_start[bn] + atomicAdd(&hs.hist[bn], 1u)] = compose(k[e], idx[e]);
+                for (int e = 0; e < 4; ++e) ex[e] = c[min((g + e) * kFinNT + tid, A.cand_cap - 1)];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if ((g + e) * kFinNT + tid < n) {
+                        k[g + e] = order_key(__uint_as_float((uint32_t)(ex[e] >> 32)));
+                        idx[g + e] = (uint32_t)ex[e];
                     }
                 }
-                __syncthreads();
-                for (int p = threadIdx.x; p < above + cnt; p += kFinNT) {
-                    const uint64_t me = s_a[p];
-                    const uint32_t bn = ((uint32_t)(me >> 32) - mn) >> shift1;
-                    const int st = (int)s_start[bn], cn = (int)hs.hist[bn];
-                    if (cn > kMaxBucket) {
-                        hs.flag = 1;  // a crowded bin above b: the row takes the sort below
-                        continue;
-                    }
-                    int r = 0;
-                    for (int i = st; i < st + cn; ++i) r += s_a[i] > me ? 1 : 0;
-                    if (st + r < nsel) write_rank(orow, st + r, composite_index(me), A.expand, vec4);
-                }
-                __syncthreads();
-                slow = hs.flag != 0;
-            }
-            if (slow) {
-                // exact pivot by a histogram descent (ties at the cut broken by a
-                // second descent over inverted indices), then a bitonic sort
-                const Descent d = hist_descent32<kFinNT, EPT>(k, n, nsel, &hs, nullptr);
-                uint32_t jpiv = 0u;
-                if (!d.exact) {
-                    uint32_t t[EPT];
-#pragma unroll
-                    for (int e = 0; e < EPT; ++e) t[e] = (e * kFinNT < n && k[e] && k[e] == d.pivot) ? ~idx[e] : 0u;
-                    jpiv = hist_descent32<kFinNT, EPT>(t, n, nsel - d.above, &hs, nullptr).pivot;
-                }
-                if (threadIdx.x == 0) hs.cnt = 0;
-                __syncthreads();
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) {
-                    const bool sel = e * kFinNT < n && k[e] &&
-                                     (k[e] > d.pivot || (k[e] == d.pivot && (d.exact || ~idx[e] >= jpiv)));
-                    if (sel) s_a[atomicAdd(&hs.cnt, 1)] = compose(k[e], idx[e]);
-                }
-                __syncthreads();
-                lds_sort_desc<kFinNT>(s_a, nsel);
-                for (int r = threadIdx.x; r < nsel; r += kFinNT) write_rank(orow, r, composite_index(s_a[r]), A.expand, vec4);
             }
         }
-        for (int i = nsel * A.expand + (int)threadIdx.x; i < A.out_len; i += kFinNT) orow[i] = -1;
+        // one histogram level over the order keys, from the threshold's key
+        // to the largest: the bin b holding the kb-th largest; every entry of
+        // a bin >= b is scattered into LDS at start[bin] + (its arrival in the
+        // bin) and ranks itself inside its bin; ranks below nsel are the
+        // selection
+        const int lane = tid & 63, wave = tid >> 6;
+        uint32_t mx = 0u;
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) mx = max(mx, k[e]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+        if (lane == 0) hs.wmax[wave] = mx;
+        for (int i = tid; i < kSelBins; i += kFinNT) hs.hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kFinWaves; ++w) mx = max(mx, hs.wmax[w]);
+        const uint32_t mn = min(tkey, mx);  // every candidate key is >= the threshold's
+        const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)
+            if (e * kFinNT < n && k[e]) atomicAdd(&hs.hist[(k[e] - mn) >> shift1], 1u);
+        __syncthreads();
+        // thread t owns bins kSelBins-1-BPT*t .. (high to low)
+        constexpr int BPT = kSelBins / kFinNT;
+        uint32_t cb[BPT];
+        int local = 0;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+            cb[j] = hs.hist[kSelBins - 1 - BPT * tid - j];
+            local += (int)cb[j];
+        }
+        int total;
+        int run = block_inclusive_scan<kFinNT>(local, hs.wsum, &total) - local;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+            const int bin = kSelBins - 1 - BPT * tid - j;
+            s_start[bin] = (uint32_t)run;
+            if (run < nsel && run + (int)cb[j] >= nsel) {
+                hs.bin = bin;
+                hs.above = run;
+                hs.cnt = (int)cb[j];
+            }
+            run += (int)cb[j];
+        }
+        __syncthreads();
+        const int b = hs.bin, above = hs.above, cnt = hs.cnt;
+        bool slow = cnt > kMaxBucket;
+        if (!slow) {
+            __syncthreads();
+            for (int i = tid; i < kSelBins; i += kFinNT) hs.hist[i] = 0u;
+            if (tid == 0) hs.flag = 0;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                if (e * kFinNT < n && k[e]) {
+                    const uint32_t bn = (k[e] - mn) >> shift1;
+                    if ((int)bn >= b) s_a[s_start[bn] + atomicAdd(&hs.hist[bn], 1u)] = compose(k[e], idx[e]);
+                }
+            }
+            __syncthreads();
+            for (int p = tid; p < above + cnt; p += kFinNT) {
+                const uint64_t me = s_a[p];
+                const uint32_t bn = ((uint32_t)(me >> 32) - mn) >> shift1;
+                const int st = (int)s_start[bn], cn = (int)hs.hist[bn];
+                if (cn > kMaxBucket) {
+                    hs.flag = 1;  // a crowded bin above b: the row takes the sort below
+                    continue;
+                }
+                int r = 0;
+                for (int i = st; i < st + cn; ++i) r += s_a[i] > me ? 1 : 0;
+                if (st + r < nsel) write_rank(orow, st + r, composite_index(me), A.expand, vec4);
+            }
+            __syncthreads();
+            slow = hs.flag != 0;
+        }
+        if (slow) {
+            // exact pivot by a histogram descent (ties at the cut broken by a
+            // second descent over inverted indices), then a bitonic sort
+            const Descent d = hist_descent32<kFinNT, EPT>(k, n, nsel, &hs, nullptr);
+            uint32_t jpiv = 0u;
+            if (!d.exact) {
+                uint32_t t[EPT];
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) t[e] = (e * kFinNT < n && k[e] && k[e] == d.pivot) ? ~idx[e] : 0u;
+                jpiv = hist_descent32<kFinNT, EPT>(t, n, nsel - d.above, &hs, nullptr).pivot;
+            }
+            if (tid == 0) hs.cnt = 0;
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) {
+                const bool sel = e * kFinNT < n && k[e] &&
+                                 (k[e] > d.pivot || (k[e] == d.pivot && (d.exact || ~idx[e] >= jpiv)));
+                if (sel) s_a[atomicAdd(&hs.cnt, 1)] = compose(k[e], idx[e]);
+            }
+            __syncthreads();
+            lds_sort_desc<kFinNT>(s_a, nsel);
+            for (int r = tid; r < nsel; r += kFinNT) write_rank(orow, r, composite_index(s_a[r]), A.expand, vec4);
+        }
     }
-}
-
-// The rows whose candidate list is unusable (too short: the threshold was
-// too high; too long: it was too low or its score has many ties; or the
-// sampling pass left the row out): exact top-kb by recomputation.
-template <int KBMAX>
-__global__ __launch_bounds__(kFinNT) void fused_recompute_kernel(FinalArgs A) {
-    constexpr int LA = KBMAX + kRecChunk;
-    __shared__ uint64_t s_a[LA];
-    __shared__ KthScratch ks;
-    __shared__ int s_pend;
-    __shared__ float s_rs[32 * kFinWaves];
-    const int row = blockIdx.x;
-    const int V = row_visible_count(A.vis, row);
-    const int nsel = min(A.kb, V);
-    const int n = A.cand_count[row];
-    if (n >= nsel && n <= A.cand_cap) return;  // fused_final_kernel's row
-    int32_t* orow = A.out + (int64_t)row * A.out_len;
-    const int have = recompute_row_topk<LA>(A, row, V, s_a, &ks, &s_pend, s_rs);
-    lds_sort_desc<kFinNT>(s_a, have);
-    for (int i = threadIdx.x; i < A.out_len; i += kFinNT) {
-        const int rank = i / A.expand, t = i - rank * A.expand;
-        int v = -1;
-        if (rank < nsel) v = (int)composite_index(s_a[rank]) * A.expand + t;
-        orow[i] = v;
-    }
+    for (int i = nsel * A.expand + tid; i < A.out_len; i += kFinNT) orow[i] = -1;
 }
 
 }  // namespace
@@ -433,28 +491,26 @@ hipError_t launch_sample_threshold(const float* samp, int64_t ld_s, const Visibl
     return hipGetLastError();
 }
 
-hipError_t launch_fused_final(const PagedArgs& a, const VisibleSource& vis, const FusedPlan& f, const uint64_t* cand,
-                              const int32_t* cand_count, int32_t kb, int32_t expand, int32_t out_len, int32_t* out,
-                              hipStream_t stream) {
+hipError_t launch_fused_final(const PagedArgs& a, const VisibleSource& vis, const FusedPlan& f, const uint64_t* thresh,
+                              const uint64_t* cand, const int32_t* cand_count, int32_t kb, int32_t expand,
+                              int32_t out_len, int32_t* out, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     FinalArgs A;
     A.a = a;
     A.vis = vis;
     A.cand = cand;
     A.cand_count = cand_count;
+    A.thresh = thresh;
     A.cand_cap = f.cand_cap;
     A.kb = kb;
     A.expand = expand;
     A.out_len = out_len;
     A.out = out;
     const dim3 grid((unsigned)a.rows);
-    if (f.capl == 4096) {
-        fused_final_kernel<1024, 4096><<<grid, kFinNT, 0, stream>>>(A);
-        fused_recompute_kernel<1024><<<grid, kFinNT, 0, stream>>>(A);
-    } else {
-        fused_final_kernel<QSA_MAX_SELECT, 8192><<<grid, kFinNT, 0, stream>>>(A);
-        fused_recompute_kernel<QSA_MAX_SELECT><<<grid, kFinNT, 0, stream>>>(A);
-    }
+    if (f.capl == 4096)
+        fused_select_kernel<1024, 4096><<<grid, kFinNT, 0, stream>>>(A);
+    else
+        fused_select_kernel<QSA_MAX_SELECT, 8192><<<grid, kFinNT, 0, stream>>>(A);
     return hipGetLastError();
 }
 

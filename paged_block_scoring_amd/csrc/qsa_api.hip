@@ -358,7 +358,7 @@ QSA_EXPORT qsa_status qsa_select_paged_tokens(const void* q, const void* kcache,
         HIP_CHECK(mark(s));
         HIP_CHECK(qsa::launch_score_filter(a, qsum, thresh, cand, count, L.plan.cand_cap, cus, s));
         HIP_CHECK(mark(s));
-        HIP_CHECK(qsa::launch_fused_final(a, vs, L.plan, cand, count, kb, expand, k, out, s));
+        HIP_CHECK(qsa::launch_fused_final(a, vs, L.plan, thresh, cand, count, kb, expand, k, out, s));
         HIP_CHECK(mark(s));
         g_events = nullptr;
         g_path = "fused";

@@ -249,31 +249,13 @@ __device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* 
     return na;
 }
 
-constexpr int kMaxBucket = 32;
 constexpr int kRecChunk = 512;  // keys scored per round by the recompute path
-
-// Writes rank r's block (expanded to `expand` tokens) into the output row
-// (one 16-byte store for the usual 4-token blocks; out_len is then a
-// multiple of 4 and the row 16-byte aligned).
-__device__ __forceinline__ void write_rank(int32_t* orow, int r, uint32_t idx, int expand, bool vec4) {
-    const int base = (int)idx * expand;
-    if (vec4) {
-        typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-        *reinterpret_cast<i32x4*>(orow + 4 * r) = i32x4{base, base + 1, base + 2, base + 3};
-        return;
-    }
-    for (int t = 0; t < expand; ++t) orow[r * expand + t] = base + t;
-}
 
 // LDS of the select kernel: the candidate path and the recompute path use
 // the same memory (a row takes one of them).
 template <int KBMAX>
 union SelectLds {
-    struct {
-        uint64_t a[KBMAX + kMaxBucket];
-        uint32_t start[kSelBins];
-        HistScratch hs;
-    } f;
+    BoundSelectLds<KBMAX> f;
     struct {
         uint64_t a[KBMAX + kRecChunk];
         KthScratch ks;
@@ -332,9 +314,6 @@ __global__ __launch_bounds__(kFinNT) void fused_select_kernel(FinalArgs A) {
         }
         return;
     }
-    uint64_t* const s_a = L.f.a;
-    uint32_t* const s_start = L.f.start;
-    HistScratch& hs = L.f.hs;
     if (nsel > 0) {
         uint32_t k[EPT], idx[EPT];
 #pragma unroll
@@ -364,104 +343,10 @@ __global__ __launch_bounds__(kFinNT) void fused_select_kernel(FinalArgs A) {
                 }
             }
         }
-        // one histogram level over the order keys, from the threshold's key
-        // to the largest: the bin b holding the kb-th largest; every entry of
-        // a bin >= b is scattered into LDS at start[bin] + (its arrival in the
-        // bin) and ranks itself inside its bin; ranks below nsel are the
-        // selection
-        const int lane = tid & 63, wave = tid >> 6;
-        uint32_t mx = 0u;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) mx = max(mx, k[e]);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
-        if (lane == 0) hs.wmax[wave] = mx;
-        for (int i = tid; i < kSelBins; i += kFinNT) hs.hist[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int w = 0; w < kFinWaves; ++w) mx = max(mx, hs.wmax[w]);
-        const uint32_t mn = min(tkey, mx);  // every candidate key is >= the threshold's
-        const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
-#pragma unroll
-        for (int e = 0; e < EPT; ++e)
-            if (e * kFinNT < n && k[e]) atomicAdd(&hs.hist[(k[e] - mn) >> shift1], 1u);
-        __syncthreads();
-        // thread t owns bins kSelBins-1-BPT*t .. (high to low)
-        constexpr int BPT = kSelBins / kFinNT;
-        uint32_t cb[BPT];
-        int local = 0;
-#pragma unroll
-        for (int j = 0; j < BPT; ++j) {
-            cb[j] = hs.hist[kSelBins - 1 - BPT * tid - j];
-            local += (int)cb[j];
-        }
-        int total;
-        int run = block_inclusive_scan<kFinNT>(local, hs.wsum, &total) - local;
-#pragma unroll
-        for (int j = 0; j < BPT; ++j) {
-            const int bin = kSelBins - 1 - BPT * tid - j;
-            s_start[bin] = (uint32_t)run;
-            if (run < nsel && run + (int)cb[j] >= nsel) {
-                hs.bin = bin;
-                hs.above = run;
-                hs.cnt = (int)cb[j];
-            }
-            run += (int)cb[j];
-        }
-        __syncthreads();
-        const int b = hs.bin, above = hs.above, cnt = hs.cnt;
-        bool slow = cnt > kMaxBucket;
-        if (!slow) {
-            __syncthreads();
-            for (int i = tid; i < kSelBins; i += kFinNT) hs.hist[i] = 0u;
-            if (tid == 0) hs.flag = 0;
-            __syncthreads();
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                if (e * kFinNT < n && k[e]) {
-                    const uint32_t bn = (k[e] - mn) >> shift1;
-                    if ((int)bn >= b) s_a[s_start[bn] + atomicAdd(&hs.hist[bn], 1u)] = compose(k[e], idx[e]);
-                }
-            }
-            __syncthreads();
-            for (int p = tid; p < above + cnt; p += kFinNT) {
-                const uint64_t me = s_a[p];
-                const uint32_t bn = ((uint32_t)(me >> 32) - mn) >> shift1;
-                const int st = (int)s_start[bn], cn = (int)hs.hist[bn];
-                if (cn > kMaxBucket) {
-                    hs.flag = 1;  // a crowded bin above b: the row takes the sort below
-                    continue;
-                }
-                int r = 0;
-                for (int i = st; i < st + cn; ++i) r += s_a[i] > me ? 1 : 0;
-                if (st + r < nsel) write_rank(orow, st + r, composite_index(me), A.expand, vec4);
-            }
-            __syncthreads();
-            slow = hs.flag != 0;
-        }
-        if (slow) {
-            // exact pivot by a histogram descent (ties at the cut broken by a
-            // second descent over inverted indices), then a bitonic sort
-            const Descent d = hist_descent32<kFinNT, EPT>(k, n, nsel, &hs, nullptr);
-            uint32_t jpiv = 0u;
-            if (!d.exact) {
-                uint32_t t[EPT];
-#pragma unroll
-                for (int e = 0; e < EPT; ++e) t[e] = (e * kFinNT < n && k[e] && k[e] == d.pivot) ? ~idx[e] : 0u;
-                jpiv = hist_descent32<kFinNT, EPT>(t, n, nsel - d.above, &hs, nullptr).pivot;
-            }
-            if (tid == 0) hs.cnt = 0;
-            __syncthreads();
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) {
-                const bool sel = e * kFinNT < n && k[e] &&
-                                 (k[e] > d.pivot || (k[e] == d.pivot && (d.exact || ~idx[e] >= jpiv)));
-                if (sel) s_a[atomicAdd(&hs.cnt, 1)] = compose(k[e], idx[e]);
-            }
-            __syncthreads();
-            lds_sort_desc<kFinNT>(s_a, nsel);
-            for (int r = tid; r < nsel; r += kFinNT) write_rank(orow, r, composite_index(s_a[r]), A.expand, vec4);
-        }
+        // every candidate's key is >= the threshold's
+        select_from_bound<kFinNT, EPT, KBMAX>(
+            k, [&](int e) { return idx[e]; }, n, nsel, tkey, L.f,
+            [&](int r, uint32_t j) { write_rank(orow, r, j, A.expand, vec4); });
     }
     for (int i = nsel * A.expand + tid; i < A.out_len; i += kFinNT) orow[i] = -1;
 }

@@ -149,18 +149,24 @@ struct HistScratch {
 
 __device__ __forceinline__ int bit_length32(uint32_t x) { return x ? 32 - __clz((int)x) : 0; }
 
+// The helpers below read key e of the calling thread as key(e) (a functor,
+// so that derived keys need no register array of their own).
+
 // Block-wide smallest and largest nonzero key (both 0 if there is none).
 // Slots e with e*NT >= nmax are skipped.  Contains barriers.
-template <int NT, int EPT>
-__device__ void block_minmax_u32(const uint32_t (&k)[EPT], int nmax, uint32_t* mn, uint32_t* mx, HistScratch* s) {
+template <int NT, int EPT, class KeyF>
+__device__ __forceinline__ void block_minmax_u32(KeyF key, int nmax, uint32_t* mn, uint32_t* mx, HistScratch* s) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t a = 0xFFFFFFFFu, b = 0u;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e)
-        if (e * NT < nmax && k[e]) {
-            a = min(a, k[e]);
-            b = max(b, k[e]);
+    for (int e = 0; e < EPT; ++e) {
+        if (e * NT >= nmax) continue;
+        const uint32_t ke = key(e);
+        if (ke) {
+            a = min(a, ke);
+            b = max(b, ke);
         }
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         a = min(a, (uint32_t)__shfl_xor((int)a, o, 64));
@@ -191,8 +197,8 @@ __device__ void block_minmax_u32(const uint32_t (&k)[EPT], int nmax, uint32_t* m
 // participants in that bin.  If `start` is given, start[bin] receives the
 // number of participants in bins above `bin`, for every bin.  Contains
 // barriers.
-template <int NT, int EPT>
-__device__ uint32_t hist_level32(const uint32_t (&k)[EPT], int nmax, uint32_t base, int shift, int pshift,
+template <int NT, int EPT, class KeyF>
+__device__ __forceinline__ uint32_t hist_level32(KeyF key, int nmax, uint32_t base, int shift, int pshift,
                                  uint32_t prefix, int need, HistScratch* s, uint32_t* start, int* above, int* cnt) {
     constexpr int BPT = kSelBins / NT;
     static_assert(BPT * NT == kSelBins, "bins per thread");
@@ -202,8 +208,10 @@ __device__ uint32_t hist_level32(const uint32_t (&k)[EPT], int nmax, uint32_t ba
     const uint32_t dmask = pshift - shift >= 32 ? 0xFFFFFFFFu : ((1u << (pshift - shift)) - 1u);
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-        if (e * NT >= nmax || !k[e]) continue;
-        const uint32_t d = k[e] - base;
+        if (e * NT >= nmax) continue;
+        const uint32_t ke = key(e);
+        if (!ke) continue;
+        const uint32_t d = ke - base;
         if (pshift < 32 && (d >> pshift) != prefix) continue;
         atomicAdd(&s->hist[(d >> shift) & dmask], 1u);
     }
@@ -251,22 +259,22 @@ struct Descent {
 // >= pivot -- or the descent reaches a single key value with more copies than
 // needed: pivot is that value, `above` keys are larger.  start1 (optional)
 // receives the top level's "keys in higher bins" counts.  Contains barriers.
-template <int NT, int EPT>
-__device__ Descent hist_descent32(const uint32_t (&k)[EPT], int nmax, int need, HistScratch* s, uint32_t* start1) {
+template <int NT, int EPT, class KeyF>
+__device__ __forceinline__ Descent hist_descent32(KeyF key, int nmax, int need, HistScratch* s, uint32_t* start1) {
     Descent r;
     uint32_t mn, mx;
-    block_minmax_u32<NT, EPT>(k, nmax, &mn, &mx, s);
+    block_minmax_u32<NT, EPT>(key, nmax, &mn, &mx, s);
     const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
     r.base = mn;
     r.shift1 = shift1;
     int above, cnt;
-    uint32_t prefix = hist_level32<NT, EPT>(k, nmax, mn, shift1, 32, 0u, need, s, start1, &above, &cnt);
+    uint32_t prefix = hist_level32<NT, EPT>(key, nmax, mn, shift1, 32, 0u, need, s, start1, &above, &cnt);
     int total_above = above;
     int nd = need - above;
     int cur = shift1;
     while (cnt != nd && cur > 0) {
         const int ns = cur > kSelBits ? cur - kSelBits : 0;
-        const uint32_t b = hist_level32<NT, EPT>(k, nmax, mn, ns, cur, prefix, nd, s, nullptr, &above, &cnt);
+        const uint32_t b = hist_level32<NT, EPT>(key, nmax, mn, ns, cur, prefix, nd, s, nullptr, &above, &cnt);
         prefix = (prefix << (cur - ns)) | b;
         cur = ns;
         nd -= above;
@@ -276,6 +284,161 @@ __device__ Descent hist_descent32(const uint32_t (&k)[EPT], int nmax, int need, 
     r.exact = cnt == nd;
     r.above = total_above;
     return r;
+}
+
+// ---------------------------------------------------------------------------
+// Selection of a row's top-nsel from keys held by the workgroup's threads.
+
+constexpr int kMaxBucket = 32;
+
+template <int KBMAX>
+struct BoundSelectLds {
+    uint64_t a[KBMAX + kMaxBucket];
+    uint32_t start[kSelBins];
+    HistScratch hs;
+};
+
+// Exact top-nsel of the nonzero keys key(e) (indices idx(e)), sorted: the
+// cut is found by a histogram descent over the keys, ties at the cut by a
+// second descent over the inverted indices of the keys equal to it; the
+// selected set is gathered into LDS and sorted (bitonic).  emit(r, index) is
+// called once for each rank r < nsel.  Contains barriers.
+template <int NT, int EPT, int KBMAX, class KeyF, class IdxF, class EmitF>
+__device__ __forceinline__ void select_exact_sorted(KeyF key, IdxF idx, int nmax, int nsel, BoundSelectLds<KBMAX>& L,
+                                                    EmitF emit) {
+    HistScratch& hs = L.hs;
+    const int tid = threadIdx.x;
+    const Descent d = hist_descent32<NT, EPT>(key, nmax, nsel, &hs, nullptr);
+    uint32_t jpiv = 0u;
+    if (!d.exact)
+        jpiv = hist_descent32<NT, EPT>(
+                   [&](int e) {
+                       const uint32_t ke = key(e);
+                       return ke && ke == d.pivot ? ~idx(e) : 0u;
+                   },
+                   nmax, nsel - d.above, &hs, nullptr)
+                   .pivot;
+    if (tid == 0) hs.cnt = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+        if (e * NT >= nmax) continue;
+        const uint32_t ke = key(e);
+        const bool sel = ke && (ke > d.pivot || (ke == d.pivot && (d.exact || ~idx(e) >= jpiv)));
+        if (sel) L.a[atomicAdd(&hs.cnt, 1)] = compose(ke, idx(e));
+    }
+    __syncthreads();
+    lds_sort_desc<NT>(L.a, nsel);
+    for (int r = tid; r < nsel; r += NT) emit(r, composite_index(L.a[r]));
+}
+
+// Exact top-nsel of register-resident keys with a known lower bound.
+//
+// Each of the NT threads holds EPT keys k[e] (element e*NT + threadIdx.x,
+// index idx(e)); 0 marks an empty slot, slots e with e*NT >= nmax are
+// skipped, and every nonempty key is >= lo.  nsel (>= 1) must not exceed the
+// number of nonempty keys, nor KBMAX.  emit(r, index) is called exactly once
+// for each rank r < nsel.
+//
+// Method: the keys are binned between lo and their maximum (kSelBins bins of
+// a power-of-two width); with start[bin] = keys in higher bins, every key of a
+// bin at or above the bin b holding the nsel-th largest is scattered into LDS
+// at start[bin] + (its arrival in the bin) and ranks itself inside its bin by
+// counting the larger (key, ~index) composites there: its rank is start[bin]
+// plus that count.  The result comes out in rank order with no sort.  If a
+// bin at or above b holds more than kMaxBucket keys (clustering or ties), the
+// workgroup takes select_exact_sorted instead.
+template <int NT, int EPT, int KBMAX, class IdxF, class EmitF>
+__device__ __forceinline__ void select_from_bound(const uint32_t (&k)[EPT], IdxF idx, int nmax, int nsel, uint32_t lo,
+                                  BoundSelectLds<KBMAX>& L, EmitF emit) {
+    static_assert(KBMAX >= 1 && (KBMAX & (KBMAX - 1)) == 0, "the sort pads nsel to a power of two <= KBMAX");
+    constexpr int BPT = kSelBins / NT;
+    static_assert(BPT * NT == kSelBins, "bins per thread");
+    HistScratch& hs = L.hs;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+        if (e * NT < nmax) mx = max(mx, k[e]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+    if (lane == 0) hs.wmax[wave] = mx;
+    for (int i = tid; i < kSelBins; i += NT) hs.hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) mx = max(mx, hs.wmax[w]);
+    const uint32_t mn = min(lo, mx);
+    const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+        if (e * NT < nmax && k[e]) atomicAdd(&hs.hist[(k[e] - mn) >> shift1], 1u);
+    __syncthreads();
+    // thread t owns bins kSelBins-1-BPT*t .. (high to low)
+    uint32_t cb[BPT];
+    int local = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        cb[j] = hs.hist[kSelBins - 1 - BPT * tid - j];
+        local += (int)cb[j];
+    }
+    int total;
+    int run = block_inclusive_scan<NT>(local, hs.wsum, &total) - local;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+        const int bin = kSelBins - 1 - BPT * tid - j;
+        L.start[bin] = (uint32_t)run;
+        if (run < nsel && run + (int)cb[j] >= nsel) {
+            hs.bin = bin;
+            hs.above = run;
+            hs.cnt = (int)cb[j];
+        }
+        run += (int)cb[j];
+    }
+    __syncthreads();
+    const int b = hs.bin, above = hs.above, cnt = hs.cnt;
+    bool slow = cnt > kMaxBucket;
+    if (!slow) {
+        __syncthreads();
+        for (int i = tid; i < kSelBins; i += NT) hs.hist[i] = 0u;
+        if (tid == 0) hs.flag = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            if (e * NT < nmax && k[e]) {
+                const uint32_t bn = (k[e] - mn) >> shift1;
+                if ((int)bn >= b) L.a[L.start[bn] + atomicAdd(&hs.hist[bn], 1u)] = compose(k[e], idx(e));
+            }
+        }
+        __syncthreads();
+        for (int p = tid; p < above + cnt; p += NT) {
+            const uint64_t me = L.a[p];
+            const uint32_t bn = ((uint32_t)(me >> 32) - mn) >> shift1;
+            const int st = (int)L.start[bn], cn = (int)hs.hist[bn];
+            if (cn > kMaxBucket) {
+                hs.flag = 1;  // a crowded bin above b: the sort below takes over
+                continue;
+            }
+            int r = 0;
+            for (int i = st; i < st + cn; ++i) r += L.a[i] > me ? 1 : 0;
+            if (st + r < nsel) emit(st + r, composite_index(me));
+        }
+        __syncthreads();
+        slow = hs.flag != 0;
+    }
+    if (slow) select_exact_sorted<NT, EPT, KBMAX>([&](int e) { return k[e]; }, idx, nmax, nsel, L, emit);
+}
+
+// Writes rank r's block, expanded to `expand` consecutive tokens, into an
+// output row (one 16-byte store for 4-token blocks when the row is 16-byte
+// aligned and its length a multiple of 4).
+__device__ __forceinline__ void write_rank(int32_t* orow, int r, uint32_t idx, int expand, bool vec4) {
+    const int base = (int)idx * expand;
+    if (vec4) {
+        typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<i32x4*>(orow + 4 * r) = i32x4{base, base + 1, base + 2, base + 3};
+        return;
+    }
+    for (int t = 0; t < expand; ++t) orow[r * expand + t] = base + t;
 }
 
 }  // namespace qsa

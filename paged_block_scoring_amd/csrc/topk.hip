@@ -24,8 +24,10 @@
 //  * A bitonic sort of the 64-bit composites in LDS yields rank order; block
 //    j is written as `expand` consecutive entries j*expand .. j*expand+expand-1
 //    (tokens) or as j (keys), and missing ranks as -1.
+#include "qsa.h"
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
+#include "qsa_select.hpp"
 
 namespace qsa {
 namespace {
@@ -185,6 +187,107 @@ __global__ __launch_bounds__(kNT) void topk_rows_kernel(TopkArgs A) {
     }
 }
 
+// Rows whose visible keys fit in registers (V <= kRegNT * EPT).  Every
+// score is loaded once, all loads issued before any use, and kept as its
+// order key (element e of thread t is key e*kRegNT + t).  One histogram level
+// over the row (kSelBins bins of a power-of-two width between its smallest
+// and largest key) finds the bin holding the kk-th largest; the keys from that
+// bin's lower edge up -- usually a few more than kk -- are compacted into LDS,
+// and select_from_bound (qsa_select.hpp) ranks them exactly, usually with no
+// sort at all.  If more than kCompact keys survive (heavy ties or clustering
+// at the cut), the row is selected by select_exact_sorted instead, with keys
+// re-read from the score row at each level.
+constexpr int kRegNT = 512;
+
+// x, with the compiler unable to reuse an earlier expression built from it:
+// element indices e*kRegNT + tid are then formed where used instead of being
+// held in EPT registers across the kernel.
+__device__ __forceinline__ int fresh(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+constexpr int kCompact = 4096;
+
+template <int KBMAX>
+struct TopkRegsLds {
+    BoundSelectLds<KBMAX> s;
+    uint64_t c[kCompact];
+    int nc;
+};
+
+// The rare path of topk_regs_kernel, kept out of line so that its register
+// needs do not constrain the common path.
+template <int EPT, int KBMAX>
+__device__ __noinline__ void topk_row_exact_sorted(const uint32_t* srow, int V, int nsel, BoundSelectLds<KBMAX>* L,
+                                                   int32_t* orow, int expand, bool vec4) {
+    const int tid = threadIdx.x;
+    select_exact_sorted<kRegNT, EPT, KBMAX>(
+        [&](int e) {
+            const int j = e * kRegNT + tid;
+            return j < V ? order_key(__uint_as_float(srow[j])) : 0u;
+        },
+        [&](int e) { return (uint32_t)(e * kRegNT + tid); }, V, nsel, *L,
+        [&](int r, uint32_t j) { write_rank(orow, r, j, expand, vec4); });
+}
+
+template <int EPT, int KBMAX>
+__global__ __launch_bounds__(kRegNT) void topk_regs_kernel(TopkArgs A) {
+    __shared__ TopkRegsLds<KBMAX> L;
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int V = row_visible(A.vis, row);
+    const int nsel = min(A.kk, V);
+    int32_t* orow = A.out + (int64_t)row * A.out_len;
+    const bool vec4 = A.expand == 4 && (A.out_len & 3) == 0 && (reinterpret_cast<uintptr_t>(A.out) & 15) == 0;
+    const auto emit = [&](int r, uint32_t j) { write_rank(orow, r, j, A.expand, vec4); };
+    if (nsel > 0) {
+        const uint32_t* srow = reinterpret_cast<const uint32_t*>(A.scores + (int64_t)row * A.ld);
+        uint32_t k[EPT];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) k[e] = srow[min(e * kRegNT + tid, V - 1)];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e)  // keys past V become 0 (all-ones mask iff e*kRegNT + tid - V < 0)
+            k[e] = order_key(__uint_as_float(k[e])) & (uint32_t)((e * kRegNT + tid - V) >> 31);
+        if (tid == 0) L.nc = 0;
+        const auto key = [&](int e) { return k[e]; };
+        uint32_t mn, mx;
+        // keys past V are 0, so every slot takes part (no per-slot range tests)
+        constexpr int kAll = EPT * kRegNT;
+        block_minmax_u32<kRegNT, EPT>(key, kAll, &mn, &mx, &L.s.hs);
+        const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
+        int above, cnt;
+        const uint32_t b = hist_level32<kRegNT, EPT>(key, kAll, mn, shift1, 32, 0u, nsel, &L.s.hs, nullptr, &above, &cnt);
+        const uint32_t lo = mn + (b << shift1);
+        const int surv = above + cnt;  // keys >= lo (lo >= the smallest key > 0)
+        if (surv <= kCompact) {
+#pragma unroll
+            for (int e = 0; e < EPT; ++e)
+                if (k[e] >= lo) L.c[atomicAdd(&L.nc, 1)] = compose(k[e], (uint32_t)(e * kRegNT + fresh(tid)));
+            __syncthreads();
+            constexpr int E2 = kCompact / kRegNT;
+            uint32_t k2[E2], i2[E2];
+#pragma unroll
+            for (int e = 0; e < E2; ++e) {
+                const int p = e * kRegNT + tid;
+                const uint64_t c = p < surv ? L.c[p] : 0ull;
+                k2[e] = (uint32_t)(c >> 32);
+                i2[e] = composite_index(c);
+            }
+            select_from_bound<kRegNT, E2, KBMAX>(k2, [&](int e) { return i2[e]; }, surv, nsel, lo, L.s, emit);
+        } else {
+            topk_row_exact_sorted<EPT, KBMAX>(srow, V, nsel, &L.s, orow, A.expand, vec4);
+        }
+    }
+    for (int i = nsel * A.expand + tid; i < A.out_len; i += kRegNT) orow[i] = -1;
+}
+
+template <int EPT>
+void launch_regs(const TopkArgs& A, int32_t rows, hipStream_t stream) {
+    if (A.kk <= 1024)
+        topk_regs_kernel<EPT, 1024><<<dim3((unsigned)rows), kRegNT, 0, stream>>>(A);
+    else
+        topk_regs_kernel<EPT, QSA_MAX_SELECT><<<dim3((unsigned)rows), kRegNT, 0, stream>>>(A);
+}
+
 }  // namespace
 
 hipError_t launch_topk_rows(const float* scores, int64_t ld, const VisibleSource& vis, int32_t rows,
@@ -199,7 +302,12 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, const VisibleSource
     A.expand = expand;
     A.out_len = out_len;
     A.out = out;
-    topk_rows_kernel<<<dim3((unsigned)rows), kNT, 0, stream>>>(A);
+    if (vis.max_visible <= kRegNT * 16)
+        launch_regs<16>(A, rows, stream);
+    else if (vis.max_visible <= kRegNT * 96)
+        launch_regs<96>(A, rows, stream);
+    else
+        topk_rows_kernel<<<dim3((unsigned)rows), kNT, 0, stream>>>(A);
     return hipGetLastError();
 }
 

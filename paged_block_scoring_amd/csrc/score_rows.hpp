@@ -260,18 +260,30 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
         }
         cnt = 0;
     };
-    // cache slot of key j of request act (page id clamped into the cache)
-    auto slot_of = [&](int act, int j) {
-        const int32_t* ptrow = a.page_table + (int64_t)act * a.pt_stride;
-        const int lp = A.kpp_shift >= 0 ? (j >> A.kpp_shift) : j / a.kpp;
-        const int slot = j - lp * a.kpp;
-        const int pg = min(max(ptrow[lp], 0), a.num_pages - 1);
-        return (uint32_t)pg * (uint32_t)a.kpp + (uint32_t)slot;
-    };
     // the single-request case builds a piece's slot table while its rows load
     const bool one_req = a.num_reqs == 1;
+    // cache slot of every key of the piece (page ids clamped into the cache);
+    // all page ids are loaded before any is used (lanes past the piece in its
+    // last group reload its last key's page and write nothing)
     auto build_slots = [&](int act, int k0, int k1) {
-        for (int i = tid; i < k1 - k0; i += NT) s_slot[i] = slot_of(act, (k0 + i) * A.stride);
+        constexpr int U = kRowsPiece / NT;
+        const int n = k1 - k0;
+        if (n <= 0) return;
+        const int32_t* ptrow = a.page_table + (int64_t)act * a.pt_stride;
+        int32_t pg[U];
+        int sl[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u * NT >= n) break;
+            const int j = (k0 + min(tid + u * NT, n - 1)) * A.stride;
+            const int lp = A.kpp_shift >= 0 ? (j >> A.kpp_shift) : j / a.kpp;
+            sl[u] = j - lp * a.kpp;
+            pg[u] = ptrow[lp];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (tid + u * NT < n)
+                s_slot[tid + u * NT] = (uint32_t)min(max(pg[u], 0), a.num_pages - 1) * (uint32_t)a.kpp + (uint32_t)sl[u];
     };
 
     while (p < pend) {
@@ -476,10 +488,12 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
                 for (int s = 0; s < kSlices; ++s)
                     kf[s] = *reinterpret_cast<const half8*>(sk + lds_key_chunk(lane & 31, 2 * s + (lane >> 5)));
                 __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_setprio(1);
                 mfma_quarter_appends<0>(acc, kf, kf[0], kf[1], qa, pm, pacc, pkb, pad);
                 mfma_quarter_appends<1>(acc, kf, kf[2], kf[3], qa, pm, pacc, pkb, pad);
                 mfma_quarter_appends<2>(acc, kf, kf[4], kf[5], qa, pm, pacc, pkb, pad);
                 mfma_quarter_appends<3>(acc, kf, kf[6], kf[7], qa, pm, pacc, pkb, pad);
+                __builtin_amdgcn_s_setprio(0);
                 __builtin_amdgcn_sched_barrier(0);
                 stage_in(buf ^ 1, pf_wait);
 

@@ -62,10 +62,12 @@ __device__ __forceinline__ int32_t visible_keys(int32_t pos, int32_t cr, int32_t
 
 // Order-preserving map of a finite fp32 to uint32 (larger float -> larger
 // key); -0 is mapped with +0 so that the two tie, as IEEE compares them.
+// Adding +0 turns -0 into +0 and leaves every other finite value unchanged
+// (fp32 denormals are kept); then a negative value's bits are inverted and a
+// non-negative value's sign bit is set -- four VALU operations, no branch.
 __device__ __forceinline__ uint32_t order_key(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u << 1) == 0u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 // Inverse of order_key (for keys produced by it).

@@ -140,7 +140,7 @@ constexpr int kSelBits = 10;
 constexpr int kSelBins = 1 << kSelBits;
 
 struct HistScratch {
-    uint32_t hist[kSelBins];
+    uint32_t hist[kSelBins + 1];  // the last bin takes empty slots' counts and is never read
     uint32_t wmin[16], wmax[16];
     int wsum[16];
     int bin, above, cnt;
@@ -157,15 +157,16 @@ __device__ __forceinline__ int bit_length32(uint32_t x) { return x ? 32 - __clz(
 template <int NT, int EPT, class KeyF>
 __device__ __forceinline__ void block_minmax_u32(KeyF key, int nmax, uint32_t* mn, uint32_t* mx, HistScratch* s) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // a = min(key - 1) over all slots (kept in that form until the end): an
+    // empty slot (0) wraps to the largest value, so it never wins unless
+    // every slot is empty; max ignores empty slots too
     uint32_t a = 0xFFFFFFFFu, b = 0u;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
         if (e * NT >= nmax) continue;
         const uint32_t ke = key(e);
-        if (ke) {
-            a = min(a, ke);
-            b = max(b, ke);
-        }
+        a = min(a, ke - 1u);
+        b = max(b, ke);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -185,7 +186,7 @@ __device__ __forceinline__ void block_minmax_u32(KeyF key, int nmax, uint32_t* m
         b = max(b, s->wmax[w]);
     }
     __syncthreads();
-    *mn = b ? a : 0u;
+    *mn = b ? a + 1u : 0u;
     *mx = b;
 }
 
@@ -206,14 +207,24 @@ __device__ __forceinline__ uint32_t hist_level32(KeyF key, int nmax, uint32_t ba
     for (int i = t; i < kSelBins; i += NT) s->hist[i] = 0u;
     __syncthreads();
     const uint32_t dmask = pshift - shift >= 32 ? 0xFFFFFFFFu : ((1u << (pshift - shift)) - 1u);
+    if (pshift >= 32) {
+        // every key takes part (no branch): an empty slot lands in the guard bin
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-        if (e * NT >= nmax) continue;
-        const uint32_t ke = key(e);
-        if (!ke) continue;
-        const uint32_t d = ke - base;
-        if (pshift < 32 && (d >> pshift) != prefix) continue;
-        atomicAdd(&s->hist[(d >> shift) & dmask], 1u);
+        for (int e = 0; e < EPT; ++e) {
+            if (e * NT >= nmax) continue;
+            const uint32_t ke = key(e);
+            atomicAdd(&s->hist[ke ? (ke - base) >> shift : (uint32_t)kSelBins], 1u);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            if (e * NT >= nmax) continue;
+            const uint32_t ke = key(e);
+            if (!ke) continue;
+            const uint32_t d = ke - base;
+            if ((d >> pshift) != prefix) continue;
+            atomicAdd(&s->hist[(d >> shift) & dmask], 1u);
+        }
     }
     __syncthreads();
     // thread t owns bins kSelBins-1-BPT*t .. kSelBins-BPT*(t+1), high to low
@@ -370,8 +381,8 @@ __device__ __forceinline__ void select_from_bound(const uint32_t (&k)[EPT], IdxF
     const uint32_t mn = min(lo, mx);
     const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
 #pragma unroll
-    for (int e = 0; e < EPT; ++e)
-        if (e * NT < nmax && k[e]) atomicAdd(&hs.hist[(k[e] - mn) >> shift1], 1u);
+    for (int e = 0; e < EPT; ++e)  // (an empty slot lands in the guard bin)
+        if (e * NT < nmax) atomicAdd(&hs.hist[k[e] ? (k[e] - mn) >> shift1 : (uint32_t)kSelBins], 1u);
     __syncthreads();
     // thread t owns bins kSelBins-1-BPT*t .. (high to low)
     uint32_t cb[BPT];

@@ -245,17 +245,20 @@ __global__ __launch_bounds__(kRegNT) void topk_regs_kernel(TopkArgs A) {
 #pragma unroll
         for (int e = 0; e < EPT; ++e) k[e] = srow[min(e * kRegNT + tid, V - 1)];
 #pragma unroll
-        for (int e = 0; e < EPT; ++e)  // keys past V become 0 (all-ones mask iff e*kRegNT + tid - V < 0)
-            k[e] = order_key(__uint_as_float(k[e])) & (uint32_t)((e * kRegNT + tid - V) >> 31);
+        for (int e = 0; e < EPT; ++e) {  // keys past V become 0 (a per-lane test only in the slot V falls in)
+            const uint32_t ke = order_key(__uint_as_float(k[e]));
+            if ((e + 1) * kRegNT <= V)
+                k[e] = ke;
+            else
+                k[e] = e * kRegNT + tid < V ? ke : 0u;
+        }
         if (tid == 0) L.nc = 0;
         const auto key = [&](int e) { return k[e]; };
         uint32_t mn, mx;
-        // keys past V are 0, so every slot takes part (no per-slot range tests)
-        constexpr int kAll = EPT * kRegNT;
-        block_minmax_u32<kRegNT, EPT>(key, kAll, &mn, &mx, &L.s.hs);
+        block_minmax_u32<kRegNT, EPT>(key, V, &mn, &mx, &L.s.hs);  // (slots wholly past V skipped)
         const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
         int above, cnt;
-        const uint32_t b = hist_level32<kRegNT, EPT>(key, kAll, mn, shift1, 32, 0u, nsel, &L.s.hs, nullptr, &above, &cnt);
+        const uint32_t b = hist_level32<kRegNT, EPT>(key, V, mn, shift1, 32, 0u, nsel, &L.s.hs, nullptr, &above, &cnt);
         const uint32_t lo = mn + (b << shift1);
         const int surv = above + cnt;  // keys >= lo (lo >= the smallest key > 0)
         if (surv <= kCompact) {

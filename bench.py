@@ -40,6 +40,8 @@ WORKLOAD_TEXT = {
     "mixed": "mixed: 8 requests, contexts U{4k..131k}, ~1,500 rows, permuted 64-token pages, top-k 2,048",
     "decode": "decode: 256 requests x 1 row, contexts U{64k..184k}, permuted pages, 1% x8 outlier keys, top-k 2,048",
     "tiny": "tiny: 64 rows at positions 960..1023 of a 1,024-token request, top-k 64",
+    "long_1": "long_1: one 184,000-token request, one row at its last position, permuted pages, top-k 2,048",
+    "long_8": "long_8: eight 184,000-token requests x 1 row, permuted pages, top-k 2,048",
 }
 
 
@@ -51,7 +53,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
     ap.add_argument("--workload", default="kernel_shape",
-                    choices=["tiny", "kernel_shape", "tie_stress", "mixed", "decode"])
+                    choices=["tiny", "kernel_shape", "tie_stress", "mixed", "decode", "long_1", "long_8"])
     ap.add_argument("--path", choices=["two_pass", "fused"], default=None,
                     help="force one execution arm (default: the library's choice)")
     ap.add_argument("--copy-probe", type=int, default=0,

@@ -346,7 +346,7 @@ __global__ __launch_bounds__(kFinNT) void fused_select_kernel(FinalArgs A) {
         // every candidate's key is >= the threshold's
         select_from_bound<kFinNT, EPT, KBMAX>(
             k, [&](int e) { return idx[e]; }, n, nsel, tkey, L.f,
-            [&](int r, uint32_t j) { write_rank(orow, r, j, A.expand, vec4); });
+            [&](int r, uint64_t c) { write_rank(orow, r, composite_index(c), A.expand, vec4); });
     }
     for (int i = nsel * A.expand + tid; i < A.out_len; i += kFinNT) orow[i] = -1;
 }

@@ -312,8 +312,9 @@ struct BoundSelectLds {
 // Exact top-nsel of the nonzero keys key(e) (indices idx(e)), sorted: the
 // cut is found by a histogram descent over the keys, ties at the cut by a
 // second descent over the inverted indices of the keys equal to it; the
-// selected set is gathered into LDS and sorted (bitonic).  emit(r, index) is
-// called once for each rank r < nsel.  Contains barriers.
+// selected set is gathered into LDS and sorted (bitonic).  emit(r, c) is
+// called once for each rank r < nsel with that rank's composite c.  Contains
+// barriers.
 template <int NT, int EPT, int KBMAX, class KeyF, class IdxF, class EmitF>
 __device__ __forceinline__ void select_exact_sorted(KeyF key, IdxF idx, int nmax, int nsel, BoundSelectLds<KBMAX>& L,
                                                     EmitF emit) {
@@ -340,7 +341,7 @@ __device__ __forceinline__ void select_exact_sorted(KeyF key, IdxF idx, int nmax
     }
     __syncthreads();
     lds_sort_desc<NT>(L.a, nsel);
-    for (int r = tid; r < nsel; r += NT) emit(r, composite_index(L.a[r]));
+    for (int r = tid; r < nsel; r += NT) emit(r, L.a[r]);
 }
 
 // Exact top-nsel of register-resident keys with a known lower bound.
@@ -348,8 +349,8 @@ __device__ __forceinline__ void select_exact_sorted(KeyF key, IdxF idx, int nmax
 // Each of the NT threads holds EPT keys k[e] (element e*NT + threadIdx.x,
 // index idx(e)); 0 marks an empty slot, slots e with e*NT >= nmax are
 // skipped, and every nonempty key is >= lo.  nsel (>= 1) must not exceed the
-// number of nonempty keys, nor KBMAX.  emit(r, index) is called exactly once
-// for each rank r < nsel.
+// number of nonempty keys, nor KBMAX.  emit(r, c) is called exactly once for
+// each rank r < nsel, with that rank's composite c.
 //
 // Method: the keys are binned between lo and their maximum (kSelBins bins of
 // a power-of-two width); with start[bin] = keys in higher bins, every key of a
@@ -431,7 +432,7 @@ __device__ __forceinline__ void select_from_bound(const uint32_t (&k)[EPT], IdxF
             }
             int r = 0;
             for (int i = st; i < st + cn; ++i) r += L.a[i] > me ? 1 : 0;
-            if (st + r < nsel) emit(st + r, composite_index(me));
+            if (st + r < nsel) emit(st + r, me);
         }
         __syncthreads();
         slow = hs.flag != 0;

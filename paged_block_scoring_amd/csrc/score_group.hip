@@ -15,9 +15,9 @@
 // the cache (256 bytes per key, HBM-bound) and a tile would hold rows of 128
 // different requests.  Here every wave (a one-wave workgroup, so that waves
 // are dispatched and retired independently) works alone on an item = (window
-// of G consecutive rows, segment of about 1,024 keys starting on a page
-// boundary and spanning at most 64 pages), G chosen by the host from the rows
-// per request; a window whose rows belong to several requests is done in one
+// of G consecutive rows, segment of about 1,024 keys -- shorter, down to 256,
+// when there are few windows -- starting on a page boundary and spanning at
+// most 64 pages), G chosen by the host from the rows per request; a window whose rows belong to several requests is done in one
 // pass per request, as in the tiled scorer.  The page ids of a segment are
 // read once, one per lane, and handed to the key loads by lane shuffles.
 //
@@ -202,7 +202,9 @@ __global__ __launch_bounds__(kGroupNT, 2) void score_group_kernel(GroupArgs A) {
             for (int i = 0; i < kBufFloats / 256; ++i) {
                 const int f = 64 * i + lane;
                 const int row = f / q4n, q4 = f - row * q4n;
-                const int lim = __shfl(lim_c, row & 31, 64);
+                // the row's bound, and the item's end: a segment shorter than
+                // the buffer leaves the buffer's tail unwritten
+                const int lim = min(__shfl(lim_c, row & 31, 64), k1);
                 const int key = wbase + 4 * q4;
                 if (row < A.G && key < lim) {
                     const float4v v = *reinterpret_cast<const float4v*>(sb + row * rstride + 4 * q4);
@@ -289,6 +291,13 @@ hipError_t launch_score_group(const PagedArgs& a, float* out, int64_t ld, hipStr
     const int64_t L = 32 / gcd * a.kpp;
     int64_t nl = std::min<int64_t>(64 * (int64_t)a.kpp / L, kSeg / L);
     if (nl < 1) nl = 1;
+    // with few windows, shorter segments (down to 256 keys) spread the keys
+    // of a handful of rows over the compute units
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    while (nl > 1 && nl % 2 == 0 && L * (nl / 2) >= 256 &&
+           (int64_t)A.windows * ((a.max_visible + L * nl - 1) / (L * nl)) < 2 * (int64_t)cus)
+        nl /= 2;
     A.seg_len = (int32_t)(L * nl);
     A.nseg = (a.max_visible + A.seg_len - 1) / A.seg_len;
     const int64_t items = (int64_t)A.windows * A.nseg;

@@ -227,7 +227,7 @@ __device__ __noinline__ void topk_row_exact_sorted(const uint32_t* srow, int V, 
             return j < V ? order_key(__uint_as_float(srow[j])) : 0u;
         },
         [&](int e) { return (uint32_t)(e * kRegNT + tid); }, V, nsel, *L,
-        [&](int r, uint32_t j) { write_rank(orow, r, j, expand, vec4); });
+        [&](int r, uint64_t c) { write_rank(orow, r, composite_index(c), expand, vec4); });
 }
 
 template <int EPT, int KBMAX>
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kRegNT) void topk_regs_kernel(TopkArgs A) {
     const int nsel = min(A.kk, V);
     int32_t* orow = A.out + (int64_t)row * A.out_len;
     const bool vec4 = A.expand == 4 && (A.out_len & 3) == 0 && (reinterpret_cast<uintptr_t>(A.out) & 15) == 0;
-    const auto emit = [&](int r, uint32_t j) { write_rank(orow, r, j, A.expand, vec4); };
+    const auto emit = [&](int r, uint64_t c) { write_rank(orow, r, composite_index(c), A.expand, vec4); };
     if (nsel > 0) {
         const uint32_t* srow = reinterpret_cast<const uint32_t*>(A.scores + (int64_t)row * A.ld);
         uint32_t k[EPT];

@@ -331,6 +331,25 @@ def test_topk_rows_all_equal(oracle_mod):
     assert np.array_equal(out, oracle_mod.select_rows(sc, np.array([n, n], np.int32), k))
 
 
+@pytest.mark.parametrize("kind", ["gauss", "ints", "few_values"])
+def test_topk_rows_few_long(oracle_mod, kind):
+    """A few long rows: lengths at, around and between multiples of the
+    workgroup's 512 threads, rows shorter than k, an empty row, and tie-heavy
+    scores (crowded histogram bins)."""
+    rng = np.random.default_rng({"gauss": 61, "ints": 62, "few_values": 63}[kind])
+    rows, ld = 9, 60_000
+    if kind == "gauss":
+        sc = rng.standard_normal((rows, ld)).astype(np.float32)
+    elif kind == "ints":
+        sc = rng.integers(-3, 4, size=(rows, ld)).astype(np.float32)
+    else:
+        sc = rng.choice(np.array([-0.0, 0.0, 1.5, 7.0], np.float32), size=(rows, ld))
+    V = np.array([ld, 4096, 4097, 8192, 12_345, 300, 0, 59_999, 20_000], np.int32)
+    for k in (512, 1024, 37):
+        out = run_topk(sc, V, k, max_visible=ld)
+        assert np.array_equal(out, oracle_mod.select_rows(sc, V, k)), (kind, k)
+
+
 def test_topk_rows_visible_none(oracle_mod):
     rng = np.random.default_rng(53)
     sc = rng.standard_normal((7, 6000)).astype(np.float32)
@@ -383,6 +402,13 @@ def test_full_mixed(oracle_mod):
     starts = np.concatenate([[0], np.cumsum(np.bincount(w.row_req))])
     sample = list(starts[:-1]) + list(starts[1:] - 1)
     sampled_parity(oracle_mod, w, 0, False, sample, paths=(None, "two_pass"))
+
+
+@pytest.mark.parametrize("name", ["long_1", "long_8"])
+def test_full_long_few(oracle_mod, name):
+    """One and eight 184k-token requests with one row each."""
+    w = W.make(name)
+    sampled_parity(oracle_mod, w, 0, False, [0, w.rows - 1], paths=(None, "fused"))
 
 
 @pytest.mark.slow

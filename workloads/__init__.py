@@ -186,12 +186,26 @@ def decode(seed=4, integer=False, num_reqs=256, ctx_lo=65_536, ctx_hi=184_000, o
                  outlier_p=outlier_p, k=2048)
 
 
+def long_few(seed=5, integer=False, num_reqs=8, ctx=184_000, outlier_p=0.01):
+    """A small batch of long requests: ``num_reqs`` requests of ``ctx``
+    tokens with one row each at the last position (the decode row shape),
+    permuted pages, 1% of key vectors scaled by 8; top-k 2,048."""
+    rng = np.random.default_rng(seed)
+    ctxs = np.full(num_reqs, ctx, dtype=np.int64)
+    rows = np.ones(num_reqs, dtype=np.int64)
+    return build(f"long_{num_reqs}", rng, seed, ctxs, rows, permute_pages=True, integer=integer,
+                 outlier_p=outlier_p, k=2048)
+
+
 CONFIGS = {
     "tiny": tiny,
     "kernel_shape": kernel_shape,
     "tie_stress": tie_stress,
     "mixed": mixed,
     "decode": decode,
+    # small batches of 184k-token requests (one or eight rows)
+    "long_1": lambda **kw: long_few(num_reqs=1, **kw),
+    "long_8": lambda **kw: long_few(num_reqs=8, **kw),
 }
 
 

@@ -246,6 +246,44 @@ def test_edges(oracle_mod):
     full_parity(oracle_mod, one, 0, True, paths=PATHS)
 
 
+@pytest.mark.parametrize("name,path", [("kernel_shape_80", "fused"), ("decode_small", "two_pass"),
+                                       ("mixed_small", "fused_fallback")])
+def test_graph_capture(oracle_mod, name, path):
+    """The whole call captured in a HIP graph (the pages name graph capture as a
+    failure site of their cooperative selector): every replay, with eager work
+    and synchronisations between replays, equals the eager result."""
+    w = REDUCED[name](False)
+    d = to_dev(w)
+    mv = int(visible(oracle_mod, w).max())
+    need = Q.qsa_select_paged_tokens_workspace_size(w.rows, w.num_reqs, mv, w.compress_ratio, w.k)
+    with force_path(path):
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
+        call = lambda out: Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"],  # noqa: E731
+                                                     w.compress_ratio, w.k, row_req=d["row_req"],
+                                                     max_visible=mv, out=out, workspace=ws)
+        eager = torch.empty((w.rows, w.k), dtype=torch.int32, device=DEV)
+        call(eager)
+        torch.cuda.synchronize()
+        exp = eager.cpu().numpy()
+        out = torch.empty_like(eager)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call(out)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call(out)
+        for i in range(4):
+            out.fill_(-7)
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(out.cpu().numpy(), exp), (name, path, i)
+            call(eager)  # eager work on the same workspace between replays
+            torch.cuda.synchronize()
+            assert np.array_equal(eager.cpu().numpy(), exp), (name, path, i)
+
+
 def test_golden_fixture_on_gpu():
     from conftest import golden_arrays, load_golden
     g = load_golden("paged_ties_expand.json")

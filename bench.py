@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph (reported as graph_ms_per_step)")
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
     ap.add_argument("--workload", default="kernel_shape",
                     choices=["tiny", "kernel_shape", "tie_stress", "mixed", "decode", "long_1", "long_8"])
@@ -259,6 +261,19 @@ def main():
     # the timed region: exactly `steps` whole steps
     ms_step, wall = time_calls(step, args.steps, args.warmup, torch)
     path = Q.qsa_last_path()
+    graph_ms = None
+    if args.graph:
+        # the same step captured once in a HIP graph and replayed: what a
+        # caller with a fixed shape (decode) sees without host launch costs
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        graph_ms, _ = time_calls(g.replay, args.steps, args.warmup, torch)
     # per-kernel durations of the same launches (instrumented repeat)
     kms, ms_instrumented = kernel_times(step, args.steps, KERNELS[path], torch, Q)
 
@@ -311,6 +326,8 @@ def main():
         "roofline": roofline,
         "wall_s_timed": round(wall, 4),
     }
+    if graph_ms is not None:
+        result["graph_ms_per_step"] = round(graph_ms, 4)
 
     if args.copy_probe > 0:
         n = args.copy_probe * (1 << 20)

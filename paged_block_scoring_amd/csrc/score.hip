@@ -1,6 +1,7 @@
-// score.hip -- launchers of the tiled scoring kernel (score_core.hpp): the
-// materialising scorer behind qsa_score_paged and the two-pass arm, the
-// strided sampling pass and the filtering pass of the fused arm.
+// score.hip -- launchers of the tiled scorers (score_rows.hpp for the default
+// form, score_core.hpp for the relu form): the materialising scorer behind
+// qsa_score_paged and the two-pass arm, the strided sampling pass and the
+// filtering pass of the fused arm.
 #include <stdlib.h>
 #include <string.h>
 
@@ -10,22 +11,22 @@
 namespace qsa {
 namespace {
 
-// Even shares of each XCD's (tile, key) positions, in whole stages: about
-// the form's resident workgroups per compute unit, but no share below
-// `min_seg` positions.
-template <bool RELU, Epi EPI>
-hipError_t launch_form(ScoreKernelArgs A, int32_t cus, int64_t min_seg, hipStream_t stream) {
-    constexpr int64_t g = Stage<RELU>::STEP;
-    A.tiles = (A.a.rows + Form<RELU>::TILE - 1) / Form<RELU>::TILE;
+// Relu form: the tiled scorer of score_core.hpp.  Even shares of each XCD's
+// (tile, key) positions, in whole stages: about the form's resident
+// workgroups per compute unit, but no share below `min_seg` positions.
+template <Epi EPI>
+hipError_t launch_relu(ScoreKernelArgs A, int32_t cus, int64_t min_seg, hipStream_t stream) {
+    constexpr int64_t g = ReluForm::STEP;
+    A.tiles = (A.a.rows + ReluForm::TILE - 1) / ReluForm::TILE;
     const int64_t stripe = ((int64_t)(A.lmax + kXcds - 1) / kXcds + g - 1) / g * g;
     A.xcd_keys = (int32_t)stripe;
     const int64_t positions = (int64_t)A.tiles * stripe;
-    int64_t per_xcd = (int64_t)(cus / kXcds > 0 ? cus / kXcds : 1) * Form<RELU>::WG_PER_CU;
+    int64_t per_xcd = (int64_t)(cus / kXcds > 0 ? cus / kXcds : 1) * ReluForm::WG_PER_CU;
     int64_t seg = ((positions + per_xcd - 1) / per_xcd + g - 1) / g * g;
     if (seg < min_seg) seg = (min_seg + g - 1) / g * g;
     per_xcd = (positions + seg - 1) / seg;
     A.seg_len = seg;
-    score_tiles_kernel<RELU, EPI><<<dim3((unsigned)(kXcds * per_xcd)), ScoreShape::NT, 0, stream>>>(A);
+    score_tiles_kernel<EPI><<<dim3((unsigned)(kXcds * per_xcd)), ScoreShape::NT, 0, stream>>>(A);
     return hipGetLastError();
 }
 
@@ -63,7 +64,7 @@ hipError_t launch_rows(const ScoreKernelArgs& K, int32_t cus, int64_t min_seg, h
 
 template <Epi EPI>
 hipError_t launch_epi(const ScoreKernelArgs& A, int32_t cus, hipStream_t stream) {
-    if (A.a.relu) return launch_form<true, EPI>(A, cus, 64, stream);
+    if (A.a.relu) return launch_relu<EPI>(A, cus, 64, stream);
     return launch_rows<EPI>(A, cus, 64, stream);
 }
 

@@ -1,47 +1,43 @@
-// score_core.hpp -- the tiled paged MQA scoring kernel shared by every arm.
+// score_core.hpp -- the tiled paged scorer of the relu form (QSA_SCORE_RELU:
+// per-head dots, each through relu, summed, times the fp32 value nearest
+// 1/sqrt(128)); the default form has its own kernel in score_rows.hpp.
 //
 // Sources: "[Perf][Qwen4Exp] Admit the cuBLAS QSA indexer and exact top-k on
 // Turing", sections "Purpose" (FP16 product with FP32 accumulation and an
 // epilogue; a paged scorer reading keys through the page table) and "Test
 // Plan" (4 index heads, head dim 128, compress ratio 4); "spec(MODEL-MM-QWEN4-
 // EXP) ...", section "The component deep-dives, and two corrections to the
-// above" (one key per ratio tokens shared by all heads; one score per query
-// token summed over heads).
+// above" (one key per ratio tokens shared by all heads; relu per head and the
+// 1/sqrt(head_dim) scale).
 //
-// Work.  Rows are cut into tiles of consecutive rows (128 in the default
-// form, 64 in the relu form: 4 waves of 32 or 16 rows); the logical keys
-// (logical key i is key stride*i of the request; stride is 1 except for the
-// sampling pass) are cut into 8 stripes, one per XCD.  Workgroup w runs on
-// XCD w % 8 (the hardware's round-robin dispatch) and owns a contiguous,
-// equal share of that XCD's (tile, key) positions, so every XCD streams only
-// its stripe of keys (which stays in its L2) and every workgroup does the
-// same amount of work.  A share is processed as pieces of one tile and at
-// most kMaxPiece keys.
+// Work.  Rows are cut into tiles of 64 consecutive rows (4 waves of 16); the
+// logical keys (logical key i is key stride*i of the request; stride is 1
+// except for the sampling pass) are cut into 8 stripes, one per XCD.
+// Workgroup w runs on XCD w % 8 (the hardware's round-robin dispatch) and
+// owns a contiguous, equal share of that XCD's (tile, key) positions, so every
+// XCD streams only its stripe of keys (which stays in its L2) and every
+// workgroup does the same amount of work.  A share is processed as pieces of
+// one tile and at most kMaxPiece keys.
 //
 // A piece.  Each of the 4 waves holds the fp16 query fragments of its rows
-// in registers (loaded once per tile).  Keys are staged 64 at a time: a
+// in registers (loaded once per tile): MFMA row m = 4*row + head, 8 rows x 4
+// heads per MFMA tile, two tiles per wave.  Keys are staged 64 at a time: a
 // per-piece table gives every logical key's slot in the cache; each thread
 // prefetches its 16-byte pieces of the next 64 keys into registers while the
 // current ones are consumed from one half of a double-buffered, XOR-swizzled
 // LDS tile (one barrier per 64 keys = two 32-key MFMA column tiles, whose
-// MFMA chains are interleaved).  The MFMA arrangements are the canonical ones
-// of qsa_device.hpp.
+// MFMA chains are interleaved).  The MFMA arrangement is the canonical one of
+// qsa_device.hpp.
 //
-// Epilogue.  Each lane ends a 32-key column tile holding scores of a single
-// row:
-//   default form -- the MFMA produces the key x row tile, so lane l holds
-//     row l%32 of the wave and 16 consecutive keys;
-//   relu form -- the head-combined scores are spread over rows, so the wave
-//     transposes them through a small LDS buffer of its own until lane l
-//     holds row l/4 and 8 consecutive keys.
-// Then
+// Epilogue.  The head-combined scores of a 32-key column tile are spread over
+// rows, so the wave transposes them through a small LDS buffer of its own
+// until lane l holds row l/4 and 8 consecutive keys.  Then
 //   Store  -- out[row*ld + i] = score with 16-byte stores (two-pass arm,
-//             sampling pass); the default form first transposes through LDS
-//             so that each store instruction writes whole 128-byte row runs;
+//             sampling pass);
 //   Filter -- keep (score, key) if score >= the row's threshold score: one
 //             compare per score against a per-lane threshold; a prefix sum
-//             over the row's lanes gives each kept entry its slot in the
-//             row's LDS staging list (score bits, key), which the wave moves
+//             over the row's 4 lanes gives each kept entry its slot in the
+//             row's LDS staging list (score bits, key), which the lanes move
 //             to the row's global list -- one atomic per row -- when it would
 //             overflow and when the workgroup leaves the tile.
 // Rows of different requests in one tile are processed in successive passes.
@@ -81,52 +77,22 @@ struct ScoreShape {
     static constexpr int NT = 64 * WAVES;
 };
 
-// The two MFMA arrangements (qsa_device.hpp) as seen by the tiled kernel.
-template <bool RELU>
-struct Form;
-// default form: head sum in K, keys as the MFMA rows and the wave's 32
-// query rows as its columns.  Lane l's accumulator element v is MFMA row
-// 8*(v/4) + 4*(l/32) + v%4; the stage keeps key sigma(m) = 16*((m/4)%2) +
-// 4*(m/8) + m%4 of each 32-key column tile in LDS row m, so that element v is
-// key 16*(l/32) + v: every lane holds 16 consecutive keys of row l%32.
-template <>
-struct Form<false> {
-    static constexpr int RPW = 32;                 // rows per wave
+// The relu form's MFMA arrangement (qsa_device.hpp) as seen by the tiled
+// kernel: heads in M, two MFMA tiles of 8 rows x 4 heads per wave; the
+// head-combined outputs o = 4*mt + g are rows 8*mt + 2*g (+1 for lane half
+// 1), transposed to lane l = row l/4, keys 8*(l%4) .. 8*(l%4)+7.
+struct ReluForm {
+    static constexpr int RPW = 16;                 // rows per wave
     static constexpr int TILE = 4 * RPW;           // rows per tile
-    static constexpr int NQ = 2 * kSlices;         // query fragments per lane: (slice, hi/lo)
-    static constexpr int SUB = 1;                  // 32-key column tiles per LDS stage
+    static constexpr int NQ = 2 * kSlices;         // query fragments per lane: (MFMA tile, slice)
+    static constexpr int SUB = 2;                  // 32-key column tiles per LDS stage
+    static constexpr int STEP = 32 * SUB;          // keys per LDS stage
+    static constexpr int NLOAD = STEP * kChunksPerKey / ScoreShape::NT;  // 16-byte pieces per thread per stage
     static constexpr int MAXPIECE = 1024;          // logical keys per piece (slot-table size)
     static constexpr int WG_PER_CU = 2;            // resident workgroups per compute unit
-    __device__ static int lane_row(int lane) { return lane & 31; }
-    // LDS row of key n of a stage (the inverse of sigma within each column tile)
-    __device__ static int stage_row(int n) {
-        const int k = n & 31;
-        return (n & ~31) | (8 * ((k >> 2) & 3) + 4 * (k >> 4) + (k & 3));
-    }
-};
-// relu form: heads in M, two MFMA tiles of 8 rows x 4 heads per wave; the
-// head-combined outputs o = 4*mt + g are rows 8*mt + 2*g (+1 for lane half
-// 1), transposed to lane l = row l/4, keys 8*(l%4) .. 8*(l%4)+7
-template <>
-struct Form<true> {
-    static constexpr int RPW = 16;
-    static constexpr int TILE = 4 * RPW;
-    static constexpr int NQ = 2 * kSlices;
-    static constexpr int SUB = 2;
-    static constexpr int MAXPIECE = 1024;
-    static constexpr int WG_PER_CU = 2;
+    static_assert(NLOAD * ScoreShape::NT == STEP * kChunksPerKey, "whole keys per thread");
     __device__ static constexpr int out_row(int o) { return 8 * (o >> 2) + 2 * (o & 3); }
     __device__ static int lane_row(int lane) { return lane >> 2; }
-    __device__ static int stage_row(int n) { return n; }
-};
-
-// Stage geometry of a form: STEP keys per LDS stage, NLOAD 16-byte pieces
-// (consecutive keys) per thread per stage.
-template <bool RELU>
-struct Stage {
-    static constexpr int STEP = 32 * Form<RELU>::SUB;
-    static constexpr int NLOAD = STEP * kChunksPerKey / ScoreShape::NT;
-    static_assert(NLOAD * ScoreShape::NT == STEP * kChunksPerKey, "whole keys per thread");
 };
 
 // Quad (lanes 4k..4k+3) exclusive prefix sum of x; *total gets the quad sum.
@@ -162,19 +128,18 @@ __device__ __forceinline__ uint64_t cand_entry(float score, int key) {
     return ((uint64_t)__float_as_uint(score) << 32) | (uint32_t)key;
 }
 
-template <bool RELU, Epi EPI>
-__global__ __launch_bounds__(ScoreShape::NT, Form<RELU>::WG_PER_CU) void score_tiles_kernel(ScoreKernelArgs A) {
-    using F = Form<RELU>;
+template <Epi EPI>
+__global__ __launch_bounds__(ScoreShape::NT, ReluForm::WG_PER_CU) void score_tiles_kernel(ScoreKernelArgs A) {
+    using F = ReluForm;
     constexpr int NT = ScoreShape::NT, TILE = F::TILE, RPW = F::RPW;
-    constexpr int kSub = F::SUB, kStepKeys = Stage<RELU>::STEP, NLOAD = Stage<RELU>::NLOAD;
+    constexpr int kSub = F::SUB, kStepKeys = F::STEP, NLOAD = F::NLOAD;
     constexpr int kMaxPiece = F::MAXPIECE;
     constexpr bool FILTER = EPI == Epi::Filter;
 
     __shared__ __attribute__((aligned(16))) unsigned char s_keys[2][kStepKeys * kKeyBytes];
     __shared__ __attribute__((aligned(16))) uint32_t s_slot[kMaxPiece];
-    // per-wave transpose buffer: relu form (16 rows), default-form Store (32 rows)
-    constexpr int TR_ROWS = RELU ? 16 : (FILTER ? 0 : 32);
-    __shared__ __attribute__((aligned(16))) float s_tr[TR_ROWS ? ScoreShape::WAVES : 1][TR_ROWS ? TR_ROWS * kTrStride : 4];
+    // per-wave transpose buffer (16 rows)
+    __shared__ __attribute__((aligned(16))) float s_tr[ScoreShape::WAVES][RPW * kTrStride];
     __shared__ int32_t s_req[TILE], s_lv[TILE], s_todo[TILE], s_lim[TILE];
     __shared__ float s_fT[FILTER ? TILE : 1];
     __shared__ uint64_t s_lbuf[FILTER ? TILE * kLCap : 1];
@@ -196,9 +161,8 @@ __global__ __launch_bounds__(ScoreShape::NT, Form<RELU>::WG_PER_CU) void score_t
     const int pk = NLOAD * (tid >> 4), pc = tid & 15;
     // epilogue: the tile row this lane works on, and its lane group
     const int erow = wave * RPW + F::lane_row(lane);
-    const int g_leader = RELU ? (lane & ~3) : (lane & 31);
-    const int g_member = RELU ? (lane & 3) : (lane >> 5);
-    constexpr int g_size = RELU ? 4 : 2;
+    const int g_leader = lane & ~3, g_member = lane & 3;
+    constexpr int g_size = 4;
 
     // every slot-table entry always holds a valid cache slot, so the prefetch
     // may read entries past the end of a pass's table
@@ -240,34 +204,17 @@ __global__ __launch_bounds__(ScoreShape::NT, Form<RELU>::WG_PER_CU) void score_t
             if (FILTER && new_tile) s_fT[t] = req >= 0 ? key_to_float((uint32_t)(A.thresh[r] >> 32)) : 0.0f;
         }
         if (new_tile) {
-            // query fragments of this wave's rows
-            if (RELU) {
+            // query fragments of this wave's rows (A operand: MFMA tile t/8
+            // rows 8*(t/8) + m/4, head m%4; slice t%8)
 #pragma unroll
-                for (int t = 0; t < F::NQ; ++t) {
-                    // A operand: MFMA tile t/8 rows 8*(t/8) + m/4, head m%4; slice t%8
-                    const int m = lane & 31;
-                    const int row = r0 + wave * RPW + (t / kSlices) * 8 + (m >> 2);
-                    half8 v = {};
-                    if (row < a.rows)
-                        v = *reinterpret_cast<const half8*>(a.q + ((int64_t)row * kHeads + (m & 3)) * kHeadDim +
-                                                            16 * (t % kSlices) + 8 * (lane >> 5));
-                    qa[t] = v;
-                }
-            } else {
-                // B operand: column m = row m; step t = (slice t/2, hi/lo t%2)
-                const int row = r0 + wave * RPW + (lane & 31);
-#pragma unroll
-                for (int s = 0; s < kSlices; ++s) {
-                    half8 h[kHeads];
-#pragma unroll
-                    for (int hh = 0; hh < kHeads; ++hh) {
-                        h[hh] = half8{};
-                        if (row < a.rows)
-                            h[hh] = *reinterpret_cast<const half8*>(a.q + ((int64_t)row * kHeads + hh) * kHeadDim +
-                                                                    16 * s + 8 * (lane >> 5));
-                    }
-                    head_sum_split(h[0], h[1], h[2], h[3], qa[2 * s], qa[2 * s + 1]);
-                }
+            for (int t = 0; t < F::NQ; ++t) {
+                const int m = lane & 31;
+                const int row = r0 + wave * RPW + (t / kSlices) * 8 + (m >> 2);
+                half8 v = {};
+                if (row < a.rows)
+                    v = *reinterpret_cast<const half8*>(a.q + ((int64_t)row * kHeads + (m & 3)) * kHeadDim +
+                                                        16 * (t % kSlices) + 8 * (lane >> 5));
+                qa[t] = v;
             }
         }
         __syncthreads();
@@ -342,7 +289,7 @@ __global__ __launch_bounds__(ScoreShape::NT, Form<RELU>::WG_PER_CU) void score_t
             auto stage_in = [&](int b, const u32x4 (&pf)[NLOAD]) {
 #pragma unroll
                 for (int i = 0; i < NLOAD; ++i)
-                    *reinterpret_cast<u32x4*>(s_keys[b] + lds_key_chunk(F::stage_row(pk + i), pc)) = pf[i];
+                    *reinterpret_cast<u32x4*>(s_keys[b] + lds_key_chunk(pk + i, pc)) = pf[i];
             };
             u32x4 pfA[NLOAD], pfB[NLOAD];
             issue(slots_of(0), pfA);
@@ -360,180 +307,80 @@ __global__ __launch_bounds__(ScoreShape::NT, Form<RELU>::WG_PER_CU) void score_t
                 // keep the prefetch issued here, ahead of the MFMAs that hide it
                 __builtin_amdgcn_sched_barrier(0);
 
-                if (RELU) {
-                    float16v acc[kSub][2];
+                float16v acc[kSub][2];
 #pragma unroll
-                    for (int st = 0; st < kSub; ++st) acc[st][0] = acc[st][1] = float16v{};
+                for (int st = 0; st < kSub; ++st) acc[st][0] = acc[st][1] = float16v{};
 #pragma unroll
-                    for (int s = 0; s < kSlices; ++s) {
-                        half8 kbs[kSub];
+                for (int s = 0; s < kSlices; ++s) {
+                    half8 kbs[kSub];
+#pragma unroll
+                    for (int st = 0; st < kSub; ++st)
+                        kbs[st] = *reinterpret_cast<const half8*>(
+                            sk + lds_key_chunk(32 * st + (lane & 31), 2 * s + (lane >> 5)));
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                         for (int st = 0; st < kSub; ++st)
-                            kbs[st] = *reinterpret_cast<const half8*>(
-                                sk + lds_key_chunk(32 * st + (lane & 31), 2 * s + (lane >> 5)));
+                            acc[st][mt] = mfma32(qa[mt * kSlices + s], kbs[st], acc[st][mt]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                float sc[kSub][8];
 #pragma unroll
-                        for (int mt = 0; mt < 2; ++mt)
+                for (int st = 0; st < kSub; ++st)
 #pragma unroll
-                            for (int st = 0; st < kSub; ++st)
-                                acc[st][mt] = mfma32(qa[mt * kSlices + s], kbs[st], acc[st][mt]);
+                    for (int o = 0; o < 8; ++o) {
+                        const int mt = o >> 2, g = o & 3;
+                        sc[st][o] = combine_relu_heads(acc[st][mt][4 * g], acc[st][mt][4 * g + 1],
+                                                       acc[st][mt][4 * g + 2], acc[st][mt][4 * g + 3]);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
-                    float sc[kSub][8];
-#pragma unroll
-                    for (int st = 0; st < kSub; ++st)
-#pragma unroll
-                        for (int o = 0; o < 8; ++o) {
-                            const int mt = o >> 2, g = o & 3;
-                            sc[st][o] = combine_relu_heads(acc[st][mt][4 * g], acc[st][mt][4 * g + 1],
-                                                           acc[st][mt][4 * g + 2], acc[st][mt][4 * g + 3]);
-                        }
-                    // stage the prefetched tile in the idle buffer (after the
-                    // last step this fills a buffer no wave reads any more:
-                    // every wave has passed this step's barrier)
-                    stage_in(buf ^ 1, pf_wait);
+                // stage the prefetched tile in the idle buffer (after the
+                // last step this fills a buffer no wave reads any more:
+                // every wave has passed this step's barrier)
+                stage_in(buf ^ 1, pf_wait);
 
-                    float* const tw = s_tr[wave];
-                    const int rr = lane >> 2, cq = lane & 3;
+                float* const tw = s_tr[wave];
+                const int rr = lane >> 2, cq = lane & 3;
 #pragma unroll
-                    for (int st = 0; st < kSub; ++st) {
-                        // transpose: lane (row rr, keys 8cq..8cq+7) of this column tile
+                for (int st = 0; st < kSub; ++st) {
+                    // transpose: lane (row rr, keys 8cq..8cq+7) of this column tile
 #pragma unroll
-                        for (int o = 0; o < 8; ++o)
-                            tw[(Form<true>::out_row(o) + (lane >> 5)) * kTrStride + (lane & 31)] = sc[st][o];
-                        __builtin_amdgcn_wave_barrier();
-                        const float4v v0 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq);
-                        const float4v v1 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq + 4);
-                        __builtin_amdgcn_wave_barrier();
-                        const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                        const int key0 = j0 + 32 * st + 8 * cq;
-                        const bool full = j0 + 32 * (st + 1) <= wlim;
-                        if (!FILTER) {
-                            float* dst = A.out + (int64_t)(r0 + erow) * A.ld + key0;
-                            if (full && A.vec_store) {
-                                *reinterpret_cast<float4v*>(dst) = v0;
-                                *reinterpret_cast<float4v*>(dst + 4) = v1;
-                            } else {
-#pragma unroll
-                                for (int i = 0; i < 8; ++i)
-                                    if (full || key0 + i < lim_r) dst[i] = v[i];
-                            }
+                    for (int o = 0; o < 8; ++o)
+                        tw[(F::out_row(o) + (lane >> 5)) * kTrStride + (lane & 31)] = sc[st][o];
+                    __builtin_amdgcn_wave_barrier();
+                    const float4v v0 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq);
+                    const float4v v1 = *reinterpret_cast<const float4v*>(tw + rr * kTrStride + 8 * cq + 4);
+                    __builtin_amdgcn_wave_barrier();
+                    const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    const int key0 = j0 + 32 * st + 8 * cq;
+                    const bool full = j0 + 32 * (st + 1) <= wlim;
+                    if (!FILTER) {
+                        float* dst = A.out + (int64_t)(r0 + erow) * A.ld + key0;
+                        if (full && A.vec_store) {
+                            *reinterpret_cast<float4v*>(dst) = v0;
+                            *reinterpret_cast<float4v*>(dst + 4) = v1;
                         } else {
-                            bool kp[8];
-                            int n = 0;
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) {
-                                kp[i] = v[i] >= fT_r && (full || key0 + i < lim_r);
-                                n += kp[i] ? 1 : 0;
-                            }
-                            int tot;
-                            const int excl = quad_exclusive_sum(n, &tot);
-                            uint64_t* lb = s_lbuf + erow * kLCap;
-                            if (__any(cnt_r + tot > kLCap))
-                                flush_staged(A, lb, r0 + erow, cnt_r, g_leader, g_member, g_size);
-                            int slot = cnt_r + excl;
 #pragma unroll
                             for (int i = 0; i < 8; ++i)
-                                if (kp[i]) lb[slot++] = cand_entry(v[i], key0 + i);
-                            cnt_r += tot;
+                                if (full || key0 + i < lim_r) dst[i] = v[i];
                         }
-                    }
-                } else {
-                    // every key fragment of the stage is read before the chain starts
-                    half8 kbs[kSub][kSlices];
+                    } else {
+                        bool kp[8];
+                        int n = 0;
 #pragma unroll
-                    for (int st = 0; st < kSub; ++st)
-#pragma unroll
-                        for (int s = 0; s < kSlices; ++s)
-                            kbs[st][s] = *reinterpret_cast<const half8*>(
-                                sk + lds_key_chunk(32 * st + (lane & 31), 2 * s + (lane >> 5)));
-                    __builtin_amdgcn_sched_barrier(0);
-                    float16v acc[kSub];
-#pragma unroll
-                    for (int st = 0; st < kSub; ++st) acc[st] = float16v{};
-#pragma unroll
-                    for (int s = 0; s < kSlices; ++s)
-#pragma unroll
-                        for (int t = 2 * s; t < 2 * s + 2; ++t)
-#pragma unroll
-                            for (int st = 0; st < kSub; ++st) acc[st] = mfma32(kbs[st][s], qa[t], acc[st]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    // stage the prefetched tile in the idle buffer (see above)
-                    stage_in(buf ^ 1, pf_wait);
-
-#pragma unroll
-                    for (int st = 0; st < kSub; ++st) {
-                        // element v: key kb + v of row erow
-                        const int kb = j0 + 32 * st + 16 * (lane >> 5);
-                        const bool full = j0 + 32 * (st + 1) <= wlim;
-                        if (!FILTER) {
-                            // transpose through LDS so that 8 consecutive lanes store
-                            // 32 consecutive keys (128 bytes) of one row: lane l then
-                            // holds keys 4*(l%8) .. +3 of rows l/8 + 8i, i = 0..3
-                            float* const tw = s_tr[wave];
-#pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                *reinterpret_cast<float4v*>(tw + (lane & 31) * kTrStride + 16 * (lane >> 5) + 4 * j) =
-                                    float4v{acc[st][4 * j], acc[st][4 * j + 1], acc[st][4 * j + 2], acc[st][4 * j + 3]};
-                            __builtin_amdgcn_wave_barrier();
-                            float4v w[4];
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                w[i] = *reinterpret_cast<const float4v*>(tw + ((lane >> 3) + 8 * i) * kTrStride + 4 * (lane & 7));
-                            __builtin_amdgcn_wave_barrier();
-                            const int key0 = j0 + 32 * st + 4 * (lane & 7);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int trow = wave * RPW + (lane >> 3) + 8 * i;
-                                float* dst = A.out + (int64_t)(r0 + trow) * A.ld + key0;
-                                if (full && A.vec_store) {
-                                    *reinterpret_cast<float4v*>(dst) = w[i];
-                                } else {
-                                    const int lim = s_lim[trow];
-#pragma unroll
-                                    for (int e = 0; e < 4; ++e)
-                                        if (full || key0 + e < lim) dst[e] = w[i][e];
-                                }
-                            }
-                        } else {
-                            // element v (key kb + v) is kept if it reaches the threshold (and,
-                            // on a column tile that crosses a bound, is visible); the full and
-                            // the bounded tile each get their own straight-line code
-                            const int nv = full ? 16 : min(max(lim_r - kb, 0), 16);
-                            int n = 0;
-                            if (full) {
-#pragma unroll
-                                for (int v = 0; v < 16; ++v) n += acc[st][v] >= fT_r ? 1 : 0;
-                            } else {
-#pragma unroll
-                                for (int v = 0; v < 16; ++v) n += (acc[st][v] >= fT_r && v < nv) ? 1 : 0;
-                            }
-                            // the row's two lanes (l and l ^ 32) hold keys kb..kb+15 and kb+16..kb+31
-                            const auto nn = __builtin_amdgcn_permlane32_swap(n, n, false, false);
-                            const int n_lo = (int)nn[0], tot = (int)nn[0] + (int)nn[1];
-                            uint64_t* lb = s_lbuf + erow * kLCap;
-                            if (__any(cnt_r + tot > kLCap))
-                                flush_staged(A, lb, r0 + erow, cnt_r, g_leader, g_member, g_size);
-                            // entries as (key, score bits) word pairs
-                            uint32_t* lw = reinterpret_cast<uint32_t*>(lb) + 2 * (cnt_r + ((lane >> 5) ? n_lo : 0));
-                            if (full) {
-#pragma unroll
-                                for (int v = 0; v < 16; ++v)
-                                    if (acc[st][v] >= fT_r) {
-                                        lw[0] = (uint32_t)(kb + v);
-                                        lw[1] = __float_as_uint(acc[st][v]);
-                                        lw += 2;
-                                    }
-                            } else {
-#pragma unroll
-                                for (int v = 0; v < 16; ++v)
-                                    if (acc[st][v] >= fT_r && v < nv) {
-                                        lw[0] = (uint32_t)(kb + v);
-                                        lw[1] = __float_as_uint(acc[st][v]);
-                                        lw += 2;
-                                    }
-                            }
-                            cnt_r += tot;
+                        for (int i = 0; i < 8; ++i) {
+                            kp[i] = v[i] >= fT_r && (full || key0 + i < lim_r);
+                            n += kp[i] ? 1 : 0;
                         }
+                        int tot;
+                        const int excl = quad_exclusive_sum(n, &tot);
+                        uint64_t* lb = s_lbuf + erow * kLCap;
+                        if (__any(cnt_r + tot > kLCap))
+                            flush_staged(A, lb, r0 + erow, cnt_r, g_leader, g_member, g_size);
+                        int slot = cnt_r + excl;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            if (kp[i]) lb[slot++] = cand_entry(v[i], key0 + i);
+                        cnt_r += tot;
                     }
                 }
             };

@@ -181,6 +181,39 @@ qsa_status qsa_select_paged_tokens(const void* q, const void* kcache, const int3
 size_t qsa_select_paged_tokens_workspace_size(int32_t rows, int32_t num_reqs, int32_t max_visible,
                                               int32_t compress_ratio, int32_t k, uint32_t flags);
 
+/*
+ * qsa_sparse_attention -- the consumer of the selection ([spec] op survey:
+ * plain GQA, 24 query heads over 2 KV heads, head_dim 256; [spec] "The
+ * component deep-dives, and two corrections to the above": the consumer
+ * attends to the raw tokens the indexer selected).  For every row r and query
+ * head h: out[r][h] = sum_t softmax_t(scale * q[r][h] . K[t]) V[t] over the
+ * tokens t listed in tokens[r], K and V of KV head h / (q_heads / kv_heads).
+ *
+ *  q            device fp16 [rows][q_heads][head_dim].
+ *  k_cache      device fp16 [num_pages][page_size][kv_heads][head_dim]: token t
+ *               of request q is slot t % page_size of page
+ *               page_table[q][t / page_size].
+ *  v_cache      device fp16, the same layout.
+ *  page_table, pt_stride, num_pages, num_reqs, row_req   as for
+ *               qsa_score_paged (row_req NULL: every row is request 0).
+ *  tokens       device int32 [rows][k]: logical token positions (for example
+ *               the output of qsa_select_paged_tokens); entries < 0 are
+ *               skipped.  Positions past the page table and page ids outside
+ *               [0, num_pages) are clamped (never an out-of-bounds access).
+ *  scale        softmax scale, e.g. 1/sqrt(head_dim).
+ *  out          device fp32 [rows][q_heads][head_dim]; a row with no token
+ *               gets zeros.
+ *  Supported: head_dim == 256, q_heads a multiple of kv_heads with at most 16
+ *  query heads per KV head, num_pages * page_size * kv_heads < 2^32.
+ *  No workspace; asynchronous on `stream`.
+ */
+qsa_status qsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* page_table, int64_t pt_stride, int32_t num_pages,
+                                int32_t num_reqs, const int32_t* row_req, const int32_t* tokens,
+                                int32_t k, int32_t rows, int32_t q_heads, int32_t kv_heads,
+                                int32_t head_dim, int32_t page_size, float scale, float* out,
+                                void* stream);
+
 /* Description of the last failure on the calling thread, "file:line: message"
  * ("" if none).  The pointer stays valid until the thread's next library call. */
 const char* qsa_last_error(void);

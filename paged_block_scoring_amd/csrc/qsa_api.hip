@@ -9,6 +9,7 @@
 // than a capability proxy (the same page, section "What the source says").
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -286,6 +287,42 @@ QSA_EXPORT qsa_status qsa_topk_rows(const float* scores, int64_t ld_scores, cons
     vs.max_visible = max_visible;
     HIP_CHECK(qsa::launch_topk_rows(scores, ld_scores, vs, rows, k, 1, k, out,
                                     static_cast<hipStream_t>(stream)));
+    return QSA_OK;
+}
+
+QSA_EXPORT qsa_status qsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache,
+                                           const int32_t* page_table, int64_t pt_stride, int32_t num_pages,
+                                           int32_t num_reqs, const int32_t* row_req, const int32_t* tokens,
+                                           int32_t k, int32_t rows, int32_t q_heads, int32_t kv_heads,
+                                           int32_t head_dim, int32_t page_size, float scale, float* out,
+                                           void* stream) {
+    g_err[0] = 0;
+    REQUIRE(rows >= 0, QSA_ERR_INVALID_ARGUMENT, "rows must be >= 0 (got %d)", rows);
+    REQUIRE(k >= 1, QSA_ERR_INVALID_ARGUMENT, "k must be >= 1 (got %d)", k);
+    REQUIRE(head_dim == 256, QSA_ERR_UNSUPPORTED, "head_dim must be 256 (got %d)", head_dim);
+    REQUIRE(kv_heads >= 1 && q_heads >= kv_heads && q_heads % kv_heads == 0, QSA_ERR_INVALID_ARGUMENT,
+            "q_heads (%d) must be a positive multiple of kv_heads (%d)", q_heads, kv_heads);
+    REQUIRE(q_heads / kv_heads <= 16, QSA_ERR_UNSUPPORTED, "at most 16 query heads per KV head (got %d)",
+            q_heads / kv_heads);
+    REQUIRE(page_size >= 1, QSA_ERR_INVALID_ARGUMENT, "page_size must be >= 1 (got %d)", page_size);
+    REQUIRE(num_pages >= 1, QSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1 (got %d)", num_pages);
+    REQUIRE(num_reqs >= 1, QSA_ERR_INVALID_ARGUMENT, "num_reqs must be >= 1 (got %d)", num_reqs);
+    REQUIRE(pt_stride >= 1, QSA_ERR_INVALID_ARGUMENT, "pt_stride must be >= 1 (got %lld)", (long long)pt_stride);
+    REQUIRE((uint64_t)num_pages * (uint64_t)page_size * (uint64_t)kv_heads < (1ull << 32), QSA_ERR_UNSUPPORTED,
+            "num_pages * page_size * kv_heads must be < 2^32");
+    REQUIRE(std::isfinite(scale), QSA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (rows == 0) return QSA_OK;
+    REQUIRE(q && k_cache && v_cache && page_table && tokens && out, QSA_ERR_INVALID_ARGUMENT,
+            "null pointer among q, k_cache, v_cache, page_table, tokens, out");
+    REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache), QSA_ERR_INVALID_ARGUMENT,
+            "q, k_cache and v_cache must be 16-byte aligned");
+    const DeviceInfo* dev = nullptr;
+    qsa_status st = check_device(&dev);
+    if (st != QSA_OK) return st;
+    HIP_CHECK(qsa::launch_attend(static_cast<const _Float16*>(q), static_cast<const _Float16*>(k_cache),
+                                 static_cast<const _Float16*>(v_cache), page_table, pt_stride, num_pages, num_reqs,
+                                 row_req, tokens, k, rows, q_heads, kv_heads, page_size, scale, out,
+                                 static_cast<hipStream_t>(stream)));
     return QSA_OK;
 }
 

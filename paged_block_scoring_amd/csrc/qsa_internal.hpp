@@ -86,4 +86,11 @@ hipError_t launch_fused_final(const PagedArgs& a, const VisibleSource& vis, cons
                               const uint64_t* cand, const int32_t* cand_count, int32_t kb, int32_t expand,
                               int32_t out_len, int32_t* out, hipStream_t stream);
 
+// Sparse attention over selected tokens (attend.hip): head_dim 256, at most
+// 16 query heads per KV head; out fp32 [rows][q_heads][256].
+hipError_t launch_attend(const _Float16* q, const _Float16* kc, const _Float16* vc, const int32_t* page_table,
+                         int64_t pt_stride, int32_t num_pages, int32_t num_reqs, const int32_t* row_req,
+                         const int32_t* tokens, int32_t k, int32_t rows, int32_t q_heads, int32_t kv_heads,
+                         int32_t page_size, float scale, float* out, hipStream_t stream);
+
 }  // namespace qsa

@@ -30,7 +30,7 @@ QSA_MAX_SELECT = 4096
 
 EXPORTED = (
     "qsa_score_paged", "qsa_topk_rows", "qsa_topk_rows_workspace_size",
-    "qsa_select_paged_tokens", "qsa_select_paged_tokens_workspace_size",
+    "qsa_select_paged_tokens", "qsa_select_paged_tokens_workspace_size", "qsa_sparse_attention",
     "qsa_last_error", "qsa_last_path", "qsa_version",
     "qsa_debug_record_events", "qsa_debug_events_recorded",
 )
@@ -67,6 +67,9 @@ def lib():
     L.qsa_select_paged_tokens.restype = ctypes.c_int
     L.qsa_select_paged_tokens_workspace_size.argtypes = [i32, i32, i32, i32, i32, u32]
     L.qsa_select_paged_tokens_workspace_size.restype = sz
+    L.qsa_sparse_attention.argtypes = [P, P, P, P, i64, i32, i32, P, P, i32, i32, i32, i32, i32, i32,
+                                       ctypes.c_float, P, P]
+    L.qsa_sparse_attention.restype = ctypes.c_int
     L.qsa_debug_record_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     L.qsa_debug_record_events.restype = ctypes.c_int
     L.qsa_debug_events_recorded.argtypes = []
@@ -210,6 +213,41 @@ def qsa_topk_rows(scores, k, *, visible=None, max_visible=None, out=None, worksp
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().qsa_topk_rows(_ptr(scores), ld, _ptr(visible), rows, int(max_visible), int(k), _ptr(out),
                                _ptr(workspace), wbytes, _stream(dev)))
+    return out
+
+
+def qsa_sparse_attention(q, k_cache, v_cache, page_table, tokens, *, row_req=None, scale=None,
+                         out=None) -> torch.Tensor:
+    """Softmax attention of every query head over the tokens listed per row
+    (entries < 0 skipped), K/V gathered from the paged main cache
+    [pages][page_size][kv_heads][head_dim]; fp32 [rows, q_heads, head_dim]."""
+    _want(q, "q", torch.float16, ndim=3)
+    dev = q.device
+    _want(k_cache, "k_cache", torch.float16, dev, 4)
+    _want(v_cache, "v_cache", torch.float16, dev, 4)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    _want(page_table, "page_table", torch.int32, dev, 2)
+    _want(tokens, "tokens", torch.int32, dev, 2)
+    rows, q_heads, head_dim = q.shape
+    if tokens.shape[0] != rows:
+        raise ValueError("tokens must have one row per query row")
+    if row_req is not None:
+        _want(row_req, "row_req", torch.int32, dev, 1)
+        if row_req.numel() != rows:
+            raise ValueError("row_req must have one entry per row")
+    num_pages, page_size, kv_heads, kd = k_cache.shape
+    if kd != head_dim:
+        raise ValueError("k_cache head_dim differs from q's")
+    if scale is None:
+        scale = 1.0 / float(head_dim) ** 0.5
+    if out is None:
+        out = torch.empty((rows, q_heads, head_dim), dtype=torch.float32, device=dev)
+    _want(out, "out", torch.float32, dev, 3)
+    _check(lib().qsa_sparse_attention(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), page_table.shape[1], num_pages,
+        page_table.shape[0], _ptr(row_req), _ptr(tokens), tokens.shape[1], rows, q_heads, kv_heads, head_dim,
+        page_size, float(scale), _ptr(out), _stream(dev)))
     return out
 
 

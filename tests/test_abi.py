@@ -155,3 +155,44 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         Q.qsa_select_paged_tokens(q, q, torch.zeros((1, 1), dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
                                   4, 64)
+
+
+def attend(**over):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, page_table=FAKE, pt_stride=16, num_pages=16, num_reqs=1, row_req=None,
+             tokens=FAKE, k=2048, rows=8, q_heads=24, kv_heads=2, head_dim=256, page_size=64, scale=0.0625,
+             out=FAKE, stream=None)
+    a.update(over)
+    st = Q.lib().qsa_sparse_attention(
+        a["q"], a["kc"], a["vc"], a["page_table"], a["pt_stride"], a["num_pages"], a["num_reqs"], a["row_req"],
+        a["tokens"], a["k"], a["rows"], a["q_heads"], a["kv_heads"], a["head_dim"], a["page_size"], a["scale"],
+        a["out"], a["stream"])
+    return st, Q.qsa_last_error()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(head_dim=128), Q.QSA_ERR_UNSUPPORTED),
+    (dict(q_heads=25), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(q_heads=34, kv_heads=2), Q.QSA_ERR_UNSUPPORTED),     # 17 query heads per KV head
+    (dict(kv_heads=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(k=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(rows=-1), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(page_size=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(num_pages=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(num_reqs=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(pt_stride=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(num_pages=1 << 30), Q.QSA_ERR_UNSUPPORTED),          # rows of the cache past 2^32
+    (dict(scale=float("inf")), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(tokens=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(vc=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(out=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(q=FAKE + 4), Q.QSA_ERR_INVALID_ARGUMENT),            # misaligned
+])
+def test_attention_rejects_before_device(over, code):
+    st, msg = attend(**over)
+    assert st == code, msg
+    assert re.match(r"^qsa_api\.hip:\d+: .+", msg), msg
+
+
+def test_attention_zero_rows_is_a_noop():
+    st, msg = attend(rows=0, q=None, kc=None, vc=None, page_table=None, tokens=None, out=None)
+    assert st == Q.QSA_OK, msg

@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--consumer", action="store_true",
+                    help="time the sparse-attention consumer over the workload's selection instead "
+                         "(GQA 24 query / 2 KV heads, head_dim 256, a random paged main KV cache)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph (reported as graph_ms_per_step)")
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
@@ -223,6 +226,47 @@ def kernel_times(fn, steps, names, torch, Q):
     return out, total
 
 
+def bench_consumer(args, w, select_step, tokens, q_index, pt, row_req, rows, k, torch, Q):
+    """The sparse-attention consumer on the workload's own selection: the
+    indexer runs once (untimed), then `steps` consumer calls are timed."""
+    dev = tokens.device
+    select_step()
+    torch.cuda.synchronize()
+    q_heads, kv_heads, d, page_size = 24, 2, 256, w.page_size
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 1000)
+    qa = torch.randn((rows, q_heads, d), generator=g, device=dev, dtype=torch.float32).half()
+    kc = torch.randn((w.num_pages, page_size, kv_heads, d), generator=g, device=dev, dtype=torch.float32).half()
+    vc = torch.randn((w.num_pages, page_size, kv_heads, d), generator=g, device=dev, dtype=torch.float32).half()
+    out = torch.empty((rows, q_heads, d), dtype=torch.float32, device=dev)
+
+    def step():
+        Q.qsa_sparse_attention(qa, kc, vc, pt, tokens, row_req=row_req, out=out)
+
+    ms, wall = time_calls(step, args.steps, args.warmup, torch)
+    nsel = int((tokens >= 0).sum().item())
+    flops = 4.0 * q_heads * d * nsel                  # (q.K and p.V) x 2 flops per multiply-add
+    gathered = 2.0 * kv_heads * d * 2 * nsel          # K and V rows of every selected token, fp16
+    result = {
+        "metric": "sparse attention rows/s over the indexer's selection (GQA 24/2, head_dim 256)",
+        "value": round(rows / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT.get(args.workload, args.workload) + "; consumer over its selection",
+                   "rows": rows, "selected_tokens": nsel, "q_heads": q_heads, "kv_heads": kv_heads,
+                   "head_dim": d},
+        "attention_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+        "gather_gbs": round(gathered / (ms * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": "attend", "bound": "hbm", "achieved": round(gathered / (ms * 1e-3) / 1e9, 3),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gathered / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "ms_per_launch": round(ms, 4)},
+        "wall_s_timed": round(wall, 4),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.summarize_profile:
@@ -257,6 +301,9 @@ def main():
     def step():
         Q.qsa_select_paged_tokens(q, kc, pt, pos, cr, k, row_req=row_req, max_visible=max_v, out=out,
                                   workspace=ws)
+
+    if args.consumer:
+        return bench_consumer(args, w, step, out, q, pt, row_req, rows, k, torch, Q)
 
     # the timed region: exactly `steps` whole steps
     ms_step, wall = time_calls(step, args.steps, args.warmup, torch)

@@ -91,6 +91,7 @@ KERNEL_SOURCES = {
     "final_select": (("fused_select_kernel",),
                      ["paged_block_scoring_amd/csrc/fused.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
     "topk_rows": (("topk_rows_kernel",), ["paged_block_scoring_amd/csrc/topk.hip"]),
+    "attend": (("attend_kernel",), ["paged_block_scoring_amd/csrc/attend.hip"]),
 }
 
 
@@ -131,7 +132,7 @@ def summarize_profile(args):
     """
     import glob
     out = {}
-    name = args.workload
+    name = args.workload + ("_consumer" if args.consumer else "")
     if args.stats_dir:
         stats = _read_csv(glob.glob(os.path.join(args.stats_dir, "*_kernel_stats.csv"))[0])
         lines = [f"# Kernel time, {name} (rocprofv3 --kernel-trace --stats)", "",
@@ -226,6 +227,17 @@ def kernel_times(fn, steps, names, torch, Q):
     return out, total
 
 
+def copy_probe(args, torch, dev):
+    """A plain device copy of known size, whose counter readings scale the
+    kernels' FETCH_SIZE / WRITE_SIZE readings in --summarize-profile."""
+    if args.copy_probe > 0:
+        n = args.copy_probe * (1 << 20)
+        src_t = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst_t = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+
+
 def bench_consumer(args, w, select_step, tokens, q_index, pt, row_req, rows, k, torch, Q):
     """The sparse-attention consumer on the workload's own selection: the
     indexer runs once (untimed), then `steps` consumer calls are timed."""
@@ -259,10 +271,12 @@ def bench_consumer(args, w, select_step, tokens, q_index, pt, row_req, rows, k, 
         "gather_gbs": round(gathered / (ms * 1e-3) / 1e9, 1),
         "roofline": {"kernel": "attend", "bound": "hbm", "achieved": round(gathered / (ms * 1e-3) / 1e9, 3),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gathered / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(gathered / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for("attend", args.workload + "_consumer"),
                      "ms_per_launch": round(ms, 4)},
         "wall_s_timed": round(wall, 4),
     }
+    copy_probe(args, torch, dev)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -376,12 +390,7 @@ def main():
     if graph_ms is not None:
         result["graph_ms_per_step"] = round(graph_ms, 4)
 
-    if args.copy_probe > 0:
-        n = args.copy_probe * (1 << 20)
-        src_t = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst_t = torch.empty(n, dtype=torch.uint8, device=dev)
-        dst_t.copy_(src_t)
-        torch.cuda.synchronize()
+    copy_probe(args, torch, dev)
 
     if not args.no_cpu_baseline:
         import oracle

@@ -214,6 +214,59 @@ qsa_status qsa_sparse_attention(const void* q, const void* k_cache, const void* 
                                 int32_t head_dim, int32_t page_size, float scale, float* out,
                                 void* stream);
 
+/*
+ * qsa_compress_keys -- the producer of the side cache the scorer reads
+ * ([spec] "The component deep-dives, and two corrections to the above": one
+ * stored state per compress_ratio tokens, written at the token whose
+ * (position + 1) is a multiple of the ratio; a pooled key, RMSNorm on it, RoPE
+ * at the block-start position).  The pages name no pooling for this model;
+ * the library takes the mean.  For block c of request q (tokens cr*c ..
+ * cr*c+cr-1, raw keys x_0 .. x_{cr-1}):
+ *   m = (x_0 + ... + x_{cr-1}) / cr;  y_i = w_i m_i / sqrt(mean_j m_j^2 + eps);
+ *   RoPE on y's leading rope_dim values at p0 = cr*c: the pair (a, b) at
+ *   frequency index i turns into (a cos - b sin, b cos + a sin),
+ *   angle p0 * rope_base^(-2i/rope_dim); pairs (i, i + rope_dim/2), or
+ *   (2i, 2i+1) with QSA_ROPE_INTERLEAVED;
+ * rounded to fp16 and stored in slot c % (page_size/cr) of physical page
+ * page_table[q][c / (page_size/cr)] of kcache (the layout qsa_score_paged
+ * reads).
+ *
+ *  k_tok        device fp16 [tokens][head_dim]: the raw index keys of this
+ *               call's tokens.  Each request's tokens form one run of
+ *               consecutive positions in consecutive slots (a prefill chunk,
+ *               or a decode token); across calls a request's positions
+ *               arrive in order, each once.
+ *  tok_req      device int32 [tokens]: request of each token; NULL means
+ *               request 0.  Tokens with a request outside [0, num_reqs) or a
+ *               negative position are ignored.
+ *  tok_pos      device int32 [tokens]: absolute position of each token.
+ *  head_dim     must be 128.
+ *  norm_w       device fp32 [head_dim] RMSNorm weights, or NULL for 1.
+ *  eps          RMSNorm epsilon (finite, >= 0).
+ *  rope_dim     0 (no rotation) .. head_dim, a multiple of 16.
+ *  rope_base    RoPE base (finite, > 0; unused when rope_dim is 0).
+ *  flags        0 or QSA_ROPE_INTERLEAVED.
+ *  state        device fp16 [num_reqs][compress_ratio][head_dim], owned by
+ *               the caller and kept between calls: the raw keys of each
+ *               request's open block.  Read and written by the call; its
+ *               initial contents never matter for a request whose positions
+ *               start at 0.  May be NULL when compress_ratio is 1.
+ *  kcache       device fp16 [num_pages][page_size/cr][head_dim]: written at
+ *               the slots of the blocks that close in this call only.
+ *  page_table, pt_stride, num_pages, num_reqs   as for qsa_score_paged;
+ *               a block whose logical page is >= pt_stride is not stored,
+ *               page ids are clamped into [0, num_pages).
+ *  Supported: 1 <= compress_ratio <= 64, page_size a multiple of it.
+ *  Two kernels on `stream`; no workspace.
+ */
+#define QSA_ROPE_INTERLEAVED 0x4u
+qsa_status qsa_compress_keys(const void* k_tok, const int32_t* tok_req, const int32_t* tok_pos,
+                             int32_t tokens, int32_t head_dim, const float* norm_w, float eps,
+                             int32_t rope_dim, double rope_base, uint32_t flags, void* state,
+                             void* kcache, const int32_t* page_table, int64_t pt_stride,
+                             int32_t num_pages, int32_t num_reqs, int32_t page_size,
+                             int32_t compress_ratio, void* stream);
+
 /* Description of the last failure on the calling thread, "file:line: message"
  * ("" if none).  The pointer stays valid until the thread's next library call. */
 const char* qsa_last_error(void);

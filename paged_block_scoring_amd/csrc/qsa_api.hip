@@ -326,6 +326,47 @@ QSA_EXPORT qsa_status qsa_sparse_attention(const void* q, const void* k_cache, c
     return QSA_OK;
 }
 
+QSA_EXPORT qsa_status qsa_compress_keys(const void* k_tok, const int32_t* tok_req, const int32_t* tok_pos,
+                                        int32_t tokens, int32_t head_dim, const float* norm_w, float eps,
+                                        int32_t rope_dim, double rope_base, uint32_t flags, void* state,
+                                        void* kcache, const int32_t* page_table, int64_t pt_stride,
+                                        int32_t num_pages, int32_t num_reqs, int32_t page_size,
+                                        int32_t compress_ratio, void* stream) {
+    g_err[0] = 0;
+    REQUIRE(tokens >= 0, QSA_ERR_INVALID_ARGUMENT, "tokens must be >= 0 (got %d)", tokens);
+    REQUIRE(head_dim == 128, QSA_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+    REQUIRE(compress_ratio >= 1, QSA_ERR_INVALID_ARGUMENT, "compress_ratio must be >= 1 (got %d)",
+            compress_ratio);
+    REQUIRE(compress_ratio <= 64, QSA_ERR_UNSUPPORTED, "compress_ratio must be <= 64 (got %d)", compress_ratio);
+    REQUIRE(page_size >= compress_ratio && page_size % compress_ratio == 0, QSA_ERR_INVALID_ARGUMENT,
+            "page_size (%d) must be a positive multiple of compress_ratio (%d)", page_size, compress_ratio);
+    REQUIRE(rope_dim >= 0 && rope_dim <= head_dim, QSA_ERR_INVALID_ARGUMENT, "rope_dim must be in [0, %d] (got %d)",
+            head_dim, rope_dim);
+    REQUIRE(rope_dim % 16 == 0, QSA_ERR_UNSUPPORTED, "rope_dim must be a multiple of 16 (got %d)", rope_dim);
+    REQUIRE(rope_dim == 0 || (std::isfinite(rope_base) && rope_base > 0.0), QSA_ERR_INVALID_ARGUMENT,
+            "rope_base must be finite and > 0");
+    REQUIRE(std::isfinite(eps) && eps >= 0.0f, QSA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    REQUIRE((flags & ~QSA_ROPE_INTERLEAVED) == 0, QSA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x", flags);
+    REQUIRE(num_pages >= 1, QSA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1 (got %d)", num_pages);
+    REQUIRE(num_reqs >= 1, QSA_ERR_INVALID_ARGUMENT, "num_reqs must be >= 1 (got %d)", num_reqs);
+    REQUIRE(pt_stride >= 1, QSA_ERR_INVALID_ARGUMENT, "pt_stride must be >= 1 (got %lld)", (long long)pt_stride);
+    if (tokens == 0) return QSA_OK;
+    REQUIRE(k_tok && tok_pos && kcache && page_table, QSA_ERR_INVALID_ARGUMENT,
+            "null pointer among k_tok, tok_pos, kcache, page_table");
+    REQUIRE(state || compress_ratio == 1, QSA_ERR_INVALID_ARGUMENT, "null pointer: state");
+    REQUIRE(aligned16(k_tok) && aligned16(kcache) && (state == nullptr || aligned16(state)),
+            QSA_ERR_INVALID_ARGUMENT, "k_tok, kcache and state must be 16-byte aligned");
+    const DeviceInfo* dev = nullptr;
+    qsa_status st = check_device(&dev);
+    if (st != QSA_OK) return st;
+    HIP_CHECK(qsa::launch_compress(static_cast<const _Float16*>(k_tok), tok_req, tok_pos, tokens, norm_w, eps,
+                                   rope_dim, rope_base, (flags & QSA_ROPE_INTERLEAVED) != 0,
+                                   static_cast<_Float16*>(state), static_cast<_Float16*>(kcache), page_table,
+                                   pt_stride, num_pages, num_reqs, page_size, compress_ratio, dev->cus,
+                                   static_cast<hipStream_t>(stream)));
+    return QSA_OK;
+}
+
 QSA_EXPORT size_t qsa_select_paged_tokens_workspace_size(int32_t rows, int32_t num_reqs, int32_t max_visible,
                                                          int32_t compress_ratio, int32_t k, uint32_t flags) {
     if (rows <= 0 || max_visible <= 0 || k < 1 || compress_ratio < 1) return 0;

@@ -26,12 +26,13 @@ QSA_ERR_DEVICE = 4
 
 QSA_SCORE_RELU = 0x1
 QSA_OUT_KEYS = 0x2
+QSA_ROPE_INTERLEAVED = 0x4
 QSA_MAX_SELECT = 4096
 
 EXPORTED = (
     "qsa_score_paged", "qsa_topk_rows", "qsa_topk_rows_workspace_size",
     "qsa_select_paged_tokens", "qsa_select_paged_tokens_workspace_size", "qsa_sparse_attention",
-    "qsa_last_error", "qsa_last_path", "qsa_version",
+    "qsa_compress_keys", "qsa_last_error", "qsa_last_path", "qsa_version",
     "qsa_debug_record_events", "qsa_debug_events_recorded",
 )
 
@@ -70,6 +71,9 @@ def lib():
     L.qsa_sparse_attention.argtypes = [P, P, P, P, i64, i32, i32, P, P, i32, i32, i32, i32, i32, i32,
                                        ctypes.c_float, P, P]
     L.qsa_sparse_attention.restype = ctypes.c_int
+    L.qsa_compress_keys.argtypes = [P, P, P, i32, i32, P, ctypes.c_float, i32, ctypes.c_double, u32, P, P, P,
+                                    i64, i32, i32, i32, i32, P]
+    L.qsa_compress_keys.restype = ctypes.c_int
     L.qsa_debug_record_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), i32]
     L.qsa_debug_record_events.restype = ctypes.c_int
     L.qsa_debug_events_recorded.argtypes = []
@@ -249,6 +253,42 @@ def qsa_sparse_attention(q, k_cache, v_cache, page_table, tokens, *, row_req=Non
         page_table.shape[0], _ptr(row_req), _ptr(tokens), tokens.shape[1], rows, q_heads, kv_heads, head_dim,
         page_size, float(scale), _ptr(out), _stream(dev)))
     return out
+
+
+def qsa_compress_keys(k_tok, tok_pos, state, kcache, page_table, compress_ratio, *, tok_req=None, norm_w=None,
+                      eps=1e-6, rope_dim=128, rope_base=10000.0, interleaved=False) -> None:
+    """Compressed-key producer: finishes every block of compress_ratio tokens
+    whose last token is in this call (mean pool, RMSNorm, RoPE at the block
+    start, fp16) into its slot of kcache [pages][page_size/cr][128], and keeps
+    the raw keys of blocks left open in state [num_reqs][cr][128]."""
+    _want(k_tok, "k_tok", torch.float16, ndim=2)
+    dev = k_tok.device
+    tokens, head_dim = k_tok.shape
+    _want(tok_pos, "tok_pos", torch.int32, dev, 1)
+    if tok_pos.numel() != tokens:
+        raise ValueError("tok_pos must have one entry per token")
+    if tok_req is not None:
+        _want(tok_req, "tok_req", torch.int32, dev, 1)
+        if tok_req.numel() != tokens:
+            raise ValueError("tok_req must have one entry per token")
+    _want(kcache, "kcache", torch.float16, dev, 3)
+    _want(page_table, "page_table", torch.int32, dev, 2)
+    if state is not None:
+        _want(state, "state", torch.float16, dev, 3)
+        if state.shape != (page_table.shape[0], int(compress_ratio), head_dim):
+            raise ValueError("state must be [num_reqs, compress_ratio, head_dim]")
+    if norm_w is not None:
+        _want(norm_w, "norm_w", torch.float32, dev, 1)
+        if norm_w.numel() != head_dim:
+            raise ValueError("norm_w must have head_dim entries")
+    if kcache.shape[2] != head_dim:
+        raise ValueError("kcache head_dim differs from k_tok's")
+    page_size = kcache.shape[1] * int(compress_ratio)
+    flags = QSA_ROPE_INTERLEAVED if interleaved else 0
+    _check(lib().qsa_compress_keys(
+        _ptr(k_tok), _ptr(tok_req), _ptr(tok_pos), tokens, head_dim, _ptr(norm_w), float(eps), int(rope_dim),
+        float(rope_base), flags, _ptr(state), _ptr(kcache), _ptr(page_table), page_table.shape[1], kcache.shape[0],
+        page_table.shape[0], page_size, int(compress_ratio), _stream(dev)))
 
 
 def qsa_select_paged_tokens_workspace_size(rows, num_reqs, max_visible, compress_ratio, k, flags=0) -> int:

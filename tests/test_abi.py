@@ -196,3 +196,53 @@ def test_attention_rejects_before_device(over, code):
 def test_attention_zero_rows_is_a_noop():
     st, msg = attend(rows=0, q=None, kc=None, vc=None, page_table=None, tokens=None, out=None)
     assert st == Q.QSA_OK, msg
+
+
+def compress(**over):
+    a = dict(k_tok=FAKE, tok_req=None, tok_pos=FAKE, tokens=64, head_dim=128, norm_w=None, eps=1e-6, rope_dim=128,
+             rope_base=10000.0, flags=0, state=FAKE, kcache=FAKE, page_table=FAKE, pt_stride=16, num_pages=16,
+             num_reqs=1, page_size=64, compress_ratio=4, stream=None)
+    a.update(over)
+    st = Q.lib().qsa_compress_keys(
+        a["k_tok"], a["tok_req"], a["tok_pos"], a["tokens"], a["head_dim"], a["norm_w"], a["eps"], a["rope_dim"],
+        a["rope_base"], a["flags"], a["state"], a["kcache"], a["page_table"], a["pt_stride"], a["num_pages"],
+        a["num_reqs"], a["page_size"], a["compress_ratio"], a["stream"])
+    return st, Q.qsa_last_error()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(tokens=-1), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(head_dim=256), Q.QSA_ERR_UNSUPPORTED),
+    (dict(compress_ratio=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(compress_ratio=128, page_size=128), Q.QSA_ERR_UNSUPPORTED),
+    (dict(page_size=66), Q.QSA_ERR_INVALID_ARGUMENT),           # not a multiple of the ratio
+    (dict(page_size=2), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(rope_dim=-16), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(rope_dim=144), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(rope_dim=40), Q.QSA_ERR_UNSUPPORTED),
+    (dict(rope_base=0.0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(rope_base=float("nan")), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(eps=-1.0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(eps=float("inf")), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(flags=0x1), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(num_pages=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(num_reqs=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(pt_stride=0), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(k_tok=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(kcache=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(state=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(state=FAKE + 2), Q.QSA_ERR_INVALID_ARGUMENT),         # misaligned
+])
+def test_compress_rejects_before_device(over, code):
+    st, msg = compress(**over)
+    assert st == code, msg
+    assert re.match(r"^qsa_api\.hip:\d+: .+", msg), msg
+
+
+def test_compress_edge_arguments_pass_the_host_checks():
+    # no tokens: nothing to do, no pointer is looked at
+    st, msg = compress(tokens=0, k_tok=None, tok_pos=None, kcache=None, page_table=None, state=None)
+    assert st == Q.QSA_OK, msg
+    # rope_dim 0 ignores the base
+    st, msg = compress(tokens=0, rope_dim=0, rope_base=0.0)
+    assert st == Q.QSA_OK, msg

@@ -197,6 +197,23 @@ def long_few(seed=5, integer=False, num_reqs=8, ctx=184_000, outlier_p=0.01):
                  outlier_p=outlier_p, k=2048)
 
 
+def raw_token_keys(seed, lengths, page_size=PAGE_SIZE, compress_ratio=COMPRESS_RATIO, spare_pages=2):
+    """Inputs of the compressed-key producer: each request's raw per-token
+    index keys (fp16 [n_q, head_dim], standard normal), RMSNorm weights
+    (float32 [head_dim], uniform in [0.5, 1.5)) and a page table over a
+    permuted pool with room for every request's compressed keys, plus
+    ``spare_pages`` pages that no request maps.  Draw order: keys request by
+    request, weights, permutation."""
+    rng = np.random.default_rng(seed)
+    keys = [_normal_f16(rng, (int(n), HEAD_DIM), chunk_rows=1 << 16) for n in lengths]
+    w = rng.uniform(0.5, 1.5, HEAD_DIM).astype(np.float32)
+    kpp = page_size // compress_ratio
+    per = max(1, max((int(n) // compress_ratio + kpp - 1) // kpp for n in lengths) if len(lengths) else 1)
+    pool = len(lengths) * per + spare_pages
+    pt = rng.permutation(pool)[:len(lengths) * per].astype(np.int32).reshape(len(lengths), per)
+    return keys, w, pt, pool
+
+
 CONFIGS = {
     "tiny": tiny,
     "kernel_shape": kernel_shape,

@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--consumer", action="store_true",
                     help="time the sparse-attention consumer over the workload's selection instead "
                          "(GQA 24 query / 2 KV heads, head_dim 256, a random paged main KV cache)")
+    ap.add_argument("--producer", action="store_true",
+                    help="time the compressed-key producer instead: the workload's requests' whole contexts "
+                         "as raw token keys, built into the side cache in one call")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph (reported as graph_ms_per_step)")
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
@@ -92,6 +95,7 @@ KERNEL_SOURCES = {
                      ["paged_block_scoring_amd/csrc/fused.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
     "topk_rows": (("topk_rows_kernel",), ["paged_block_scoring_amd/csrc/topk.hip"]),
     "attend": (("attend_kernel",), ["paged_block_scoring_amd/csrc/attend.hip"]),
+    "compress_blocks": (("compress_blocks_kernel",), ["paged_block_scoring_amd/csrc/compress.hip"]),
 }
 
 
@@ -132,7 +136,7 @@ def summarize_profile(args):
     """
     import glob
     out = {}
-    name = args.workload + ("_consumer" if args.consumer else "")
+    name = args.workload + ("_consumer" if args.consumer else "") + ("_producer" if args.producer else "")
     if args.stats_dir:
         stats = _read_csv(glob.glob(os.path.join(args.stats_dir, "*_kernel_stats.csv"))[0])
         lines = [f"# Kernel time, {name} (rocprofv3 --kernel-trace --stats)", "",
@@ -281,6 +285,56 @@ def bench_consumer(args, w, select_step, tokens, q_index, pt, row_req, rows, k, 
     return 0
 
 
+def bench_producer(args, w, torch, Q):
+    """The compressed-key producer building the workload's side cache: every
+    request's whole context (positions 0 .. ctx-1) as random fp16 raw keys in
+    one call; `steps` such calls are timed (each rebuilds the same cache)."""
+    dev = torch.device("cuda:0")
+    cr, d = w.compress_ratio, 128
+    ctx = torch.from_numpy(w.ctx.astype(np.int64)).to(dev)
+    tokens = int(w.ctx.sum())
+    req = torch.repeat_interleave(torch.arange(w.num_reqs, device=dev, dtype=torch.int32), ctx)
+    starts = torch.cumsum(ctx, 0) - ctx
+    pos = (torch.arange(tokens, device=dev, dtype=torch.int64) - starts[req.long()]).to(torch.int32)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 2000)
+    k_tok = torch.randn((tokens, d), generator=g, device=dev, dtype=torch.float16)
+    norm_w = torch.rand(d, generator=g, device=dev, dtype=torch.float32) + 0.5
+    kc = torch.zeros(w.kcache.shape, dtype=torch.float16, device=dev)
+    pt = torch.from_numpy(w.page_table).to(dev)
+    state = torch.zeros((w.num_reqs, cr, d), dtype=torch.float16, device=dev)
+
+    def step():
+        Q.qsa_compress_keys(k_tok, pos, state, kc, pt, cr, tok_req=req, norm_w=norm_w)
+
+    ms, wall = time_calls(step, args.steps, args.warmup, torch)
+    names = ["compress_blocks", "stage_open"] if cr > 1 else ["compress_blocks"]
+    kms, _ = kernel_times(step, args.steps, names, torch, Q)
+    blocks = int((w.ctx // cr).sum())
+    # each token's key and its (request, position) read once, each finished key written once
+    algo = tokens * (2 * d + 8) + blocks * 2 * d
+    k_ms = kms["compress_blocks"]
+    gbs = algo / (k_ms * 1e-3) / 1e9
+    result = {
+        "metric": "compressed-key producer tokens/s (mean pool, RMSNorm, RoPE, paged store)",
+        "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT.get(args.workload, args.workload)
+                   + "; producer over every request's whole context", "tokens": tokens, "blocks": blocks,
+                   "compress_ratio": cr, "head_dim": d, "rope_dim": 128},
+        "kernels_ms": {k: round(v, 4) for k, v in kms.items()},
+        "roofline": {"kernel": "compress_blocks", "bound": "hbm", "achieved": round(gbs, 3),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for("compress_blocks", args.workload + "_producer"),
+                     "algorithmic_bytes": algo, "ms_per_launch": round(k_ms, 4)},
+        "wall_s_timed": round(wall, 4),
+    }
+    copy_probe(args, torch, dev)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.summarize_profile:
@@ -298,6 +352,8 @@ def main():
     w = W.make(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.producer:
+        return bench_producer(args, w, torch, Q)
     q = torch.from_numpy(w.q).to(dev)
     kc = torch.from_numpy(w.kcache).to(dev)
     pt = torch.from_numpy(w.page_table).to(dev)

@@ -279,13 +279,14 @@ const char* qsa_last_path(void);
 const char* qsa_version(void);
 
 /* Instrumentation for benchmarks and profilers.  Arms the calling thread's
- * next qsa_select_paged_tokens call to record events[0] on its stream before
- * its first kernel and events[i] after its i-th kernel, for at most n events
- * (hipEvent_t handles created and owned by the caller, passed as void*; they
- * must stay valid until that call returns).  The call disarms the hook;
- * qsa_debug_events_recorded() then returns how many events it recorded.
- * Kernel order: two-pass arm = scorer, selector; fused arm = sampling scorer,
- * threshold, filtering scorer, final select. */
+ * next qsa_select_paged_tokens or qsa_compress_keys call to record events[0]
+ * on its stream before its first kernel and events[i] after its i-th kernel,
+ * for at most n events (hipEvent_t handles created and owned by the caller,
+ * passed as void*; they must stay valid until that call returns).  The call
+ * disarms the hook; qsa_debug_events_recorded() then returns how many events
+ * it recorded.  Kernel order: two-pass arm = scorer, selector; fused arm =
+ * sampling scorer, threshold, filtering scorer, final select; producer =
+ * block compression, staging of open blocks (none when compress_ratio is 1). */
 qsa_status qsa_debug_record_events(void* const* events, int32_t n);
 int32_t qsa_debug_events_recorded(void);
 

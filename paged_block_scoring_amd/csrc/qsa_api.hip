@@ -333,6 +333,7 @@ QSA_EXPORT qsa_status qsa_compress_keys(const void* k_tok, const int32_t* tok_re
                                         int32_t num_pages, int32_t num_reqs, int32_t page_size,
                                         int32_t compress_ratio, void* stream) {
     g_err[0] = 0;
+    g_recorded = 0;
     REQUIRE(tokens >= 0, QSA_ERR_INVALID_ARGUMENT, "tokens must be >= 0 (got %d)", tokens);
     REQUIRE(head_dim == 128, QSA_ERR_UNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
     REQUIRE(compress_ratio >= 1, QSA_ERR_INVALID_ARGUMENT, "compress_ratio must be >= 1 (got %d)",
@@ -363,7 +364,8 @@ QSA_EXPORT qsa_status qsa_compress_keys(const void* k_tok, const int32_t* tok_re
                                    rope_dim, rope_base, (flags & QSA_ROPE_INTERLEAVED) != 0,
                                    static_cast<_Float16*>(state), static_cast<_Float16*>(kcache), page_table,
                                    pt_stride, num_pages, num_reqs, page_size, compress_ratio, dev->cus,
-                                   static_cast<hipStream_t>(stream)));
+                                   static_cast<hipStream_t>(stream), mark));
+    g_events = nullptr;
     return QSA_OK;
 }
 

@@ -94,11 +94,12 @@ hipError_t launch_attend(const _Float16* q, const _Float16* kc, const _Float16* 
                          int32_t page_size, float scale, float* out, hipStream_t stream);
 
 // Compressed-key producer (compress.hip): finishes the blocks that close in
-// this call and stages the keys of blocks left open.
+// this call and stages the keys of blocks left open; `mark` is called on the
+// stream before the first kernel and after each one.
 hipError_t launch_compress(const _Float16* k_tok, const int32_t* tok_req, const int32_t* tok_pos, int32_t T,
                            const float* norm_w, float eps, int32_t rope_dim, double rope_base, bool interleaved,
                            _Float16* state, _Float16* kcache, const int32_t* page_table, int64_t pt_stride,
                            int32_t num_pages, int32_t num_reqs, int32_t page_size, int32_t cr, int32_t cus,
-                           hipStream_t stream);
+                           hipStream_t stream, hipError_t (*mark)(hipStream_t));
 
 }  // namespace qsa

@@ -98,7 +98,7 @@ def qsa_version() -> str:
 
 
 class record_events:
-    """Arms the next qsa_select_paged_tokens call on this thread to record
+    """Arms the next qsa_select_paged_tokens or qsa_compress_keys call on this thread to record
     the given torch.cuda.Event objects between its kernels (see
     qsa_debug_record_events in include/qsa.h).  Keep the object alive until
     that call has returned."""

@@ -255,9 +255,11 @@ def bench_consumer(args, w, select_step, tokens, q_index, pt, row_req, rows, k, 
     kc = torch.randn((w.num_pages, page_size, kv_heads, d), generator=g, device=dev, dtype=torch.float32).half()
     vc = torch.randn((w.num_pages, page_size, kv_heads, d), generator=g, device=dev, dtype=torch.float32).half()
     out = torch.empty((rows, q_heads, d), dtype=torch.float32, device=dev)
+    need = Q.qsa_sparse_attention_workspace_size(rows, q_heads, kv_heads, d, tokens.shape[1])
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
     def step():
-        Q.qsa_sparse_attention(qa, kc, vc, pt, tokens, row_req=row_req, out=out)
+        Q.qsa_sparse_attention(qa, kc, vc, pt, tokens, row_req=row_req, out=out, workspace=ws)
 
     ms, wall = time_calls(step, args.steps, args.warmup, torch)
     nsel = int((tokens >= 0).sum().item())
@@ -270,7 +272,7 @@ def bench_consumer(args, w, select_step, tokens, q_index, pt, row_req, rows, k, 
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT.get(args.workload, args.workload) + "; consumer over its selection",
                    "rows": rows, "selected_tokens": nsel, "q_heads": q_heads, "kv_heads": kv_heads,
-                   "head_dim": d},
+                   "head_dim": d, "list_splits_workspace_bytes": need},
         "attention_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
         "gather_gbs": round(gathered / (ms * 1e-3) / 1e9, 1),
         "roofline": {"kernel": "attend", "bound": "hbm", "achieved": round(gathered / (ms * 1e-3) / 1e9, 3),

@@ -203,16 +203,25 @@ size_t qsa_select_paged_tokens_workspace_size(int32_t rows, int32_t num_reqs, in
  *  scale        softmax scale, e.g. 1/sqrt(head_dim).
  *  out          device fp32 [rows][q_heads][head_dim]; a row with no token
  *               gets zeros.
+ *  workspace    device scratch of at least
+ *               qsa_sparse_attention_workspace_size(rows, q_heads, kv_heads,
+ *               head_dim, k) bytes, 16-byte aligned (may be NULL when that
+ *               size is 0).  With fewer than 512 (row, KV head) pairs each
+ *               row's list is split over several workgroups, whose partial
+ *               softmax states a second kernel merges; the workspace holds
+ *               them.
  *  Supported: head_dim == 256, q_heads a multiple of kv_heads with at most 16
  *  query heads per KV head, num_pages * page_size * kv_heads < 2^32.
- *  No workspace; asynchronous on `stream`.
+ *  Asynchronous on `stream`.
  */
+size_t qsa_sparse_attention_workspace_size(int32_t rows, int32_t q_heads, int32_t kv_heads,
+                                           int32_t head_dim, int32_t k);
 qsa_status qsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* page_table, int64_t pt_stride, int32_t num_pages,
                                 int32_t num_reqs, const int32_t* row_req, const int32_t* tokens,
                                 int32_t k, int32_t rows, int32_t q_heads, int32_t kv_heads,
                                 int32_t head_dim, int32_t page_size, float scale, float* out,
-                                void* stream);
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * qsa_compress_keys -- the producer of the side cache the scorer reads

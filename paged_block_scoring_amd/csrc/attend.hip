@@ -26,9 +26,15 @@
 //                      lanes; V^T's fragments are read from the chunk's rows.
 // Each wave thus keeps its own running max, sum and output for its tokens;
 // the four are merged at the end (the same rescaling as between chunks).
+// With fewer than 512 (row, KV head) pairs, each pair's list is cut into up
+// to 16 spans of at least 128 entries, one workgroup each; a span leaves its
+// merged state (max, sum, unnormalised output) in the caller's workspace and
+// attend_merge_kernel combines the spans with the same rescaling.
 #include "qsa.h"
 #include "qsa_device.hpp"
 #include "qsa_internal.hpp"
+
+#include <algorithm>
 
 namespace qsa {
 namespace {
@@ -43,6 +49,7 @@ constexpr int kWin = 2048;       // list entries whose rows are staged at once
 constexpr int kRow = kD + 8;     // LDS row of a K or V vector, in halves (padded against bank conflicts)
 constexpr int kPieces = kCh * kD / 8 / kNT;  // 16-byte pieces per thread per chunk, K or V
 constexpr uint32_t kNone = 0xFFFFFFFFu;
+constexpr int kMaxSplits = 16;   // workgroups per (row, KV head) at most
 
 struct AttendArgs {
     const _Float16* q;      // [rows][q_heads][256]
@@ -56,6 +63,18 @@ struct AttendArgs {
     int32_t k, rows, q_heads, kv_heads, group, page_size;
     float scale;
     float* out;             // [rows][q_heads][256]
+    int32_t splits;         // workgroups per (row, KV head), each over `span` list entries
+    int32_t span;
+    float* part;            // splits > 1: [rows * kv_heads * splits] partial records
+};
+
+// Partial result of one split of a (row, KV head): per head of the group its
+// running max m (-inf when the split saw no token), its sum l of e^(s - m) and
+// its unnormalised output sum_t e^(s_t - m) V_t.
+struct AttendPart {
+    float m[16];
+    float l[16];
+    float o[16 * kD];
 };
 
 struct AttendLds {
@@ -81,7 +100,9 @@ __device__ __forceinline__ float4v mfma16x16(half4 a, half4 b, float4v c) {
 
 __global__ __launch_bounds__(kNT, 2) void attend_kernel(AttendArgs A) {
     __shared__ AttendLds L;
-    const int row = blockIdx.x / A.kv_heads, kvh = blockIdx.x - row * A.kv_heads;
+    const int split = blockIdx.x % A.splits, rk = blockIdx.x / A.splits;
+    const int row = rk / A.kv_heads, kvh = rk - row * A.kv_heads;
+    const int e_begin = split * A.span, e_end = min(A.k, e_begin + A.span);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, quad = lane >> 4;  // MFMA column (head) and lane group
     const int req = A.row_req ? A.row_req[row] : 0;
@@ -106,8 +127,8 @@ __global__ __launch_bounds__(kNT, 2) void attend_kernel(AttendArgs A) {
 
     const int32_t* list = A.tokens + (int64_t)row * A.k;
     const int32_t* ptrow = A.page_table + (int64_t)(req_ok ? req : 0) * A.pt_stride;
-    for (int w0 = 0; w0 < A.k; w0 += kWin) {
-        const int wl = min(kWin, A.k - w0);
+    for (int w0 = e_begin; w0 < e_end; w0 += kWin) {
+        const int wl = min(kWin, e_end - w0);
         // rows of this window's entries, and the last valid one
         if (tid == 0) L.last = -1;
         __syncthreads();
@@ -228,20 +249,86 @@ __global__ __launch_bounds__(kNT, 2) void attend_kernel(AttendArgs A) {
     for (int t = 0; t < kD / 16; ++t)
         *reinterpret_cast<float4v*>(&L.u.o[wave][n * kD + 16 * t + 4 * quad]) = o[t] * f;
     __syncthreads();
-    for (int e = tid; e < A.group * kD; e += kNT) {
-        const int h = e / kD, d = e - h * kD;
-        const float acc = (L.u.o[0][e] + L.u.o[1][e]) + (L.u.o[2][e] + L.u.o[3][e]);
-        const float lsum = L.lh[h];
-        A.out[((int64_t)row * A.q_heads + kvh * A.group + h) * kD + d] = lsum > 0.0f ? acc / lsum : 0.0f;
+    if (A.splits == 1) {
+        for (int e = tid; e < A.group * kD; e += kNT) {
+            const int h = e / kD, d = e - h * kD;
+            const float acc = (L.u.o[0][e] + L.u.o[1][e]) + (L.u.o[2][e] + L.u.o[3][e]);
+            const float lsum = L.lh[h];
+            A.out[((int64_t)row * A.q_heads + kvh * A.group + h) * kD + d] = lsum > 0.0f ? acc / lsum : 0.0f;
+        }
+        return;
     }
+    // a split leaves its partial record for attend_merge_kernel
+    AttendPart* P = reinterpret_cast<AttendPart*>(A.part) + blockIdx.x;
+    if (tid < 16) {
+        P->m[tid] = L.lh[tid] > 0.0f ? L.mh[tid] : -__builtin_huge_valf();
+        P->l[tid] = L.lh[tid];
+    }
+    for (int e = tid; e < A.group * kD; e += kNT)
+        P->o[e] = (L.u.o[0][e] + L.u.o[1][e]) + (L.u.o[2][e] + L.u.o[3][e]);
+}
+
+// One workgroup per (row, query head), one thread per output value: the
+// splits' partial results merged with the same rescaling as between waves
+// (every split's values are requested before any is used).
+__global__ __launch_bounds__(kD) void attend_merge_kernel(AttendArgs A) {
+    const int row = blockIdx.x / A.q_heads, h = blockIdx.x - row * A.q_heads;
+    const int kvh = h / A.group, hh = h - kvh * A.group, d = threadIdx.x;
+    const AttendPart* P = reinterpret_cast<const AttendPart*>(A.part) + ((int64_t)row * A.kv_heads + kvh) * A.splits;
+    float ms[kMaxSplits], ls[kMaxSplits], os[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+        const bool in = s < A.splits;
+        const AttendPart* Ps = P + (in ? s : 0);
+        ms[s] = Ps->m[hh];
+        ls[s] = Ps->l[hh];
+        os[s] = Ps->o[hh * kD + d];
+        if (!in) ms[s] = -__builtin_huge_valf();
+    }
+    float mall = -__builtin_huge_valf();
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) mall = fmaxf(mall, ms[s]);
+    float lsum = 0.0f, acc = 0.0f;
+    if (mall > -__builtin_huge_valf()) {
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s) {
+            // a split that saw no token (or lies past the list) adds nothing
+            const float f = ms[s] == -__builtin_huge_valf() ? 0.0f : __expf(ms[s] - mall);
+            lsum += ls[s] * f;
+            acc += os[s] * f;
+        }
+    }
+    A.out[((int64_t)row * A.q_heads + h) * kD + d] = lsum > 0.0f ? acc / lsum : 0.0f;
 }
 
 }  // namespace
 
+// Splits per (row, KV head): enough workgroups to give every compute unit
+// two (512 in all) when the rows alone do not, with at least two chunks (128
+// list entries) per split and at most 16 splits.  Depends on the arguments
+// only.  (Finer splits measured slower: each workgroup's fixed costs and the
+// merge outweigh the added parallelism.)
+static void attend_split_plan(int32_t rows, int32_t kv_heads, int32_t k, int32_t* splits, int32_t* span) {
+    const int64_t wgs = (int64_t)rows * kv_heads;
+    int64_t s = wgs >= 512 ? 1 : (512 + wgs - 1) / wgs;
+    s = std::min<int64_t>(std::min<int64_t>(s, kMaxSplits), std::max<int64_t>(1, k / (2 * kCh)));
+    int64_t sp = (k + s - 1) / s;
+    sp = (sp + kCh - 1) / kCh * kCh;
+    *span = (int32_t)sp;
+    *splits = (int32_t)((k + sp - 1) / sp);
+}
+
+size_t attend_workspace_bytes(int32_t rows, int32_t kv_heads, int32_t k) {
+    if (rows <= 0 || kv_heads <= 0 || k <= 0) return 0;
+    int32_t splits, span;
+    attend_split_plan(rows, kv_heads, k, &splits, &span);
+    return splits > 1 ? (size_t)rows * kv_heads * splits * sizeof(AttendPart) : 0;
+}
+
 hipError_t launch_attend(const _Float16* q, const _Float16* kc, const _Float16* vc, const int32_t* page_table,
                          int64_t pt_stride, int32_t num_pages, int32_t num_reqs, const int32_t* row_req,
                          const int32_t* tokens, int32_t k, int32_t rows, int32_t q_heads, int32_t kv_heads,
-                         int32_t page_size, float scale, float* out, hipStream_t stream) {
+                         int32_t page_size, float scale, float* out, void* workspace, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
     AttendArgs A;
     A.q = q;
@@ -261,7 +348,13 @@ hipError_t launch_attend(const _Float16* q, const _Float16* kc, const _Float16* 
     A.page_size = page_size;
     A.scale = scale;
     A.out = out;
-    attend_kernel<<<dim3((unsigned)(rows * kv_heads)), kNT, 0, stream>>>(A);
+    attend_split_plan(rows, kv_heads, k, &A.splits, &A.span);
+    A.part = static_cast<float*>(workspace);
+    if (A.splits > 1 && workspace == nullptr) return hipErrorInvalidValue;
+    attend_kernel<<<dim3((unsigned)((int64_t)rows * kv_heads * A.splits)), kNT, 0, stream>>>(A);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || A.splits == 1) return e;
+    attend_merge_kernel<<<dim3((unsigned)((int64_t)rows * q_heads)), kD, 0, stream>>>(A);
     return hipGetLastError();
 }
 

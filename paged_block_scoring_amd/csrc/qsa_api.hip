@@ -290,12 +290,18 @@ QSA_EXPORT qsa_status qsa_topk_rows(const float* scores, int64_t ld_scores, cons
     return QSA_OK;
 }
 
+QSA_EXPORT size_t qsa_sparse_attention_workspace_size(int32_t rows, int32_t q_heads, int32_t kv_heads,
+                                                     int32_t head_dim, int32_t k) {
+    if (head_dim != 256 || kv_heads < 1 || q_heads < kv_heads) return 0;
+    return qsa::attend_workspace_bytes(rows, kv_heads, k);
+}
+
 QSA_EXPORT qsa_status qsa_sparse_attention(const void* q, const void* k_cache, const void* v_cache,
                                            const int32_t* page_table, int64_t pt_stride, int32_t num_pages,
                                            int32_t num_reqs, const int32_t* row_req, const int32_t* tokens,
                                            int32_t k, int32_t rows, int32_t q_heads, int32_t kv_heads,
                                            int32_t head_dim, int32_t page_size, float scale, float* out,
-                                           void* stream) {
+                                           void* workspace, size_t workspace_bytes, void* stream) {
     g_err[0] = 0;
     REQUIRE(rows >= 0, QSA_ERR_INVALID_ARGUMENT, "rows must be >= 0 (got %d)", rows);
     REQUIRE(k >= 1, QSA_ERR_INVALID_ARGUMENT, "k must be >= 1 (got %d)", k);
@@ -311,7 +317,12 @@ QSA_EXPORT qsa_status qsa_sparse_attention(const void* q, const void* k_cache, c
     REQUIRE((uint64_t)num_pages * (uint64_t)page_size * (uint64_t)kv_heads < (1ull << 32), QSA_ERR_UNSUPPORTED,
             "num_pages * page_size * kv_heads must be < 2^32");
     REQUIRE(std::isfinite(scale), QSA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    const size_t need = qsa::attend_workspace_bytes(rows, kv_heads, k);
+    REQUIRE(workspace_bytes >= need, QSA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < required %zu",
+            workspace_bytes, need);
     if (rows == 0) return QSA_OK;
+    REQUIRE(need == 0 || workspace != nullptr, QSA_ERR_INVALID_ARGUMENT, "null pointer: workspace");
+    REQUIRE(need == 0 || aligned16(workspace), QSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
     REQUIRE(q && k_cache && v_cache && page_table && tokens && out, QSA_ERR_INVALID_ARGUMENT,
             "null pointer among q, k_cache, v_cache, page_table, tokens, out");
     REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache), QSA_ERR_INVALID_ARGUMENT,
@@ -322,7 +333,7 @@ QSA_EXPORT qsa_status qsa_sparse_attention(const void* q, const void* k_cache, c
     HIP_CHECK(qsa::launch_attend(static_cast<const _Float16*>(q), static_cast<const _Float16*>(k_cache),
                                  static_cast<const _Float16*>(v_cache), page_table, pt_stride, num_pages, num_reqs,
                                  row_req, tokens, k, rows, q_heads, kv_heads, page_size, scale, out,
-                                 static_cast<hipStream_t>(stream)));
+                                 need > 0 ? workspace : nullptr, static_cast<hipStream_t>(stream)));
     return QSA_OK;
 }
 

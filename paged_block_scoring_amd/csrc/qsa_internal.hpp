@@ -87,11 +87,14 @@ hipError_t launch_fused_final(const PagedArgs& a, const VisibleSource& vis, cons
                               int32_t out_len, int32_t* out, hipStream_t stream);
 
 // Sparse attention over selected tokens (attend.hip): head_dim 256, at most
-// 16 query heads per KV head; out fp32 [rows][q_heads][256].
+// 16 query heads per KV head; out fp32 [rows][q_heads][256].  With few rows
+// each row's list is split over several workgroups whose partial results
+// (attend_workspace_bytes of workspace) a second kernel merges.
+size_t attend_workspace_bytes(int32_t rows, int32_t kv_heads, int32_t k);
 hipError_t launch_attend(const _Float16* q, const _Float16* kc, const _Float16* vc, const int32_t* page_table,
                          int64_t pt_stride, int32_t num_pages, int32_t num_reqs, const int32_t* row_req,
                          const int32_t* tokens, int32_t k, int32_t rows, int32_t q_heads, int32_t kv_heads,
-                         int32_t page_size, float scale, float* out, hipStream_t stream);
+                         int32_t page_size, float scale, float* out, void* workspace, hipStream_t stream);
 
 // Compressed-key producer (compress.hip): finishes the blocks that close in
 // this call and stages the keys of blocks left open; `mark` is called on the

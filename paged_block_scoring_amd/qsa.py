@@ -32,7 +32,7 @@ QSA_MAX_SELECT = 4096
 EXPORTED = (
     "qsa_score_paged", "qsa_topk_rows", "qsa_topk_rows_workspace_size",
     "qsa_select_paged_tokens", "qsa_select_paged_tokens_workspace_size", "qsa_sparse_attention",
-    "qsa_compress_keys", "qsa_last_error", "qsa_last_path", "qsa_version",
+    "qsa_sparse_attention_workspace_size", "qsa_compress_keys", "qsa_last_error", "qsa_last_path", "qsa_version",
     "qsa_debug_record_events", "qsa_debug_events_recorded",
 )
 
@@ -69,7 +69,9 @@ def lib():
     L.qsa_select_paged_tokens_workspace_size.argtypes = [i32, i32, i32, i32, i32, u32]
     L.qsa_select_paged_tokens_workspace_size.restype = sz
     L.qsa_sparse_attention.argtypes = [P, P, P, P, i64, i32, i32, P, P, i32, i32, i32, i32, i32, i32,
-                                       ctypes.c_float, P, P]
+                                       ctypes.c_float, P, P, sz, P]
+    L.qsa_sparse_attention_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.qsa_sparse_attention_workspace_size.restype = sz
     L.qsa_sparse_attention.restype = ctypes.c_int
     L.qsa_compress_keys.argtypes = [P, P, P, i32, i32, P, ctypes.c_float, i32, ctypes.c_double, u32, P, P, P,
                                     i64, i32, i32, i32, i32, P]
@@ -220,8 +222,13 @@ def qsa_topk_rows(scores, k, *, visible=None, max_visible=None, out=None, worksp
     return out
 
 
+def qsa_sparse_attention_workspace_size(rows, q_heads, kv_heads, head_dim, k) -> int:
+    return int(lib().qsa_sparse_attention_workspace_size(int(rows), int(q_heads), int(kv_heads), int(head_dim),
+                                                         int(k)))
+
+
 def qsa_sparse_attention(q, k_cache, v_cache, page_table, tokens, *, row_req=None, scale=None,
-                         out=None) -> torch.Tensor:
+                         out=None, workspace=None) -> torch.Tensor:
     """Softmax attention of every query head over the tokens listed per row
     (entries < 0 skipped), K/V gathered from the paged main cache
     [pages][page_size][kv_heads][head_dim]; fp32 [rows, q_heads, head_dim]."""
@@ -248,10 +255,14 @@ def qsa_sparse_attention(q, k_cache, v_cache, page_table, tokens, *, row_req=Non
     if out is None:
         out = torch.empty((rows, q_heads, head_dim), dtype=torch.float32, device=dev)
     _want(out, "out", torch.float32, dev, 3)
+    need = qsa_sparse_attention_workspace_size(rows, q_heads, kv_heads, head_dim, tokens.shape[1])
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().qsa_sparse_attention(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table), page_table.shape[1], num_pages,
         page_table.shape[0], _ptr(row_req), _ptr(tokens), tokens.shape[1], rows, q_heads, kv_heads, head_dim,
-        page_size, float(scale), _ptr(out), _stream(dev)))
+        page_size, float(scale), _ptr(out), _ptr(workspace), wbytes, _stream(dev)))
     return out
 
 

@@ -160,12 +160,12 @@ def test_binding_refuses_host_tensors():
 def attend(**over):
     a = dict(q=FAKE, kc=FAKE, vc=FAKE, page_table=FAKE, pt_stride=16, num_pages=16, num_reqs=1, row_req=None,
              tokens=FAKE, k=2048, rows=8, q_heads=24, kv_heads=2, head_dim=256, page_size=64, scale=0.0625,
-             out=FAKE, stream=None)
+             out=FAKE, workspace=FAKE, workspace_bytes=1 << 30, stream=None)
     a.update(over)
     st = Q.lib().qsa_sparse_attention(
         a["q"], a["kc"], a["vc"], a["page_table"], a["pt_stride"], a["num_pages"], a["num_reqs"], a["row_req"],
         a["tokens"], a["k"], a["rows"], a["q_heads"], a["kv_heads"], a["head_dim"], a["page_size"], a["scale"],
-        a["out"], a["stream"])
+        a["out"], a["workspace"], a["workspace_bytes"], a["stream"])
     return st, Q.qsa_last_error()
 
 
@@ -186,6 +186,9 @@ def attend(**over):
     (dict(vc=None), Q.QSA_ERR_INVALID_ARGUMENT),
     (dict(out=None), Q.QSA_ERR_INVALID_ARGUMENT),
     (dict(q=FAKE + 4), Q.QSA_ERR_INVALID_ARGUMENT),            # misaligned
+    (dict(workspace_bytes=1000), Q.QSA_ERR_WORKSPACE_TOO_SMALL),  # 8 rows split over several workgroups
+    (dict(workspace=None), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(workspace=FAKE + 8), Q.QSA_ERR_INVALID_ARGUMENT),    # misaligned
 ])
 def test_attention_rejects_before_device(over, code):
     st, msg = attend(**over)
@@ -245,4 +248,25 @@ def test_compress_edge_arguments_pass_the_host_checks():
     assert st == Q.QSA_OK, msg
     # rope_dim 0 ignores the base
     st, msg = compress(tokens=0, rope_dim=0, rope_base=0.0)
+    assert st == Q.QSA_OK, msg
+
+
+def test_attention_workspace_sizes():
+    ws = Q.qsa_sparse_attention_workspace_size
+    # 256 rows x 2 KV heads fill the device: no split, no workspace
+    assert ws(256, 24, 2, 256, 2048) == 0
+    assert ws(2000, 24, 2, 256, 2048) == 0
+    # few rows: each (row, KV head) splits its list; one record per split
+    one = ws(1, 24, 2, 256, 2048)
+    eight = ws(8, 24, 2, 256, 2048)
+    assert one > 0 and eight > 0
+    assert eight % (8 * 2) == 0 and one % 2 == 0
+    # lists are not split below 128 entries per split
+    assert ws(1, 24, 2, 256, 100) == 0
+    assert ws(1, 24, 2, 256, 256) == 2 * 2 * (32 + 16 * 256) * 4
+    # unsupported shapes need nothing
+    assert ws(1, 24, 2, 128, 2048) == 0
+    assert ws(0, 24, 2, 256, 2048) == 0
+    # a large enough workspace passes the host checks (zero rows: nothing runs)
+    st, msg = attend(rows=0, workspace_bytes=eight)
     assert st == Q.QSA_OK, msg

@@ -94,6 +94,35 @@ def test_attention_large_scores():
     check(q, k, v, pt, tok, rr)
 
 
+def test_attention_split_lists():
+    """Few rows split each list over several workgroups (a workspace holds the
+    partial results): tokens only in the first or only in the last split,
+    every split but one empty, an empty row, and scores far from zero in
+    different splits."""
+    rng, q, k, v, pt, rr = make_cache(15, reqs=2, ctx=6000, rows=5)
+    kmax = 2048
+    assert Q.qsa_sparse_attention_workspace_size(5, 24, 2, 256, kmax) > 0
+    tok = np.full((5, kmax), -1, np.int32)
+    tok[0, :5] = rng.choice(6000, 5, replace=False)             # first split only
+    tok[1, kmax - 7:] = rng.choice(6000, 7, replace=False)      # last split only
+    tok[2, ::500] = rng.choice(6000, len(range(0, kmax, 500)), replace=False)  # one token in a few splits
+    tok[4, :] = rng.choice(6000, kmax, replace=False)           # every split full
+    q[4] *= np.float16(5)                                       # large scores, maxima in different splits
+    check(q, k, v, pt, tok, rr)
+
+
+def test_attention_many_rows_no_split():
+    """Enough (row, KV head) pairs to fill the device: one workgroup per pair,
+    no workspace."""
+    rows = 260
+    assert Q.qsa_sparse_attention_workspace_size(rows, 24, 2, 256, 300) == 0
+    rng, q, k, v, pt, rr = make_cache(16, reqs=4, ctx=3000, rows=rows)
+    tok = np.stack([rng.choice(3000, 300, replace=False) for _ in range(rows)]).astype(np.int32)
+    tok[7, 100:] = -1
+    tok[8, :] = -1
+    check(q, k, v, pt, tok, rr)
+
+
 def test_attention_after_the_indexer():
     """End to end on a reduced kernel shape (80 rows of a 184k context): the
     indexer's token selection feeds the consumer."""

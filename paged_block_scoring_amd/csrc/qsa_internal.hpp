@@ -28,7 +28,10 @@ struct PagedArgs {
 // Head sums of the query rows (default form) in the MFMA fragment order of
 // the row-tiled scorer: qsum[((tile*4 + wave)*16 + t)*64 + lane] holds 8
 // fp16 values, t = 2*slice + (0: hi, 1: lo); zero for rows past the end.
+// After the fragments: one int32 per tile of 128 rows, the largest visible-key
+// count of its rows (qsum_tile_visible).
 size_t qsum_bytes(int32_t rows);
+const int32_t* qsum_tile_visible(const _Float16* qsum, int32_t rows);
 hipError_t launch_qsum_prep(const PagedArgs& a, _Float16* qsum, hipStream_t stream);
 
 // Scorer: writes scores[r*ld + j] for j < V_r.  qsum (default form) may be

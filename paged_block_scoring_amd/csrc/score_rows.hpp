@@ -66,6 +66,7 @@ struct RowsArgs {
     int32_t stride;    // logical key i is key stride*i
     int32_t lmax;      // logical keys of the longest row: ceil(max_visible / stride)
     int32_t tiles;     // ceil(rows / 128)
+    const int32_t* tile_v; // [tiles] visible keys of each tile's longest row, or null (see below)
     int32_t xcd_keys;  // logical keys per XCD stripe (a multiple of 32)
     int32_t kpp_shift; // log2(keys per page) when that is a power of two, else -1
     int64_t seg_len;   // (tile, key) positions per workgroup (a multiple of 32)
@@ -217,14 +218,93 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
     const PagedArgs& a = A.a;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int xcd = blockIdx.x % kXcds, loc = blockIdx.x / kXcds;
+    // Work positions of this XCD.  Without tile counts: keys xk0 .. xk0+span
+    // of the XCD's stripe of the longest row, for every tile.  With them
+    // (tile_v): each tile's own visible keys cut into 8 stripes, this XCD's
+    // stripe of every tile laid end to end, and the workgroups of the XCD
+    // share that total evenly, so that tiles of short rows cost nothing.
+    // Stripes are padded to whole stages so that every piece starts on a
+    // stage boundary (keys past the end are invisible to every row).
+    const bool bal = A.tile_v != nullptr;
     const int xk0 = xcd * A.xcd_keys;
-    // keys of this XCD's stripe, padded to whole stages so that every piece
-    // starts on a stage boundary (keys past the end are invisible to every row)
     const int span = min(A.xcd_keys, (A.lmax - xk0 + STEP - 1) / STEP * STEP);
-    if (span <= 0) return;
-    const int64_t total = (int64_t)A.tiles * span;
-    int64_t p = (int64_t)loc * A.seg_len;
-    const int64_t pend = min(p + A.seg_len, total);
+    if (!bal && span <= 0) return;
+    // this XCD's stage-padded share of tile t's keys; *st = the tile's stripe
+    auto share = [&](int t, int* st) {
+        const int lv = (A.tile_v[t] + A.stride - 1) / A.stride;
+        *st = ((lv + kXcds - 1) / kXcds + STEP - 1) / STEP * STEP;
+        const int u = min(max(lv - xcd * *st, 0), *st);
+        return (u + STEP - 1) / STEP * STEP;
+    };
+    int64_t p, pend;
+    int tcur = 0, ucur = 0, stcur = 0;  // balanced mapping: the tile holding p, its share and stripe
+    int64_t pbase = 0;                  // ... and the position where its share starts
+    if (bal) {
+        __shared__ int32_t s_ws[NT / 64];
+        __shared__ int64_t s_found;
+        // an inclusive block scan of the shares of tiles t0 .. t0+NT-1
+        auto scan = [&](int t0, int& u, int& incl, int& chunk) {
+            int st;
+            u = t0 + tid < A.tiles ? share(t0 + tid, &st) : 0;
+            incl = u;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int nb = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += nb;
+            }
+            if (lane == 63) s_ws[wave] = incl;
+            __syncthreads();
+            chunk = 0;
+#pragma unroll
+            for (int w = 0; w < NT / 64; ++w) {
+                incl += w < wave ? s_ws[w] : 0;
+                chunk += s_ws[w];
+            }
+            __syncthreads();
+        };
+        int64_t total = 0;
+        int u0 = 0, incl0 = 0;  // the first chunk's scan, kept for the search below
+        for (int t0 = 0; t0 < A.tiles; t0 += NT) {
+            int u, incl, chunk;
+            scan(t0, u, incl, chunk);
+            if (t0 == 0) {
+                u0 = u;
+                incl0 = incl;
+            }
+            total += chunk;
+        }
+        const int64_t per = gridDim.x / kXcds;
+        const int64_t seg = max<int64_t>(STEP, ((total + per - 1) / per + STEP - 1) / STEP * STEP);
+        p = (int64_t)loc * seg;
+        pend = min(p + seg, total);
+        if (p < pend) {
+            // the tile whose share holds p (exactly one thread finds it); with
+            // at most NT tiles the first scan already holds every prefix
+            if (tid == 0) s_found = -1;
+            __syncthreads();
+            if (A.tiles <= NT) {
+                if (u0 > 0 && incl0 - u0 <= p && p < incl0)
+                    s_found = ((int64_t)tid << 32) | (uint64_t)(uint32_t)(incl0 - u0);
+            } else {
+                int64_t base = 0;
+                for (int t0 = 0; t0 < A.tiles; t0 += NT) {
+                    int u, incl, chunk;
+                    scan(t0, u, incl, chunk);
+                    if (u > 0 && base + incl - u <= p && p < base + incl)
+                        s_found = ((int64_t)(t0 + tid) << 32) | (uint64_t)(uint32_t)(base + incl - u);
+                    base += chunk;
+                }
+            }
+            __syncthreads();
+            tcur = (int)(s_found >> 32);
+            pbase = (int64_t)(uint32_t)(s_found & 0xFFFFFFFFll);
+            ucur = share(tcur, &stcur);
+        }
+    } else {
+        const int64_t total = (int64_t)A.tiles * span;
+        p = (int64_t)loc * A.seg_len;
+        pend = min(p + A.seg_len, total);
+    }
 
     // staging: this thread's NLOAD consecutive keys of a stage and its chunk
     const int pk = NLOAD * (tid >> 4), pc = tid & 15;
@@ -287,10 +367,24 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
     };
 
     while (p < pend) {
-        const int tile = (int)(p / span);
-        const int off = (int)(p - (int64_t)tile * span);
-        const int len = (int)min<int64_t>(min<int64_t>((int64_t)(span - off), pend - p), (int64_t)kRowsPiece);
-        const int c0 = xk0 + off, c1 = c0 + len;
+        int tile, len, c0;
+        if (bal) {
+            while (p >= pbase + ucur) {  // on to the next tile with keys on this XCD
+                pbase += ucur;
+                ++tcur;
+                ucur = share(tcur, &stcur);
+            }
+            tile = tcur;
+            const int off = (int)(p - pbase);
+            len = (int)min<int64_t>(min<int64_t>((int64_t)(ucur - off), pend - p), (int64_t)kRowsPiece);
+            c0 = xcd * stcur + off;
+        } else {
+            tile = (int)(p / span);
+            const int off = (int)(p - (int64_t)tile * span);
+            len = (int)min<int64_t>(min<int64_t>((int64_t)(span - off), pend - p), (int64_t)kRowsPiece);
+            c0 = xk0 + off;
+        }
+        const int c1 = c0 + len;
         p += len;
         const int r0 = tile * TILE;
         const bool new_tile = r0 != tile_r0;

@@ -252,28 +252,82 @@ __global__ __launch_bounds__(kRegNT) void topk_regs_kernel(TopkArgs A) {
             else
                 k[e] = e * kRegNT + tid < V ? ke : 0u;
         }
-        if (tid == 0) L.nc = 0;
         const auto key = [&](int e) { return k[e]; };
         uint32_t mn, mx;
         block_minmax_u32<kRegNT, EPT>(key, V, &mn, &mx, &L.s.hs);  // (slots wholly past V skipped)
         const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
-        int above, cnt;
-        const uint32_t b = hist_level32<kRegNT, EPT>(key, V, mn, shift1, 32, 0u, nsel, &L.s.hs, nullptr, &above, &cnt);
-        const uint32_t lo = mn + (b << shift1);
-        const int surv = above + cnt;  // keys >= lo (lo >= the smallest key > 0)
-        if (surv <= kCompact) {
+        // A cheap bound first: the histogram of every 8th slot gives the bin of
+        // its m-th largest key (m covers nsel/8 with a margin); the keys at or
+        // above that bin's lower edge are then counted exactly.  With at least
+        // nsel of them they hold the row's top nsel; with too few or too many
+        // the histogram of every key decides instead.
+        uint32_t lo = 0u;
+        int surv = -1;
+        if constexpr (EPT >= 64) {
+            constexpr int S = EPT / 8;
+            int sampled = 0;  // nonzero keys in slots 0, 8, 16, ...
 #pragma unroll
-            for (int e = 0; e < EPT; ++e)
-                if (k[e] >= lo) L.c[atomicAdd(&L.nc, 1)] = compose(k[e], (uint32_t)(e * kRegNT + fresh(tid)));
+            for (int j = 0; j < S; ++j) sampled += min(max(V - 8 * j * kRegNT, 0), kRegNT);
+            const float q = (float)nsel / 8.0f;
+            const int m = (int)(q + 3.0f * sqrtf(q) + 8.0f);
+            if (m <= sampled) {
+                int sa, sc;
+                const auto skey = [&](int j) { return k[8 * j]; };
+                const uint32_t bs = hist_level32<kRegNT, S>(skey, (V + 7) / 8, mn, shift1, 32, 0u, m, &L.s.hs,
+                                                            nullptr, &sa, &sc);
+                lo = mn + (bs << shift1);
+                int c = 0;
+#pragma unroll
+                for (int e = 0; e < EPT; ++e) c += k[e] >= lo ? 1 : 0;
+                int total;
+                (void)block_inclusive_scan<kRegNT>(c, L.s.hs.wsum, &total);
+                surv = total;
+            }
+        }
+        if (surv < nsel || surv > kCompact) {
+            int above, cnt;
+            const uint32_t b = hist_level32<kRegNT, EPT>(key, V, mn, shift1, 32, 0u, nsel, &L.s.hs, nullptr, &above, &cnt);
+            lo = mn + (b << shift1);
+            surv = above + cnt;  // keys >= lo (lo >= the smallest key > 0)
+        }
+        if (surv <= kCompact) {
+            if (tid == 0) L.nc = 0;
+            __syncthreads();
+            // the survivors, eight slots at a time: one LDS atomic per wave and
+            // batch reserves the batch's places, ballots order the lanes
+            const int lane = tid & 63;
+            const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+            for (int g = 0; g < EPT; g += 8) {
+                uint64_t mk[8];
+                int tot = 0;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    mk[u] = __ballot(g + u < EPT && k[g + u] >= lo);
+                    tot += __popcll(mk[u]);
+                }
+                if (tot) {  // (wave-uniform)
+                    int at = 0;
+                    if (lane == 0) at = atomicAdd(&L.nc, tot);
+                    at = __builtin_amdgcn_readfirstlane(at);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        if (g + u < EPT && ((mk[u] >> lane) & 1ull))
+                            L.c[at + __popcll(mk[u] & below)] =
+                                compose(k[g + u], (uint32_t)((g + u) * kRegNT + fresh(tid)));
+                        at += __popcll(mk[u]);
+                    }
+                }
+            }
             __syncthreads();
             constexpr int E2 = kCompact / kRegNT;
             uint32_t k2[E2], i2[E2];
 #pragma unroll
             for (int e = 0; e < E2; ++e) {
                 const int p = e * kRegNT + tid;
-                const uint64_t c = p < surv ? L.c[p] : 0ull;
-                k2[e] = (uint32_t)(c >> 32);
-                i2[e] = composite_index(c);
+                const uint64_t ce = p < surv ? L.c[p] : 0ull;
+                k2[e] = (uint32_t)(ce >> 32);
+                i2[e] = composite_index(ce);
             }
             select_from_bound<kRegNT, E2, KBMAX>(k2, [&](int e) { return i2[e]; }, surv, nsel, lo, L.s, emit);
         } else {

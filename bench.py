@@ -342,8 +342,8 @@ def main():
     if args.summarize_profile:
         return summarize_profile(args)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(the indexer shards across GPUs only as a design, see the design notes)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(sharding the indexer across GPUs is not implemented)", file=sys.stderr)
         return 2
     if args.path:
         os.environ["QSA_FORCE_PATH"] = args.path

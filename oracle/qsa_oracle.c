@@ -22,8 +22,7 @@
  *  [thor]  "qwen4_exp QSA cooperative_topk cannot launch on NVIDIA Thor
  *          (sm_110): cluster misconfiguration", section "What happens".
  *
- * Readings taken where the pages leave a step open (each also listed in the
- * repository's design notes):
+ * Readings taken where the pages leave a step open:
  *  - Default score: the per-head dot products summed over the index heads in
  *    fp32, no relu and no scale (the plain sum the measured workloads are
  *    defined with).  With ORACLE_SCORE_RELU the [spec] form is used: relu on

@@ -246,6 +246,19 @@ def test_edges(oracle_mod):
     full_parity(oracle_mod, one, 0, True, paths=PATHS)
 
 
+def test_tiles_without_keys(oracle_mod):
+    """Several requests (the scorer then shares each tile's own visible keys
+    among its workgroups): a whole 128-row tile whose rows see no key at all,
+    a tile mixing such rows with rows of a long context, and a short and a long
+    request side by side; every arm, integer inputs, end to end."""
+    rng = np.random.default_rng(44)
+    w = W.build("tiles", rng, 44, [20000, 300, 9000, 40], [128, 200, 70, 30], permute_pages=True, integer=True,
+                k=2048)
+    w.pos = w.pos.copy()
+    w.pos[128:328] = np.arange(200) % 3          # request 1: positions 0..2, no visible key
+    full_parity(oracle_mod, w, 0, True, paths=PATHS)
+
+
 @pytest.mark.parametrize("name,path", [("kernel_shape_80", "fused"), ("decode_small", "two_pass"),
                                        ("mixed_small", "fused_fallback")])
 def test_graph_capture(oracle_mod, name, path):

@@ -188,14 +188,19 @@ FusedLayout fused_layout(int32_t rows, int32_t max_visible, int32_t kb) {
 enum class Path { TwoPass, Fused };
 
 // The fused arm scores every key twice over a 1/16 sample but never writes
-// the score matrix; it pays off when many rows share each request's keys.
-// Few rows per request (decode) stream each key once through the two-pass arm.
+// the score matrix; it pays off when many rows share each request's keys and
+// there is enough work to cover its five launches (measured crossover: rows x
+// longest row between 4.2 M and 6.6 M keys).  Few rows per request (decode),
+// and small batches, take the two-pass arm.
+constexpr int64_t kFusedMinWork = 5000000;
+
 Path choose_path(int32_t rows, int32_t num_reqs, int32_t max_visible) {
     const char* f = getenv("QSA_FORCE_PATH");
     if (f && strcmp(f, "two_pass") == 0) return Path::TwoPass;
     if (f && strcmp(f, "fused") == 0) return Path::Fused;
     if (max_visible <= 0) return Path::TwoPass;
-    return (rows / (num_reqs > 0 ? num_reqs : 1) >= 32) ? Path::Fused : Path::TwoPass;
+    if (rows / (num_reqs > 0 ? num_reqs : 1) < 32) return Path::TwoPass;
+    return (int64_t)rows * max_visible >= kFusedMinWork ? Path::Fused : Path::TwoPass;
 }
 
 bool force_fallback() {

@@ -300,7 +300,7 @@ __device__ __forceinline__ Descent hist_descent32(KeyF key, int nmax, int need, 
 // ---------------------------------------------------------------------------
 // Selection of a row's top-nsel from keys held by the workgroup's threads.
 
-constexpr int kMaxBucket = 32;
+constexpr int kMaxBucket = 256;
 
 template <int KBMAX>
 struct BoundSelectLds {

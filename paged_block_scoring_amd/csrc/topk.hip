@@ -187,9 +187,9 @@ __global__ __launch_bounds__(kNT) void topk_rows_kernel(TopkArgs A) {
     }
 }
 
-// Rows whose visible keys fit in registers (V <= kRegNT * EPT).  Every
-// score is loaded once, all loads issued before any use, and kept as its
-// order key (element e of thread t is key e*kRegNT + t).  One histogram level
+// Rows whose visible keys fit in registers (V <= NT * EPT, with NT threads
+// per workgroup).  Every score is loaded once, all loads issued before any
+// use, and kept as its order key (element e of thread t is key e*NT + t).  One histogram level
 // over the row (kSelBins bins of a power-of-two width between its smallest
 // and largest key) finds the bin holding the kk-th largest; the keys from that
 // bin's lower edge up -- usually a few more than kk -- are compacted into LDS,
@@ -197,10 +197,10 @@ __global__ __launch_bounds__(kNT) void topk_rows_kernel(TopkArgs A) {
 // sort at all.  If more than kCompact keys survive (heavy ties or clustering
 // at the cut), the row is selected by select_exact_sorted instead, with keys
 // re-read from the score row at each level.
-constexpr int kRegNT = 512;
+constexpr int kRegNT = 512;  // threads per workgroup for rows of 8,193 .. 49,152 keys
 
 // x, with the compiler unable to reuse an earlier expression built from it:
-// element indices e*kRegNT + tid are then formed where used instead of being
+// element indices e*NT + tid are then formed where used instead of being
 // held in EPT registers across the kernel.
 __device__ __forceinline__ int fresh(int x) {
     asm volatile("" : "+v"(x));
@@ -217,21 +217,21 @@ struct TopkRegsLds {
 
 // The rare path of topk_regs_kernel, kept out of line so that its register
 // needs do not constrain the common path.
-template <int EPT, int KBMAX>
+template <int NT, int EPT, int KBMAX>
 __device__ __noinline__ void topk_row_exact_sorted(const uint32_t* srow, int V, int nsel, BoundSelectLds<KBMAX>* L,
                                                    int32_t* orow, int expand, bool vec4) {
     const int tid = threadIdx.x;
-    select_exact_sorted<kRegNT, EPT, KBMAX>(
+    select_exact_sorted<NT, EPT, KBMAX>(
         [&](int e) {
-            const int j = e * kRegNT + tid;
+            const int j = e * NT + tid;
             return j < V ? order_key(__uint_as_float(srow[j])) : 0u;
         },
-        [&](int e) { return (uint32_t)(e * kRegNT + tid); }, V, nsel, *L,
+        [&](int e) { return (uint32_t)(e * NT + tid); }, V, nsel, *L,
         [&](int r, uint64_t c) { write_rank(orow, r, composite_index(c), expand, vec4); });
 }
 
-template <int EPT, int KBMAX>
-__global__ __launch_bounds__(kRegNT) void topk_regs_kernel(TopkArgs A) {
+template <int NT, int EPT, int KBMAX>
+__global__ __launch_bounds__(NT) void topk_regs_kernel(TopkArgs A) {
     __shared__ TopkRegsLds<KBMAX> L;
     const int row = blockIdx.x, tid = threadIdx.x;
     const int V = row_visible(A.vis, row);
@@ -243,18 +243,18 @@ __global__ __launch_bounds__(kRegNT) void topk_regs_kernel(TopkArgs A) {
         const uint32_t* srow = reinterpret_cast<const uint32_t*>(A.scores + (int64_t)row * A.ld);
         uint32_t k[EPT];
 #pragma unroll
-        for (int e = 0; e < EPT; ++e) k[e] = srow[min(e * kRegNT + tid, V - 1)];
+        for (int e = 0; e < EPT; ++e) k[e] = srow[min(e * NT + tid, V - 1)];
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {  // keys past V become 0 (a per-lane test only in the slot V falls in)
             const uint32_t ke = order_key(__uint_as_float(k[e]));
-            if ((e + 1) * kRegNT <= V)
+            if ((e + 1) * NT <= V)
                 k[e] = ke;
             else
-                k[e] = e * kRegNT + tid < V ? ke : 0u;
+                k[e] = e * NT + tid < V ? ke : 0u;
         }
         const auto key = [&](int e) { return k[e]; };
         uint32_t mn, mx;
-        block_minmax_u32<kRegNT, EPT>(key, V, &mn, &mx, &L.s.hs);  // (slots wholly past V skipped)
+        block_minmax_u32<NT, EPT>(key, V, &mn, &mx, &L.s.hs);  // (slots wholly past V skipped)
         const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
         // A cheap bound first: the histogram of every 8th slot gives the bin of
         // its m-th largest key (m covers nsel/8 with a margin); the keys at or
@@ -267,26 +267,26 @@ __global__ __launch_bounds__(kRegNT) void topk_regs_kernel(TopkArgs A) {
             constexpr int S = EPT / 8;
             int sampled = 0;  // nonzero keys in slots 0, 8, 16, ...
 #pragma unroll
-            for (int j = 0; j < S; ++j) sampled += min(max(V - 8 * j * kRegNT, 0), kRegNT);
+            for (int j = 0; j < S; ++j) sampled += min(max(V - 8 * j * NT, 0), NT);
             const float q = (float)nsel / 8.0f;
             const int m = (int)(q + 3.0f * sqrtf(q) + 8.0f);
             if (m <= sampled) {
                 int sa, sc;
                 const auto skey = [&](int j) { return k[8 * j]; };
-                const uint32_t bs = hist_level32<kRegNT, S>(skey, (V + 7) / 8, mn, shift1, 32, 0u, m, &L.s.hs,
+                const uint32_t bs = hist_level32<NT, S>(skey, (V + 7) / 8, mn, shift1, 32, 0u, m, &L.s.hs,
                                                             nullptr, &sa, &sc);
                 lo = mn + (bs << shift1);
                 int c = 0;
 #pragma unroll
                 for (int e = 0; e < EPT; ++e) c += k[e] >= lo ? 1 : 0;
                 int total;
-                (void)block_inclusive_scan<kRegNT>(c, L.s.hs.wsum, &total);
+                (void)block_inclusive_scan<NT>(c, L.s.hs.wsum, &total);
                 surv = total;
             }
         }
         if (surv < nsel || surv > kCompact) {
             int above, cnt;
-            const uint32_t b = hist_level32<kRegNT, EPT>(key, V, mn, shift1, 32, 0u, nsel, &L.s.hs, nullptr, &above, &cnt);
+            const uint32_t b = hist_level32<NT, EPT>(key, V, mn, shift1, 32, 0u, nsel, &L.s.hs, nullptr, &above, &cnt);
             lo = mn + (b << shift1);
             surv = above + cnt;  // keys >= lo (lo >= the smallest key > 0)
         }
@@ -314,35 +314,35 @@ __global__ __launch_bounds__(kRegNT) void topk_regs_kernel(TopkArgs A) {
                     for (int u = 0; u < 8; ++u) {
                         if (g + u < EPT && ((mk[u] >> lane) & 1ull))
                             L.c[at + __popcll(mk[u] & below)] =
-                                compose(k[g + u], (uint32_t)((g + u) * kRegNT + fresh(tid)));
+                                compose(k[g + u], (uint32_t)((g + u) * NT + fresh(tid)));
                         at += __popcll(mk[u]);
                     }
                 }
             }
             __syncthreads();
-            constexpr int E2 = kCompact / kRegNT;
+            constexpr int E2 = kCompact / NT;
             uint32_t k2[E2], i2[E2];
 #pragma unroll
             for (int e = 0; e < E2; ++e) {
-                const int p = e * kRegNT + tid;
+                const int p = e * NT + tid;
                 const uint64_t ce = p < surv ? L.c[p] : 0ull;
                 k2[e] = (uint32_t)(ce >> 32);
                 i2[e] = composite_index(ce);
             }
-            select_from_bound<kRegNT, E2, KBMAX>(k2, [&](int e) { return i2[e]; }, surv, nsel, lo, L.s, emit);
+            select_from_bound<NT, E2, KBMAX>(k2, [&](int e) { return i2[e]; }, surv, nsel, lo, L.s, emit);
         } else {
-            topk_row_exact_sorted<EPT, KBMAX>(srow, V, nsel, &L.s, orow, A.expand, vec4);
+            topk_row_exact_sorted<NT, EPT, KBMAX>(srow, V, nsel, &L.s, orow, A.expand, vec4);
         }
     }
-    for (int i = nsel * A.expand + tid; i < A.out_len; i += kRegNT) orow[i] = -1;
+    for (int i = nsel * A.expand + tid; i < A.out_len; i += NT) orow[i] = -1;
 }
 
-template <int EPT>
+template <int NT, int EPT>
 void launch_regs(const TopkArgs& A, int32_t rows, hipStream_t stream) {
     if (A.kk <= 1024)
-        topk_regs_kernel<EPT, 1024><<<dim3((unsigned)rows), kRegNT, 0, stream>>>(A);
+        topk_regs_kernel<NT, EPT, 1024><<<dim3((unsigned)rows), NT, 0, stream>>>(A);
     else
-        topk_regs_kernel<EPT, QSA_MAX_SELECT><<<dim3((unsigned)rows), kRegNT, 0, stream>>>(A);
+        topk_regs_kernel<NT, EPT, QSA_MAX_SELECT><<<dim3((unsigned)rows), NT, 0, stream>>>(A);
 }
 
 }  // namespace
@@ -359,10 +359,12 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, const VisibleSource
     A.expand = expand;
     A.out_len = out_len;
     A.out = out;
-    if (vis.max_visible <= kRegNT * 16)
-        launch_regs<16>(A, rows, stream);
+    // rows of up to 8,192 keys in 256-thread workgroups (several resident per
+    // compute unit), longer ones in 512-thread workgroups
+    if (vis.max_visible <= 256 * 32)
+        launch_regs<256, 32>(A, rows, stream);
     else if (vis.max_visible <= kRegNT * 96)
-        launch_regs<96>(A, rows, stream);
+        launch_regs<kRegNT, 96>(A, rows, stream);
     else
         topk_rows_kernel<<<dim3((unsigned)rows), kNT, 0, stream>>>(A);
     return hipGetLastError();

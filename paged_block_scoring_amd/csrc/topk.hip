@@ -359,9 +359,12 @@ hipError_t launch_topk_rows(const float* scores, int64_t ld, const VisibleSource
     A.expand = expand;
     A.out_len = out_len;
     A.out = out;
-    // rows of up to 8,192 keys in 256-thread workgroups (several resident per
-    // compute unit), longer ones in 512-thread workgroups
-    if (vis.max_visible <= 256 * 32)
+    // rows of up to 8,192 keys: 256-thread workgroups (two resident per compute
+    // unit) when the rows outnumber the compute units, else 512 threads per row
+    // (lower latency); longer rows: 512 threads
+    if (vis.max_visible <= kRegNT * 16 && rows < 256)
+        launch_regs<kRegNT, 16>(A, rows, stream);
+    else if (vis.max_visible <= 256 * 32)
         launch_regs<256, 32>(A, rows, stream);
     else if (vis.max_visible <= kRegNT * 96)
         launch_regs<kRegNT, 96>(A, rows, stream);

@@ -270,3 +270,21 @@ def test_attention_workspace_sizes():
     # a large enough workspace passes the host checks (zero rows: nothing runs)
     st, msg = attend(rows=0, workspace_bytes=eight)
     assert st == Q.QSA_OK, msg
+
+
+def test_binding_refuses_host_tensors_and_bad_shapes_for_the_adjacent_steps():
+    import torch
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)  # noqa: E731
+    f16 = lambda *s: torch.zeros(s, dtype=torch.float16)  # noqa: E731
+    # producer: host tensors are refused before the library is called
+    with pytest.raises(ValueError):
+        Q.qsa_compress_keys(f16(8, 128), i32(8), f16(1, 4, 128), f16(4, 16, 128), i32(1, 4), 4)
+    # wrong dtype
+    with pytest.raises(TypeError):
+        Q.qsa_compress_keys(torch.zeros((8, 128)), i32(8), f16(1, 4, 128), f16(4, 16, 128), i32(1, 4), 4)
+    # consumer: host tensors refused
+    with pytest.raises(ValueError):
+        Q.qsa_sparse_attention(f16(2, 24, 256), f16(4, 64, 2, 256), f16(4, 64, 2, 256), i32(1, 4), i32(2, 16))
+    with pytest.raises(TypeError):
+        Q.qsa_sparse_attention(torch.zeros((2, 24, 256)), f16(4, 64, 2, 256), f16(4, 64, 2, 256), i32(1, 4),
+                               i32(2, 16))

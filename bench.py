@@ -348,11 +348,11 @@ def main():
         print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(sharding the indexer across GPUs is not implemented)", file=sys.stderr)
         return 2
-    if args.path:
-        os.environ["QSA_FORCE_PATH"] = args.path
     import torch
     import workloads as W
     from paged_block_scoring_amd import qsa as Q
+    if args.path:
+        Q.qsa_debug_force({"two_pass": Q.QSA_DEBUG_FORCE_TWO_PASS, "fused": Q.QSA_DEBUG_FORCE_FUSED}[args.path])
 
     w = W.make(args.workload)
     dev = torch.device("cuda:0")

@@ -59,7 +59,11 @@
  *    V_r > max_visible) never causes an out-of-bounds access: page ids are
  *    clamped into range, rows with an invalid request select nothing, and V_r
  *    is clamped to max_visible.  The results for such rows are unspecified.
- *  - Inputs must be finite; NaN scores are outside the contract.
+ *  - Inputs must be finite (any finite fp16 value, up to +-65504 in every
+ *    head; NaN and Inf are outside the contract).  Scores are exact fp16
+ *    products accumulated in fp32, so no finite input overflows them; the
+ *    default form stays exact when the per-dimension sum over heads leaves
+ *    the fp16 range (it is carried divided by 2 or 4, a power of two).
  *  - Calls are thread-safe.  Library state is a per-device properties cache
  *    and a thread-local error string.
  *  - Indices are logical positions within the request (key j, token t); the
@@ -294,10 +298,25 @@ const char* qsa_version(void);
  * passed as void*; they must stay valid until that call returns).  The call
  * disarms the hook; qsa_debug_events_recorded() then returns how many events
  * it recorded.  Kernel order: two-pass arm = scorer, selector; fused arm =
- * sampling scorer, threshold, filtering scorer, final select; producer =
- * block compression, staging of open blocks (none when compress_ratio is 1). */
+ * head-sum preparation (default form; nothing in the relu form), sampling
+ * scorer, threshold, filtering scorer, final select; producer = block
+ * compression, staging of open blocks (none when compress_ratio is 1). */
 qsa_status qsa_debug_record_events(void* const* events, int32_t n);
 int32_t qsa_debug_events_recorded(void);
+
+/* Overrides of the library's own choices, for tests and benchmarks that must
+ * drive one execution arm or one scorer deliberately.  Process-wide (every
+ * thread and device) until the next qsa_debug_force call; mask 0 restores the
+ * library's choices.  The workspace-size queries follow the forced arm.
+ * Conflicting or unknown bits return QSA_ERR_INVALID_ARGUMENT and change
+ * nothing.  The library reads no environment variables. */
+#define QSA_DEBUG_FORCE_TWO_PASS 0x1u   /* qsa_select_paged_tokens: the two-pass arm */
+#define QSA_DEBUG_FORCE_FUSED    0x2u   /* ... the fused arm */
+#define QSA_DEBUG_FORCE_FALLBACK 0x4u   /* the fused arm, every row on its exact recompute path */
+#define QSA_DEBUG_FORCE_TILES    0x8u   /* materialising scorer: the row-tiled kernel */
+#define QSA_DEBUG_FORCE_GROUPS   0x10u  /* materialising scorer: the windowed kernel */
+qsa_status qsa_debug_force(uint32_t mask);
+uint32_t qsa_debug_forced(void);
 
 #ifdef __cplusplus
 }

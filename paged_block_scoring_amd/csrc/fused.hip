@@ -177,6 +177,22 @@ __device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* 
     const int32_t* ptrow = p.page_table + (int64_t)req * p.pt_stride;
     const _Float16* qrow = p.q + (int64_t)row * kHeads * kHeadDim;
     const int m = lane & 31, g = lane >> 5;
+    // default form: the row's head-sum factor f; the row is ranked on chain
+    // results (score / f), as the filtering pass ranks it
+    float inv_f = 1.0f;
+    if (!p.relu) {
+        float um = 0.0f;
+#pragma unroll
+        for (int s = 0; s < kSlices; ++s) {
+            const _Float16* qs = qrow + 16 * s + 8 * g;
+            um = fmaxf(um, head_sum_absmax(*reinterpret_cast<const half8*>(qs),
+                                           *reinterpret_cast<const half8*>(qs + kHeadDim),
+                                           *reinterpret_cast<const half8*>(qs + 2 * kHeadDim),
+                                           *reinterpret_cast<const half8*>(qs + 3 * kHeadDim)));
+        }
+        um = fmaxf(um, __shfl_xor(um, 32, 64));
+        inv_f = 1.0f / head_sum_factor(um);
+    }
     int na = 0;
     uint64_t cut = 0ull;  // composites must exceed this to matter once na == kb
     for (int c0 = 0; c0 < V; c0 += ch) {
@@ -213,7 +229,7 @@ __device__ int recompute_row_topk(const FinalArgs& A, int row, int V, uint64_t* 
 #pragma unroll
                         for (int hh = 0; hh < kHeads; ++hh)
                             h[hh] = *reinterpret_cast<const half8*>(qrow + hh * kHeadDim + 16 * s + 8 * g);
-                        head_sum_split(h[0], h[1], h[2], h[3], hi, lo);
+                        head_sum_split(h[0], h[1], h[2], h[3], inv_f, hi, lo);
                     }
                     acc = mfma32(kb8[s], hi, acc);
                     acc = mfma32(kb8[s], lo, acc);

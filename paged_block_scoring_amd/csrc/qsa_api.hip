@@ -9,6 +9,7 @@
 // than a capability proxy (the same page, section "What the source says").
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -60,7 +61,7 @@ qsa_status fail_at(const char* file, int line, qsa_status code, const char* fmt,
 
 constexpr int kMaxDevices = 64;
 struct DeviceInfo {
-    bool probed = false;
+    std::atomic<bool> probed{false};  // set (release) once the fields below are final
     bool supported = false;
     int cus = 0;
     size_t lds = 0;
@@ -69,22 +70,28 @@ struct DeviceInfo {
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
 
+// Arm and scorer overrides set by qsa_debug_force (QSA_DEBUG_FORCE_* bits).
+std::atomic<uint32_t> g_force{0};
+
 // Identify the current device once: the kernels are written for gfx950
 // (CDNA4) and its 64-wide wavefronts, 16x16x32 f16 MFMA and 160 KB LDS.
+// After the first call per device this is one hipGetDevice and one load.
 qsa_status check_device(const DeviceInfo** out) {
     int dev = -1;
     HIP_CHECK(hipGetDevice(&dev));
     REQUIRE(dev >= 0 && dev < kMaxDevices, QSA_ERR_UNSUPPORTED, "device index %d out of range", dev);
-    std::lock_guard<std::mutex> lock(g_dev_mu);
     DeviceInfo& d = g_dev[dev];
-    if (!d.probed) {
-        hipDeviceProp_t p;
-        HIP_CHECK(hipGetDeviceProperties(&p, dev));
-        snprintf(d.arch, sizeof d.arch, "%s", p.gcnArchName);
-        d.cus = p.multiProcessorCount;
-        d.lds = p.sharedMemPerBlock;
-        d.supported = strncmp(d.arch, "gfx950", 6) == 0 && p.warpSize == 64 && d.lds >= 64 * 1024;
-        d.probed = true;
+    if (!d.probed.load(std::memory_order_acquire)) {
+        std::lock_guard<std::mutex> lock(g_dev_mu);
+        if (!d.probed.load(std::memory_order_relaxed)) {
+            hipDeviceProp_t p;
+            HIP_CHECK(hipGetDeviceProperties(&p, dev));
+            snprintf(d.arch, sizeof d.arch, "%s", p.gcnArchName);
+            d.cus = p.multiProcessorCount;
+            d.lds = p.sharedMemPerBlock;
+            d.supported = strncmp(d.arch, "gfx950", 6) == 0 && p.warpSize == 64 && d.lds >= 64 * 1024;
+            d.probed.store(true, std::memory_order_release);
+        }
     }
     REQUIRE(d.supported, QSA_ERR_UNSUPPORTED,
             "device %d is %s; this library is built for gfx950 (MI355X)", dev, d.arch);
@@ -195,23 +202,21 @@ enum class Path { TwoPass, Fused };
 constexpr int64_t kFusedMinWork = 5000000;
 
 Path choose_path(int32_t rows, int32_t num_reqs, int32_t max_visible) {
-    const char* f = getenv("QSA_FORCE_PATH");
-    if (f && strcmp(f, "two_pass") == 0) return Path::TwoPass;
-    if (f && strcmp(f, "fused") == 0) return Path::Fused;
+    const uint32_t f = g_force.load(std::memory_order_relaxed);
+    if (f & QSA_DEBUG_FORCE_TWO_PASS) return Path::TwoPass;
+    if (f & (QSA_DEBUG_FORCE_FUSED | QSA_DEBUG_FORCE_FALLBACK)) return Path::Fused;
     if (max_visible <= 0) return Path::TwoPass;
     if (rows / (num_reqs > 0 ? num_reqs : 1) < 32) return Path::TwoPass;
     return (int64_t)rows * max_visible >= kFusedMinWork ? Path::Fused : Path::TwoPass;
 }
 
-bool force_fallback() {
-    const char* f = getenv("QSA_DEBUG_FORCE_FALLBACK");
-    return f && f[0] == '1';
-}
+bool force_fallback() { return (g_force.load(std::memory_order_relaxed) & QSA_DEBUG_FORCE_FALLBACK) != 0; }
 
-int device_cus() {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    return cus;
+qsa::ScorerChoice scorer_choice() {
+    const uint32_t f = g_force.load(std::memory_order_relaxed);
+    if (f & QSA_DEBUG_FORCE_TILES) return qsa::ScorerChoice::Tiles;
+    if (f & QSA_DEBUG_FORCE_GROUPS) return qsa::ScorerChoice::Groups;
+    return qsa::ScorerChoice::Auto;
 }
 
 }  // namespace
@@ -230,6 +235,21 @@ QSA_EXPORT qsa_status qsa_debug_record_events(void* const* events, int32_t n) {
 }
 
 QSA_EXPORT int32_t qsa_debug_events_recorded(void) { return g_recorded; }
+
+QSA_EXPORT qsa_status qsa_debug_force(uint32_t mask) {
+    g_err[0] = 0;
+    constexpr uint32_t known = QSA_DEBUG_FORCE_TWO_PASS | QSA_DEBUG_FORCE_FUSED | QSA_DEBUG_FORCE_FALLBACK |
+                               QSA_DEBUG_FORCE_TILES | QSA_DEBUG_FORCE_GROUPS;
+    REQUIRE((mask & ~known) == 0, QSA_ERR_INVALID_ARGUMENT, "unknown debug bits 0x%x", mask & ~known);
+    REQUIRE(!((mask & QSA_DEBUG_FORCE_TWO_PASS) && (mask & (QSA_DEBUG_FORCE_FUSED | QSA_DEBUG_FORCE_FALLBACK))),
+            QSA_ERR_INVALID_ARGUMENT, "the two-pass and the fused arm cannot both be forced (0x%x)", mask);
+    REQUIRE(!((mask & QSA_DEBUG_FORCE_TILES) && (mask & QSA_DEBUG_FORCE_GROUPS)), QSA_ERR_INVALID_ARGUMENT,
+            "the tiled and the windowed scorer cannot both be forced (0x%x)", mask);
+    g_force.store(mask, std::memory_order_relaxed);
+    return QSA_OK;
+}
+
+QSA_EXPORT uint32_t qsa_debug_forced(void) { return g_force.load(std::memory_order_relaxed); }
 
 QSA_EXPORT qsa_status qsa_score_paged(const void* q, const void* kcache, const int32_t* page_table,
                                       int64_t pt_stride, int32_t num_pages, int32_t num_reqs,
@@ -251,7 +271,8 @@ QSA_EXPORT qsa_status qsa_score_paged(const void* q, const void* kcache, const i
     if ((st = check_device(&dev)) != QSA_OK) return st;
     qsa::PagedArgs a = make_paged(q, kcache, page_table, pt_stride, num_pages, num_reqs, row_req, pos, rows,
                                   page_size, compress_ratio, max_visible, flags);
-    HIP_CHECK(qsa::launch_score_paged(a, nullptr, scores, ld_scores, static_cast<hipStream_t>(stream)));
+    HIP_CHECK(qsa::launch_score_paged(a, nullptr, scores, ld_scores, dev->cus, scorer_choice(),
+                                      static_cast<hipStream_t>(stream)));
     return QSA_OK;
 }
 
@@ -444,11 +465,11 @@ QSA_EXPORT qsa_status qsa_select_paged_tokens(const void* q, const void* kcache,
         int32_t* count = reinterpret_cast<int32_t*>(w + L.off_count);
         uint64_t* cand = reinterpret_cast<uint64_t*>(w + L.off_cand);
         _Float16* qsum = a.relu ? nullptr : reinterpret_cast<_Float16*>(w + L.off_qsum);
-        const int cus = device_cus();
+        const int cus = dev->cus;
         HIP_CHECK(mark(s));
         if (qsum) HIP_CHECK(qsa::launch_qsum_prep(a, qsum, s));
         HIP_CHECK(mark(s));
-        HIP_CHECK(qsa::launch_score_store(a, qsum, L.plan.stride, samp, L.plan.ld_s, cus, s));
+        HIP_CHECK(qsa::launch_score_store(a, qsum, L.plan.stride, false, samp, L.plan.ld_s, cus, s));
         HIP_CHECK(mark(s));
         HIP_CHECK(qsa::launch_sample_threshold(samp, L.plan.ld_s, vs, L.plan, force_fallback(), thresh, count, rows, s));
         HIP_CHECK(mark(s));
@@ -466,7 +487,7 @@ QSA_EXPORT qsa_status qsa_select_paged_tokens(const void* q, const void* kcache,
     _Float16* qsum = a.relu ? nullptr
                             : reinterpret_cast<_Float16*>(static_cast<unsigned char*>(workspace) +
                                                           two_pass_scores_bytes(rows, max_visible));
-    if (max_visible > 0) HIP_CHECK(qsa::launch_score_paged(a, qsum, scores, ld, s));
+    if (max_visible > 0) HIP_CHECK(qsa::launch_score_paged(a, qsum, scores, ld, dev->cus, scorer_choice(), s));
     HIP_CHECK(mark(s));
     HIP_CHECK(qsa::launch_topk_rows(scores, ld, vs, rows, kb, expand, k, out, s));
     HIP_CHECK(mark(s));

@@ -11,8 +11,10 @@
 //   default form (head sum in K): the score is linear in the query heads,
 //     sum_h q_h.k = (sum_h q_h).k, so each query row is first reduced to the
 //     fp32 head sum u = ((q_0 + q_1) + q_2) + q_3 (exact fp16 -> fp32 adds),
-//     carried as the fp16 pair hi = fp16(u), lo = fp16(u - hi), which
-//     represents u to a relative 2^-22 (exactly for small integers).  The
+//     carried as the fp16 pair hi = fp16(u/f), lo = fp16(u/f - hi), which
+//     represents u/f to a relative 2^-22 (exactly for small integers); f is
+//     1, or 2 or 4 for a row whose head sums leave the fp16 range
+//     (head_sum_factor), and the chain's result times f is the score.  The
 //     keys are the MFMA rows and the query rows its columns; a chain of 16
 //     MFMAs, step t = (slice t/2, part t%2), with A = slice t/2 of the key and
 //     B = slice t/2 of hi (t even) or lo (t odd), accumulates the score in one
@@ -88,12 +90,39 @@ __device__ __forceinline__ float16v mfma32(half8 a, half8 b, float16v c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// hi/lo fp16 pair of the fp32 head sum of 8 query dims (default form).
+// Largest magnitude the hi part of a head sum may take: fp16's largest
+// finite value.
+constexpr float kHalfMax = 65504.0f;
+
+// max |u_i| over the 8 query dims of one fragment, u = ((q0 + q1) + q2) + q3
+// in fp32 (default form).
+__device__ __forceinline__ float head_sum_absmax(const half8& q0, const half8& q1, const half8& q2,
+                                                 const half8& q3) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        m = fmaxf(m, fabsf((((float)q0[i] + (float)q1[i]) + (float)q2[i]) + (float)q3[i]));
+    return m;
+}
+
+// The power of two f by which a row's head sum is divided before it is split
+// into fp16 parts, from the largest |u| over the row's 128 dims: 1 while every
+// u fits fp16 (the common case, where nothing changes), else 2 or 4 -- four
+// finite fp16 values sum to at most 4 * 65504, so u / 4 always fits.  The
+// split then carries u / f, and the chain's fp32 result times f (an exact
+// scale) is the score.  Every score of a row carries the same f, so a row may
+// be ranked on chain results directly.
+__device__ __forceinline__ float head_sum_factor(float umax) {
+    return umax <= kHalfMax ? 1.0f : (umax <= 2.0f * kHalfMax ? 2.0f : 4.0f);
+}
+
+// hi/lo fp16 pair of the fp32 head sum of 8 query dims times inv_f (the
+// reciprocal of the row's head_sum_factor: 1, 1/2 or 1/4, an exact scale).
 __device__ __forceinline__ void head_sum_split(const half8& q0, const half8& q1, const half8& q2, const half8& q3,
-                                               half8& hi, half8& lo) {
+                                               float inv_f, half8& hi, half8& lo) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float u = (((float)q0[i] + (float)q1[i]) + (float)q2[i]) + (float)q3[i];
+        const float u = ((((float)q0[i] + (float)q1[i]) + (float)q2[i]) + (float)q3[i]) * inv_f;
         const _Float16 h = (_Float16)u;
         hi[i] = h;
         lo[i] = (_Float16)(u - (float)h);

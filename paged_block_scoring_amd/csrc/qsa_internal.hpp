@@ -29,28 +29,38 @@ struct PagedArgs {
 // the row-tiled scorer: qsum[((tile*4 + wave)*16 + t)*64 + lane] holds 8
 // fp16 values, t = 2*slice + (0: hi, 1: lo); zero for rows past the end.
 // After the fragments: one int32 per tile of 128 rows, the largest visible-key
-// count of its rows (qsum_tile_visible).
+// count of its rows (qsum_tile_visible); then one float per row slot of every
+// tile, the row's head-sum factor f (qsa_device.hpp head_sum_factor; 1 for
+// slots past the last row): a chain over the fragments gives score / f.
 size_t qsum_bytes(int32_t rows);
 const int32_t* qsum_tile_visible(const _Float16* qsum, int32_t rows);
+const float* qsum_row_factor(const _Float16* qsum, int32_t rows);
 hipError_t launch_qsum_prep(const PagedArgs& a, _Float16* qsum, hipStream_t stream);
 
+// Which materialising scorer runs: chosen from the rows per request, or forced.
+enum class ScorerChoice { Auto, Tiles, Groups };
+
 // Scorer: writes scores[r*ld + j] for j < V_r.  qsum (default form) may be
-// null, in which case the scorer forms the head sums itself.
-hipError_t launch_score_paged(const PagedArgs& a, const _Float16* qsum, float* scores, int64_t ld,
-                              hipStream_t stream);
+// null, in which case the scorer forms the head sums itself.  `cus` is the
+// device's compute-unit count.
+hipError_t launch_score_paged(const PagedArgs& a, const _Float16* qsum, float* scores, int64_t ld, int32_t cus,
+                              ScorerChoice choice, hipStream_t stream);
 
 // Rows per window of the few-rows-per-request scorer: the rows per request
 // rounded up to a power of two, at most 32 (8 in the relu form).
 int32_t group_rows_for(int32_t rows, int32_t num_reqs, bool relu);
 
 // Few-rows-per-request scorer (score_group.hip): same scores as the tiled one.
-hipError_t launch_score_group(const PagedArgs& a, float* out, int64_t ld, hipStream_t stream);
+hipError_t launch_score_group(const PagedArgs& a, float* out, int64_t ld, int32_t cus, hipStream_t stream);
 
 // Scorer over logical keys i (key stride*i): out[r*ld + i] for i < ceil(V_r/stride).
-hipError_t launch_score_store(const PagedArgs& a, const _Float16* qsum, int32_t stride, float* out, int64_t ld,
-                              int32_t cus, hipStream_t stream);
+// With true_scores false the default form stores chain results (score / f of
+// the row's head-sum factor f), the unit the filtering pass compares in.
+hipError_t launch_score_store(const PagedArgs& a, const _Float16* qsum, int32_t stride, bool true_scores, float* out,
+                              int64_t ld, int32_t cus, hipStream_t stream);
 
-// Scorer that appends every composite >= thresh[r] to row r's candidate list.
+// Scorer that appends every composite >= thresh[r] to row r's candidate list
+// (default form: composites of chain results, the sampling pass's unit).
 hipError_t launch_score_filter(const PagedArgs& a, const _Float16* qsum, const uint64_t* thresh, uint64_t* cand,
                                int32_t* cand_count, int32_t cand_cap, int32_t cus, hipStream_t stream);
 

@@ -2,9 +2,6 @@
 // form, score_core.hpp for the relu form): the materialising scorer behind
 // qsa_score_paged and the two-pass arm, the strided sampling pass and the
 // filtering pass of the fused arm.
-#include <stdlib.h>
-#include <string.h>
-
 #include "qsa_internal.hpp"
 #include "score_core.hpp"
 
@@ -37,6 +34,8 @@ hipError_t launch_rows(const ScoreKernelArgs& K, int32_t cus, int64_t min_seg, h
     RowsArgs A = {};
     A.a = K.a;
     A.qsum = K.qsum;
+    A.qfac = qsum_row_factor(K.qsum, K.a.rows);
+    A.true_scores = K.true_scores;
     A.stride = K.stride;
     A.lmax = K.lmax;
     A.out = K.out;
@@ -75,8 +74,8 @@ hipError_t launch_epi(const ScoreKernelArgs& A, int32_t cus, hipStream_t stream)
 
 }  // namespace
 
-hipError_t launch_score_store(const PagedArgs& a, const _Float16* qsum, int32_t stride, float* out, int64_t ld,
-                              int32_t cus, hipStream_t stream) {
+hipError_t launch_score_store(const PagedArgs& a, const _Float16* qsum, int32_t stride, bool true_scores, float* out,
+                              int64_t ld, int32_t cus, hipStream_t stream) {
     if (a.rows <= 0 || a.max_visible <= 0) return hipSuccess;
     ScoreKernelArgs A = {};
     A.a = a;
@@ -86,6 +85,7 @@ hipError_t launch_score_store(const PagedArgs& a, const _Float16* qsum, int32_t 
     A.out = out;
     A.ld = ld;
     A.vec_store = (ld % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) ? 1 : 0;
+    A.true_scores = true_scores ? 1 : 0;
     return launch_epi<Epi::Store>(A, cus, stream);
 }
 
@@ -93,24 +93,20 @@ hipError_t launch_score_store(const PagedArgs& a, const _Float16* qsum, int32_t 
 // 32 rows per request on average those rows mostly belong to different
 // requests, and the windowed scorer, which streams every key once per window,
 // takes over.
-static bool use_group_scorer(const PagedArgs& a) {
-    const char* f = getenv("QSA_FORCE_SCORER");
-    if (f && strcmp(f, "tiles") == 0) return false;
-    if (f && strcmp(f, "groups") == 0) return true;
+static bool use_group_scorer(const PagedArgs& a, ScorerChoice choice) {
+    if (choice != ScorerChoice::Auto) return choice == ScorerChoice::Groups;
     const int32_t reqs = a.num_reqs > 0 ? a.num_reqs : 1;
     return a.rows / reqs < 32;
 }
 
-hipError_t launch_score_paged(const PagedArgs& a, const _Float16* qsum, float* scores, int64_t ld,
-                              hipStream_t stream) {
-    if (use_group_scorer(a)) return launch_score_group(a, scores, ld, stream);
+hipError_t launch_score_paged(const PagedArgs& a, const _Float16* qsum, float* scores, int64_t ld, int32_t cus,
+                              ScorerChoice choice, hipStream_t stream) {
+    if (use_group_scorer(a, choice)) return launch_score_group(a, scores, ld, cus, stream);
     if (qsum && !a.relu) {
         const hipError_t e = launch_qsum_prep(a, const_cast<_Float16*>(qsum), stream);
         if (e != hipSuccess) return e;
     }
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    return launch_score_store(a, qsum, 1, scores, ld, cus, stream);
+    return launch_score_store(a, qsum, 1, true, scores, ld, cus, stream);
 }
 
 hipError_t launch_score_filter(const PagedArgs& a, const _Float16* qsum, const uint64_t* thresh, uint64_t* cand,
@@ -128,17 +124,23 @@ hipError_t launch_score_filter(const PagedArgs& a, const _Float16* qsum, const u
     return launch_epi<Epi::Filter>(A, cus, stream);
 }
 
-// One thread per (tile, wave, slice, lane): the fp32 head sum of the 8 query
-// dims that lane supplies for that slice, as its fp16 hi/lo pair
-// (head_sum_split, the same arithmetic as the scorers' own), stored at steps
-// t = 2*slice and 2*slice + 1 of the fragment order.  The last `tiles`
-// workgroups instead write each tile's visible-key count (the largest over
-// its rows; 0 for rows past the end or of an unknown request), which the
-// tiled scorer uses to share out only the keys a tile can see.
-__global__ __launch_bounds__(256) void qsum_prep_kernel(PagedArgs a, _Float16* __restrict__ qsum, int32_t n,
-                                                        int32_t frag_blocks, int32_t* __restrict__ tile_v) {
+// One workgroup per (tile, wave) of the fragment order, i.e. 32 query rows,
+// with one wave per slice s: lane l handles dims 16s + 8g .. 16s + 8g + 7 (g =
+// l/32) of row l%32 and stores their fp32 head sums as fp16 hi/lo pairs
+// (head_sum_split, the same arithmetic as the scorers' own) at steps t = 2s
+// and 2s + 1.  The row's head-sum factor comes from the largest |u| over its
+// 16 (slice, half) parts, met in LDS; the slice-0 wave also stores it.  The
+// last `tiles` workgroups instead write each tile's visible-key count (the
+// largest over its rows; 0 for rows past the end or of an unknown request),
+// which the tiled scorer uses to share out only the keys a tile can see.
+constexpr int kPrepNT = 64 * kSlices;
+
+__global__ __launch_bounds__(kPrepNT) void qsum_prep_kernel(PagedArgs a, _Float16* __restrict__ qsum,
+                                                            int32_t frag_blocks, int32_t* __restrict__ tile_v,
+                                                            float* __restrict__ row_f) {
+    const int lane = threadIdx.x & 63, s = threadIdx.x >> 6;
     if ((int)blockIdx.x >= frag_blocks) {
-        __shared__ int32_t s_w[4];
+        __shared__ int32_t s_w[kSlices];
         const int t = blockIdx.x - frag_blocks;
         const int row = t * RowsShape::TILE + threadIdx.x;
         int v = 0;
@@ -148,36 +150,57 @@ __global__ __launch_bounds__(256) void qsum_prep_kernel(PagedArgs a, _Float16* _
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-        if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = v;
+        if (lane == 0) s_w[s] = v;
         __syncthreads();
-        if (threadIdx.x == 0) tile_v[t] = max(max(s_w[0], s_w[1]), max(s_w[2], s_w[3]));
+        if (threadIdx.x == 0) {
+            int m = 0;
+#pragma unroll
+            for (int i = 0; i < kSlices; ++i) m = max(m, s_w[i]);
+            tile_v[t] = m;
+        }
         return;
     }
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
-    const int lane = i & 63, s = (i >> 6) & 7, wave = (i >> 9) & 3, tile = i >> 11;
-    const int row = tile * RowsShape::TILE + wave * RowsShape::RPW + (lane & 31);
-    half8 hi = {}, lo = {};
-    if (row < a.rows) {
-        const _Float16* qr = a.q + (int64_t)row * kHeads * kHeadDim + 16 * s + 8 * (lane >> 5);
-        head_sum_split(*reinterpret_cast<const half8*>(qr), *reinterpret_cast<const half8*>(qr + kHeadDim),
-                       *reinterpret_cast<const half8*>(qr + 2 * kHeadDim),
-                       *reinterpret_cast<const half8*>(qr + 3 * kHeadDim), hi, lo);
+    __shared__ float s_um[kSlices][64];
+    const int tw = blockIdx.x;  // tile * 4 + wave of the fragment order
+    const int row = tw * RowsShape::RPW + (lane & 31);
+    const bool live = row < a.rows;
+    const _Float16* qr = a.q + (int64_t)(live ? row : 0) * kHeads * kHeadDim + 16 * s + 8 * (lane >> 5);
+    half8 h[kHeads];
+#pragma unroll
+    for (int hh = 0; hh < kHeads; ++hh) {
+        const half8 v = *reinterpret_cast<const half8*>(qr + hh * kHeadDim);
+        h[hh] = live ? v : half8{};
     }
-    half8* out = reinterpret_cast<half8*>(qsum) + ((int64_t)tile * RowsShape::WAVES + wave) * 16 * 64 + lane;
+    s_um[s][lane] = head_sum_absmax(h[0], h[1], h[2], h[3]);
+    __syncthreads();
+    float um = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i) um = fmaxf(um, fmaxf(s_um[i][lane & 31], s_um[i][(lane & 31) + 32]));
+    const float f = head_sum_factor(um);
+    half8 hi, lo;
+    head_sum_split(h[0], h[1], h[2], h[3], 1.0f / f, hi, lo);
+    half8* out = reinterpret_cast<half8*>(qsum) + (int64_t)tw * 16 * 64 + lane;
     out[64 * (2 * s)] = hi;
     out[64 * (2 * s + 1)] = lo;
+    if (s == 0 && lane < 32) row_f[tw * RowsShape::RPW + lane] = f;
 }
 
-// fragments of every tile, then one visible-key count per tile
+// fragments of every tile, then one visible-key count per tile, then one
+// head-sum factor per row slot of every tile
 static size_t qsum_frag_bytes(int32_t rows) {
     const int64_t tiles = (rows + RowsShape::TILE - 1) / RowsShape::TILE;
     return (size_t)tiles * RowsShape::WAVES * 16 * 64 * sizeof(half8);
 }
 
+static size_t qsum_tile_v_bytes(int32_t rows) {
+    const int64_t tiles = (rows + RowsShape::TILE - 1) / RowsShape::TILE;
+    return (size_t)((tiles * sizeof(int32_t) + 255) / 256 * 256);
+}
+
 size_t qsum_bytes(int32_t rows) {
     const int64_t tiles = (rows + RowsShape::TILE - 1) / RowsShape::TILE;
-    return qsum_frag_bytes(rows) + (size_t)((tiles * sizeof(int32_t) + 255) / 256 * 256);
+    return qsum_frag_bytes(rows) + qsum_tile_v_bytes(rows) +
+           (size_t)((tiles * RowsShape::TILE * sizeof(float) + 255) / 256 * 256);
 }
 
 const int32_t* qsum_tile_visible(const _Float16* qsum, int32_t rows) {
@@ -185,13 +208,20 @@ const int32_t* qsum_tile_visible(const _Float16* qsum, int32_t rows) {
                 : nullptr;
 }
 
+const float* qsum_row_factor(const _Float16* qsum, int32_t rows) {
+    return qsum ? reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(qsum) +
+                                                 qsum_frag_bytes(rows) + qsum_tile_v_bytes(rows))
+                : nullptr;
+}
+
 hipError_t launch_qsum_prep(const PagedArgs& a, _Float16* qsum, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     const int64_t tiles = (a.rows + RowsShape::TILE - 1) / RowsShape::TILE;
-    const int32_t n = (int32_t)(tiles * RowsShape::WAVES * kSlices * 64);
-    const int32_t frag_blocks = (n + 255) / 256;
     int32_t* tile_v = const_cast<int32_t*>(qsum_tile_visible(qsum, a.rows));
-    qsum_prep_kernel<<<dim3((unsigned)(frag_blocks + tiles)), 256, 0, stream>>>(a, qsum, n, frag_blocks, tile_v);
+    float* row_f = const_cast<float*>(qsum_row_factor(qsum, a.rows));
+    const int32_t frag_blocks = (int32_t)(tiles * RowsShape::WAVES);
+    qsum_prep_kernel<<<dim3((unsigned)(frag_blocks + tiles)), kPrepNT, 0, stream>>>(a, qsum, frag_blocks, tile_v,
+                                                                                    row_f);
     return hipGetLastError();
 }
 

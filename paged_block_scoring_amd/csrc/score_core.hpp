@@ -65,6 +65,7 @@ struct ScoreKernelArgs {
     float* out;
     int64_t ld;
     int32_t vec_store;  // out and ld allow 16-byte stores
+    int32_t true_scores;  // default form: store scores, else chain results (score / head-sum factor)
     // Filter
     const uint64_t* thresh;  // [rows] threshold composite; only its score is used
     uint64_t* cand;          // [rows][cand_cap] entries (score bits << 32 | key)

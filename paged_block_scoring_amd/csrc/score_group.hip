@@ -101,6 +101,7 @@ __global__ __launch_bounds__(kGroupNT, 2) void score_group_kernel(GroupArgs A) {
     }
     bool todo = req_c >= 0 && v_c > k0;
     half8 qa[2 * kSlices];
+    float fac = 1.0f;  // head-sum factor of this lane's row (default form)
 
     for (;;) {
         // one pass per request among the window's pending rows, smallest first
@@ -133,16 +134,19 @@ __global__ __launch_bounds__(kGroupNT, 2) void score_group_kernel(GroupArgs A) {
             }
         } else {
             const _Float16* qp = a.q + (int64_t)(on ? r0 + c : r0) * kHeads * kHeadDim + 8 * g;
+            auto load = [&](int s, int hh) {
+                const half8 v = *reinterpret_cast<const half8*>(qp + hh * kHeadDim + 16 * s);
+                return on ? v : half8{};
+            };
+            // the row's head-sum factor (lanes l and l^32 hold its two halves)
+            float um = 0.0f;
 #pragma unroll
-            for (int s = 0; s < kSlices; ++s) {
-                half8 h[kHeads];
+            for (int s = 0; s < kSlices; ++s) um = fmaxf(um, head_sum_absmax(load(s, 0), load(s, 1), load(s, 2), load(s, 3)));
+            um = fmaxf(um, __shfl_xor(um, 32, 64));
+            fac = head_sum_factor(um);
 #pragma unroll
-                for (int hh = 0; hh < kHeads; ++hh) {
-                    const half8 v = *reinterpret_cast<const half8*>(qp + hh * kHeadDim + 16 * s);
-                    h[hh] = on ? v : half8{};
-                }
-                head_sum_split(h[0], h[1], h[2], h[3], qa[2 * s], qa[2 * s + 1]);
-            }
+            for (int s = 0; s < kSlices; ++s)
+                head_sum_split(load(s, 0), load(s, 1), load(s, 2), load(s, 3), 1.0f / fac, qa[2 * s], qa[2 * s + 1]);
         }
 
         const int32_t* ptrow = a.page_table + (int64_t)act * a.pt_stride;
@@ -190,10 +194,11 @@ __global__ __launch_bounds__(kGroupNT, 2) void score_group_kernel(GroupArgs A) {
                         sb[(2 * i + g) * rstride + off + m] =
                             combine_relu_heads(acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]);
             } else if (c < A.G) {
+                // chain result x head-sum factor = score
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     *reinterpret_cast<float4v*>(sb + c * rstride + off + 16 * g + 4 * i) =
-                        float4v{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+                        float4v{acc[4 * i] * fac, acc[4 * i + 1] * fac, acc[4 * i + 2] * fac, acc[4 * i + 3] * fac};
             }
         };
         auto flush = [&](int wbase) {
@@ -272,7 +277,7 @@ int32_t group_rows_for(int32_t rows, int32_t num_reqs, bool relu) {
     return G > cap ? cap : G;
 }
 
-hipError_t launch_score_group(const PagedArgs& a, float* out, int64_t ld, hipStream_t stream) {
+hipError_t launch_score_group(const PagedArgs& a, float* out, int64_t ld, int32_t cus, hipStream_t stream) {
     if (a.rows <= 0 || a.max_visible <= 0) return hipSuccess;
     GroupArgs A;
     A.a = a;
@@ -293,8 +298,6 @@ hipError_t launch_score_group(const PagedArgs& a, float* out, int64_t ld, hipStr
     if (nl < 1) nl = 1;
     // with few windows, shorter segments (down to 256 keys) spread the keys
     // of a handful of rows over the compute units
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     while (nl > 1 && nl % 2 == 0 && L * (nl / 2) >= 256 &&
            (int64_t)A.windows * ((a.max_visible + L * nl - 1) / (L * nl)) < 2 * (int64_t)cus)
         nl /= 2;

@@ -34,7 +34,9 @@
 // accumulator element v the score of row l%32 and key 16*(l/32) + v.
 //
 // Epilogues.
-//   Store  -- out[row*ld + i] = score: the wave transposes its 32 x 32 tile
+//   Store  -- out[row*ld + i] = score (or, for the sampling pass, the chain
+//             result score / f of the row's head-sum factor f, the unit the
+//             filtering pass compares in): the wave transposes its 32 x 32 tile
 //             through LDS so that 8 consecutive lanes store 32 consecutive
 //             keys (128 bytes) of one row with 16-byte stores;
 //   Filter -- keep (key, score) if score >= the row's threshold score.  Each
@@ -63,6 +65,7 @@ constexpr int kLaneCap = 24;     // entries of a lane's LDS candidate list (>= 1
 struct RowsArgs {
     PagedArgs a;
     const _Float16* qsum;  // head sums in fragment order (qsa_internal.hpp), or null
+    const float* qfac;     // with qsum: each row slot's head-sum factor
     int32_t stride;    // logical key i is key stride*i
     int32_t lmax;      // logical keys of the longest row: ceil(max_visible / stride)
     int32_t tiles;     // ceil(rows / 128)
@@ -74,6 +77,7 @@ struct RowsArgs {
     float* out;
     int64_t ld;
     int32_t vec_store;  // out and ld allow 16-byte stores
+    int32_t true_scores;  // store scores (chain result x head-sum factor), else chain results
     // Filter
     const uint64_t* thresh;  // [rows] threshold composite; only its score is used
     uint64_t* cand;          // [rows][cand_cap] entries (score bits << 32 | key)
@@ -316,7 +320,8 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
     for (int i = tid; i < kRowsPiece; i += NT) s_slot[i] = 0u;
 
     half8 qa[2 * kSlices];
-    float fT = 0.0f;  // threshold score of this lane's row (Filter)
+    float fac = 1.0f;  // head-sum factor of this lane's row (Store with true_scores)
+    float fT = 0.0f;  // threshold chain result of this lane's row (Filter)
     int cnt = 0;      // entries in this lane's list (Filter)
     const uint32_t list0 =
         (uint32_t)reinterpret_cast<uintptr_t>(static_cast<void*>(&s_list[0])) + (uint32_t)(tid * kLaneCap * 8);
@@ -406,23 +411,31 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
             const half8* qs = reinterpret_cast<const half8*>(A.qsum) + ((int64_t)tile * S::WAVES + wave) * 16 * 64 + lane;
 #pragma unroll
             for (int t = 0; t < 2 * kSlices; ++t) qa[t] = qs[64 * t];
+            if (!FILTER && A.true_scores) fac = A.qfac[r0 + erow];
         } else if (new_tile) {
             // B operand: column m = row m; step t of the chain = (slice t/2, hi/lo t%2)
             const int row = r0 + wave * RPW + (lane & 31);
             const int rowc = row < a.rows ? row : a.rows - 1;
+            const _Float16* qr = a.q + (int64_t)rowc * kHeads * kHeadDim + 8 * (lane >> 5);
+            auto load = [&](int s, int hh) {
+                const half8 v = *reinterpret_cast<const half8*>(qr + hh * kHeadDim + 16 * s);
+                return row < a.rows ? v : half8{};
+            };
+            // the row's head-sum factor (lanes l and l^32 hold its two halves)
+            float um = 0.0f;
 #pragma unroll
-            for (int s = 0; s < kSlices; ++s) {
-                half8 h[kHeads];
+            for (int s = 0; s < kSlices; ++s) um = fmaxf(um, head_sum_absmax(load(s, 0), load(s, 1), load(s, 2), load(s, 3)));
+            um = fmaxf(um, __shfl_xor(um, 32, 64));
+            fac = head_sum_factor(um);
 #pragma unroll
-                for (int hh = 0; hh < kHeads; ++hh) {
-                    const half8 v = *reinterpret_cast<const half8*>(a.q + ((int64_t)rowc * kHeads + hh) * kHeadDim +
-                                                                    16 * s + 8 * (lane >> 5));
-                    h[hh] = row < a.rows ? v : half8{};
-                }
-                head_sum_split(h[0], h[1], h[2], h[3], qa[2 * s], qa[2 * s + 1]);
-            }
+            for (int s = 0; s < kSlices; ++s)
+                head_sum_split(load(s, 0), load(s, 1), load(s, 2), load(s, 3), 1.0f / fac, qa[2 * s], qa[2 * s + 1]);
+            if (!A.true_scores) fac = 1.0f;
         }
-        if (one_req) build_slots(0, c0, c1);
+        // (the stripe end c1 is padded to whole stages and may lie up to 31
+        // keys past the last visible key; the table stops at that key, so no
+        // page-table entry beyond the request's visible pages is read)
+        if (one_req) build_slots(0, c0, min(c1, A.lmax));
         if (tid < TILE) {
             int lv = 0;
             if (rr >= a.rows || req < 0 || req >= a.num_reqs) {
@@ -534,6 +547,10 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
                 // element v: key kb + v of row erow
                 const int kb = j0 + 16 * (lane >> 5);
                 const bool full = j0 + STEP <= wlim;
+                if (A.true_scores) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[v] *= fac;
+                }
                 {
                     // transpose so that lane l holds keys 4*(l%8) .. +3 of rows l/8 + 8i
                     float* const tw = s_tr[wave];

@@ -45,11 +45,11 @@ def test_workspace_sizes():
     assert Q.qsa_select_paged_tokens_workspace_size(0, 1, 100, 4, 64) == 0
     assert Q.qsa_select_paged_tokens_workspace_size(10, 1, 0, 4, 64) == 0
     fused = Q.qsa_select_paged_tokens_workspace_size(1616, 1, 46000, 4, 2048)
-    os.environ["QSA_FORCE_PATH"] = "two_pass"
+    Q.qsa_debug_force(Q.QSA_DEBUG_FORCE_TWO_PASS)
     try:
         two_pass = Q.qsa_select_paged_tokens_workspace_size(1616, 1, 46000, 4, 2048)
     finally:
-        del os.environ["QSA_FORCE_PATH"]
+        Q.qsa_debug_force(0)
     assert two_pass >= 1616 * 46000 * 4          # the materialised score matrix
     assert 0 < fused < two_pass                   # the fused arm never holds it
     # decode-like batches (one row per request) take the two-pass arm
@@ -152,9 +152,68 @@ def test_zero_rows_is_a_noop_without_device():
 def test_binding_refuses_host_tensors():
     import torch
     q = torch.zeros((2, 4, 128), dtype=torch.float16)
-    with pytest.raises(ValueError):
-        Q.qsa_select_paged_tokens(q, q, torch.zeros((1, 1), dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
-                                  4, 64)
+    kc = torch.zeros((3, 16, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="device tensor"):
+        Q.qsa_select_paged_tokens(q, kc, torch.zeros((1, 1), dtype=torch.int32), torch.zeros(2, dtype=torch.int32),
+                                  4, 64, max_visible=1)
+
+
+def _host_paged():
+    import torch
+    return dict(q=torch.zeros((2, 4, 128), dtype=torch.float16), kcache=torch.zeros((3, 16, 128), dtype=torch.float16),
+                page_table=torch.zeros((1, 3), dtype=torch.int32), pos=torch.zeros(2, dtype=torch.int32))
+
+
+def test_binding_requires_max_visible():
+    """The binding computes nothing: the visible-key bound is the caller's."""
+    a = _host_paged()
+    with pytest.raises(TypeError):
+        Q.qsa_select_paged_tokens(a["q"], a["kcache"], a["page_table"], a["pos"], 4, 64)
+    with pytest.raises(TypeError):
+        Q.qsa_score_paged(a["q"], a["kcache"], a["page_table"], a["pos"], 4)
+
+
+def test_binding_refuses_mis_shaped_tensors_before_any_call():
+    """Shape relations are checked before the device check, so these fail on
+    the host with a shape message; the library is never called."""
+    import torch
+    a = _host_paged()
+    with pytest.raises(ValueError, match="head_dim"):
+        Q.qsa_select_paged_tokens(a["q"], torch.zeros((3, 16, 64), dtype=torch.float16), a["page_table"], a["pos"],
+                                  4, 64, max_visible=1)
+    with pytest.raises(ValueError, match="shape"):
+        Q.qsa_select_paged_tokens(a["q"], a["kcache"], a["page_table"], a["pos"], 4, 64, max_visible=1,
+                                  out=torch.zeros((2, 32), dtype=torch.int32))
+    with pytest.raises(ValueError, match="shape"):
+        Q.qsa_score_paged(a["q"], a["kcache"], a["page_table"], a["pos"], 4, max_visible=5,
+                          scores=torch.zeros((2, 4), dtype=torch.float32))
+    with pytest.raises(ValueError, match="shape"):
+        Q.qsa_topk_rows(torch.zeros((3, 10), dtype=torch.float32), 4, out=torch.zeros((3, 5), dtype=torch.int32))
+    with pytest.raises(ValueError, match="shape"):
+        Q.qsa_sparse_attention(torch.zeros((2, 24, 256), dtype=torch.float16),
+                               torch.zeros((1, 64, 2, 256), dtype=torch.float16),
+                               torch.zeros((1, 64, 2, 256), dtype=torch.float16), a["page_table"],
+                               torch.zeros((2, 8), dtype=torch.int32), out=torch.zeros((2, 24, 128)))
+    Q.qsa_last_error()  # nothing was called: no error is pending from these
+
+
+def test_debug_force_rejects_bad_masks():
+    assert Q.qsa_debug_forced() == 0
+    for bad in (0x20, Q.QSA_DEBUG_FORCE_TWO_PASS | Q.QSA_DEBUG_FORCE_FUSED,
+                Q.QSA_DEBUG_FORCE_TWO_PASS | Q.QSA_DEBUG_FORCE_FALLBACK,
+                Q.QSA_DEBUG_FORCE_TILES | Q.QSA_DEBUG_FORCE_GROUPS):
+        with pytest.raises(Q.QSAError) as e:
+            Q.qsa_debug_force(bad)
+        assert e.value.status == Q.QSA_ERR_INVALID_ARGUMENT
+        assert Q.qsa_debug_forced() == 0
+    Q.qsa_debug_force(Q.QSA_DEBUG_FORCE_FALLBACK | Q.QSA_DEBUG_FORCE_GROUPS)
+    try:
+        assert Q.qsa_debug_forced() == Q.QSA_DEBUG_FORCE_FALLBACK | Q.QSA_DEBUG_FORCE_GROUPS
+        # the workspace query follows the forced arm: a decode batch now sizes the fused arm
+        fused = Q.qsa_select_paged_tokens_workspace_size(256, 256, 46000, 4, 2048)
+    finally:
+        Q.qsa_debug_force(0)
+    assert 0 < fused < Q.qsa_select_paged_tokens_workspace_size(256, 256, 46000, 4, 2048)
 
 
 def attend(**over):

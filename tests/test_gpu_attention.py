@@ -128,8 +128,10 @@ def test_attention_after_the_indexer():
     indexer's token selection feeds the consumer."""
     w = W.kernel_shape(rows=80)
     dq = lambda a: torch.from_numpy(a).to(DEV)  # noqa: E731
+    import oracle
+    mv = max(oracle.visible_keys(int(p), w.compress_ratio) for p in w.pos)
     tok = Q.qsa_select_paged_tokens(dq(w.q), dq(w.kcache), dq(w.page_table), dq(w.pos), w.compress_ratio, w.k,
-                                    row_req=dq(w.row_req))
+                                    max_visible=mv, row_req=dq(w.row_req))
     torch.cuda.synchronize()
     tok = tok.cpu().numpy()
     rng = np.random.default_rng(14)

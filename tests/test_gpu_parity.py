@@ -11,7 +11,6 @@ token sets identical in all rows); "spec(MODEL-MM-QWEN4-EXP) ...", section
 "The component deep-dives, and two corrections to the above".
 """
 import contextlib
-import os
 import sys
 
 import numpy as np
@@ -31,24 +30,27 @@ KEYS = Q.QSA_OUT_KEYS
 PATHS = ["two_pass", "fused", "fused_fallback"]
 
 
+ARM_BITS = {"two_pass": Q.QSA_DEBUG_FORCE_TWO_PASS, "fused": Q.QSA_DEBUG_FORCE_FUSED,
+            "fused_fallback": Q.QSA_DEBUG_FORCE_FALLBACK}
+SCORER_BITS = {"tiles": Q.QSA_DEBUG_FORCE_TILES, "groups": Q.QSA_DEBUG_FORCE_GROUPS}
+
+
 @contextlib.contextmanager
-def force_path(name):
-    """Drive one execution arm deliberately (the library reads these
-    variables on every call); "fused_fallback" makes every row of the fused
-    arm take its exact recompute path."""
-    old = {k: os.environ.get(k) for k in ("QSA_FORCE_PATH", "QSA_DEBUG_FORCE_FALLBACK")}
-    if name is not None:
-        os.environ["QSA_FORCE_PATH"] = "fused" if name.startswith("fused") else name
-        if name == "fused_fallback":
-            os.environ["QSA_DEBUG_FORCE_FALLBACK"] = "1"
+def _forced(group, bit):
+    """Replace the override bits of one group (arms or scorers) for the block."""
+    old = Q.qsa_debug_forced()
+    Q.qsa_debug_force((old & ~sum(group.values())) | bit)
     try:
         yield
     finally:
-        for k, v in old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+        Q.qsa_debug_force(old)
+
+
+def force_path(name):
+    """Drive one execution arm deliberately; "fused_fallback" makes every row
+    of the fused arm take its exact recompute path; None leaves the choice to
+    the library."""
+    return _forced(ARM_BITS, 0 if name is None else ARM_BITS[name])
 
 
 def note(*a):
@@ -65,16 +67,22 @@ def visible(oracle_mod, w):
     return np.array([oracle_mod.visible_keys(int(p), w.compress_ratio) for p in w.pos], np.int32)
 
 
+def max_visible(w):
+    """The caller's bound on every row's visible key count (the oracle's rule)."""
+    import oracle
+    return max([oracle.visible_keys(int(p), w.compress_ratio) for p in w.pos], default=0)
+
+
 def gpu_scores(d, w, flags):
-    s = Q.qsa_score_paged(d["q"], d["kcache"], d["page_table"], d["pos"], w.compress_ratio, row_req=d["row_req"],
-                          flags=flags & RELU)
+    s = Q.qsa_score_paged(d["q"], d["kcache"], d["page_table"], d["pos"], w.compress_ratio,
+                          max_visible=max_visible(w), row_req=d["row_req"], flags=flags & RELU)
     torch.cuda.synchronize()
     return s.cpu().numpy()
 
 
 def gpu_select(d, w, flags, k=None):
     out = Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"], w.compress_ratio,
-                                    k or w.k, row_req=d["row_req"], flags=flags)
+                                    k or w.k, max_visible=max_visible(w), row_req=d["row_req"], flags=flags)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -91,7 +99,10 @@ def expected_from_scores(oracle_mod, scores, V, k, cr, flags):
     return blocks if flags & KEYS else expand(blocks, cr)
 
 
-def assert_scores(gs, ref, V, exact, rows=None):
+def assert_scores(gs, ref, V, exact, rows=None, floors=None):
+    """floors[r] replaces the 1 of max(|ref|, 1) for rows whose query is the
+    N(0,1) draw scaled by a power of two c: scaling q by c scales every score
+    (and both sides' rounding errors) by c exactly, so the bar moves with it."""
     rows = range(len(V)) if rows is None else rows
     worst = 0.0
     for i, r in enumerate(rows):
@@ -100,13 +111,14 @@ def assert_scores(gs, ref, V, exact, rows=None):
         if exact:
             assert np.array_equal(a, b), f"row {r}: first mismatch at {np.argmax(a != b)}"
         else:
-            err = np.abs(a - b) / np.maximum(np.abs(b), 1.0)
+            floor = 1.0 if floors is None else float(floors[r])
+            err = np.abs(a - b) / np.maximum(np.abs(b), floor)
             worst = max(worst, float(err.max(initial=0.0)))
             assert np.all(err <= 1e-3), f"row {r}: max rel err {err.max()}"
     return worst
 
 
-def full_parity(oracle_mod, w, flags, integer, paths=(None,)):
+def full_parity(oracle_mod, w, flags, integer, paths=(None,), floors=None):
     """Scores element by element, the GPU selection on its own scores, and
     (integer inputs) the whole path against the oracle, for each forced arm."""
     d = to_dev(w)
@@ -114,7 +126,7 @@ def full_parity(oracle_mod, w, flags, integer, paths=(None,)):
     gs = gpu_scores(d, w, flags)
     ref = oracle_mod.score_paged(w.q, w.kcache, w.page_table, w.pos, w.compress_ratio, row_req=w.row_req,
                                  flags=flags & RELU)
-    worst = assert_scores(gs, ref, V, exact=integer)
+    worst = assert_scores(gs, ref, V, exact=integer, floors=floors)
     exp = expected_from_scores(oracle_mod, gs, V, w.k, w.compress_ratio, flags)
     full = None
     if integer:
@@ -166,20 +178,11 @@ def test_reduced(oracle_mod, name, integer, flags):
     full_parity(oracle_mod, w, flags, integer or name == "tie_stress_96", paths=PATHS)
 
 
-@contextlib.contextmanager
 def force_scorer(name):
     """Pick the scorer behind qsa_score_paged and the two-pass arm: "tiles"
     (rows of a tile share staged keys) or "groups" (each wave streams the keys
     of a small row window)."""
-    old = os.environ.get("QSA_FORCE_SCORER")
-    os.environ["QSA_FORCE_SCORER"] = name
-    try:
-        yield
-    finally:
-        if old is None:
-            os.environ.pop("QSA_FORCE_SCORER", None)
-        else:
-            os.environ["QSA_FORCE_SCORER"] = old
+    return _forced(SCORER_BITS, SCORER_BITS[name])
 
 
 @pytest.mark.parametrize("flags", [0, RELU])
@@ -200,6 +203,43 @@ def test_scorers_bit_identical(oracle_mod, name, flags):
     with force_scorer("groups"), force_path("two_pass"):
         out = gpu_select(d, w, flags)
     assert np.array_equal(out, expected_from_scores(oracle_mod, a, V, w.k, w.compress_ratio, flags))
+
+
+LARGE_Q = ["kernel_shape_80", "mixed_small", "decode_small", "three_reqs_40"]
+
+
+@pytest.mark.parametrize("integer", [True, False])
+@pytest.mark.parametrize("name", LARGE_Q)
+def test_large_query(oracle_mod, name, integer):
+    """Query rows whose sum over the index heads leaves fp16's range in some
+    dimension (up to 4 * 65504, with rows at 65504, 65520, 131008, 131040 and
+    262016 exactly): the default form's folded head sum must still give the
+    oracle's scores -- bit-exact on the integer twin, within the tolerance on
+    Gaussian rows scaled by 2^14 (its floor scaled by 2^14 too) -- and the
+    same selection, in every arm."""
+    w = W.large_query(REDUCED[name](integer), seed=77)
+    floors = np.where(np.abs(w.q.astype(np.float32)).max(axis=(1, 2)) > 64.0, 16384.0, 1.0)
+    for flags in (0, KEYS) + ((RELU,) if integer else ()):
+        full_parity(oracle_mod, w, flags, integer, paths=PATHS, floors=None if integer else floors)
+
+
+@pytest.mark.parametrize("name", LARGE_Q)
+def test_large_query_scorers(oracle_mod, name):
+    """The same large integer rows through both scorers: bit-identical scores,
+    exact against the oracle, and the two-pass selection on the windowed
+    scorer's output equal to the oracle's end to end."""
+    w = W.large_query(REDUCED[name](True), seed=78)
+    d = to_dev(w)
+    V = visible(oracle_mod, w)
+    ref = oracle_mod.score_paged(w.q, w.kcache, w.page_table, w.pos, w.compress_ratio, row_req=w.row_req)
+    for scorer in ("tiles", "groups"):
+        with force_scorer(scorer):
+            gs = gpu_scores(d, w, 0)
+        assert_scores(gs, ref, V, exact=True)
+    full = oracle_mod.select_paged_tokens(w.q, w.kcache, w.page_table, w.pos, w.compress_ratio, w.k,
+                                          row_req=w.row_req)
+    with force_scorer("groups"), force_path("two_pass"):
+        assert np.array_equal(gpu_select(d, w, 0), full)
 
 
 def test_out_keys_reduced(oracle_mod):
@@ -304,13 +344,14 @@ def test_golden_fixture_on_gpu():
     d = dict(q=torch.from_numpy(q).to(DEV), kcache=torch.from_numpy(kc).to(DEV),
              page_table=torch.from_numpy(pt).to(DEV), pos=torch.from_numpy(pos).to(DEV))
     cr = g["compress_ratio"]
-    out = Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"], cr, g["k"])
-    assert out.cpu().numpy().tolist() == g["expected_tokens"]
-    out = Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"], cr, g["k"], flags=RELU)
-    assert out.cpu().numpy().tolist() == g["expected_tokens_relu"]
-    out = Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"], cr, g["k_keys"], flags=KEYS)
-    assert out.cpu().numpy().tolist() == g["expected_keys"]
-    s = Q.qsa_score_paged(d["q"], d["kcache"], d["page_table"], d["pos"], cr)
+    import oracle
+    mv = max(oracle.visible_keys(int(p), cr) for p in pos)
+    sel = lambda k, flags=0: Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"], cr, k,  # noqa: E731
+                                                       max_visible=mv, flags=flags)
+    assert sel(g["k"]).cpu().numpy().tolist() == g["expected_tokens"]
+    assert sel(g["k"], RELU).cpu().numpy().tolist() == g["expected_tokens_relu"]
+    assert sel(g["k_keys"], KEYS).cpu().numpy().tolist() == g["expected_keys"]
+    s = Q.qsa_score_paged(d["q"], d["kcache"], d["page_table"], d["pos"], cr, max_visible=mv)
     assert s[0, :16].cpu().numpy().tolist() == g["expected_scores_row0_first16"]
 
 
@@ -322,7 +363,8 @@ def test_determinism(path):
         outs = [gpu_select(d, w, 0) for _ in range(3)]
     side = torch.cuda.Stream()
     with force_path(path), torch.cuda.stream(side):
-        o = Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"], 4, w.k, row_req=d["row_req"])
+        o = Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"], 4, w.k,
+                                      max_visible=max_visible(w), row_req=d["row_req"])
     side.synchronize()
     outs.append(o.cpu().numpy())
     for o in outs[1:]:

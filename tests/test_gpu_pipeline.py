@@ -65,12 +65,12 @@ def test_produce_select_attend():
     rows = len(pos)
     q = rng.standard_normal((rows, 4, D)).astype(np.float16)
     d_q, d_pt, d_pos, d_rr = dev(q), dev(pt), dev(pos), dev(row_req)
-    scores = Q.qsa_score_paged(d_q, kc, d_pt, d_pos, cr, row_req=d_rr)
-    tok = Q.qsa_select_paged_tokens(d_q, kc, d_pt, d_pos, cr, k, row_req=d_rr)
+    V = np.array([O.visible_keys(int(p), cr) for p in pos], np.int32)
+    scores = Q.qsa_score_paged(d_q, kc, d_pt, d_pos, cr, max_visible=int(V.max()), row_req=d_rr)
+    tok = Q.qsa_select_paged_tokens(d_q, kc, d_pt, d_pos, cr, k, max_visible=int(V.max()), row_req=d_rr)
     torch.cuda.synchronize()
     gs, tok = scores.cpu().numpy(), tok.cpu().numpy()
     ref = O.score_paged(q, cache, pt, pos, cr, row_req=row_req)
-    V = np.array([O.visible_keys(int(p), cr) for p in pos], np.int32)
     for r in range(rows):
         a, b = gs[r, :V[r]].astype(np.float64), ref[r, :V[r]].astype(np.float64)
         assert np.all(np.abs(a - b) <= 1e-3 * np.maximum(np.abs(b), 1.0)), r

@@ -89,6 +89,23 @@ def test_integer_scores_exact_int64(oracle_mod, seed):
         assert np.all(np.isnan(s[r, V:]))
 
 
+def test_large_integer_query_scores_exact_int64(oracle_mod):
+    """Integer queries with planted values up to 65504 whose sum over the
+    heads reaches 4 * 65504 in a dimension: every per-head dot is an integer
+    below 2^21 and their sum below 2^24, so the oracle's fp32 score is the
+    exact int64 dot product (the large-magnitude parity cases rely on it)."""
+    w = W.large_query(_int_workload(3, [260, 97, 130], [12, 3, 9]), seed=5)
+    u = np.abs(w.q.astype(np.int64).sum(axis=1)).max(axis=1)
+    assert u.max() == 4 * 65504 and np.any((u > 65504) & (u <= 2 * 65504))
+    s = oracle_mod.score_paged(w.q, w.kcache, w.page_table, w.pos, 4, row_req=w.row_req)
+    for r in range(w.rows):
+        V = (int(w.pos[r]) + 1) // 4
+        K = dense_keys(w, int(w.row_req[r]))[:V].astype(np.int64)
+        heads = K @ w.q[r].astype(np.int64).T
+        assert np.abs(heads).max(initial=0) < 2 ** 21 and np.abs(heads.sum(axis=1)).max(initial=0) < 2 ** 24
+        assert np.array_equal(s[r, :V], heads.sum(axis=1).astype(np.float32)), r
+
+
 @pytest.mark.parametrize("seed", [0, 1])
 def test_integer_scores_relu_exact(oracle_mod, seed):
     """relu form: sum over heads of relu(integer dot) is an exact integer; the

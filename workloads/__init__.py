@@ -214,6 +214,52 @@ def raw_token_keys(seed, lengths, page_size=PAGE_SIZE, compress_ratio=COMPRESS_R
     return keys, w, pt, pool
 
 
+# fp16 integers of large magnitude: multiples of 16 in [2^14, 2^15) and of 32
+# in [2^15, 65504] are exact in fp16
+_LARGE_INTS = np.array([16384, 20000, 24576, 30000, 32752, 32768, 40000, 49152, 65504], dtype=np.float32)
+# head values of rows whose largest head sum sits at an edge: 65504 (the fp16
+# maximum), 65520 (just past it), 131008 (twice it) and 131040 (just past
+# that), and 4 * 65504 (the largest sum four fp16 values can reach)
+_EDGE_HEADS = [(32752, 32752, 0, 0), (32752, 32768, 0, 0), (65504, 65504, 0, 0), (65504, 65504, 32, 0),
+               (65504, 65504, 65504, 65504)]
+
+
+def large_query(w, seed, frac=0.5):
+    """A copy of workload ``w`` with large query values planted in a seeded
+    subset of its rows, so that the per-dimension sum over the index heads
+    leaves fp16's range (up to 4 * 65504).
+
+    Integer workloads (q in -2..2) get integer values exact in fp16: in each
+    chosen row, 1 to 3 dimensions where 2 to 4 heads take +-values from
+    ``_LARGE_INTS``; rows 0..4 (and, negated, 5..9) carry the edge sums of
+    ``_EDGE_HEADS`` in one dimension.  Every per-head dot then stays an
+    integer below 2^21, so fp32 sums are exact in any order.  Gaussian
+    workloads get whole rows scaled by 2^14 (exact in fp16) and clipped to
+    +-65504.  Draw order: chosen rows, then per row its dimensions, heads,
+    values and signs."""
+    rng = np.random.default_rng(seed)
+    q = w.q.copy()
+    rows = q.shape[0]
+    integer = bool(np.all(np.abs(w.q.astype(np.float32)) <= 2) and np.all(np.rint(w.q) == w.q))
+    chosen = np.flatnonzero(rng.random(rows) < frac)
+    if integer:
+        for r in chosen:
+            nd = int(rng.integers(1, 4))
+            for d in rng.choice(q.shape[2], size=nd, replace=False):
+                nh = int(rng.integers(2, 5))
+                heads = rng.choice(q.shape[1], size=nh, replace=False)
+                vals = rng.choice(_LARGE_INTS, size=nh) * rng.choice(np.array([-1.0, 1.0], np.float32), size=nh)
+                q[r, heads, d] = vals.astype(np.float16)
+        for i, hv in enumerate(_EDGE_HEADS):
+            for sign, r in ((1.0, i), (-1.0, i + len(_EDGE_HEADS))):
+                if r < rows:
+                    q[r, :, 7] = (sign * np.array(hv, np.float32)).astype(np.float16)
+    else:
+        big = q[chosen].astype(np.float32) * np.float32(16384.0)
+        q[chosen] = np.clip(big, -65504.0, 65504.0).astype(np.float16)
+    return dataclasses.replace(w, name=w.name + "_largeq", q=q)
+
+
 CONFIGS = {
     "tiny": tiny,
     "kernel_shape": kernel_shape,

@@ -186,6 +186,31 @@ size_t qsa_select_paged_tokens_workspace_size(int32_t rows, int32_t num_reqs, in
                                               int32_t compress_ratio, int32_t k, uint32_t flags);
 
 /*
+ * qsa_select_paged_tokens_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): qsa_select_paged_tokens with the same arguments and
+ * results, minus the workspace.  Its scratch is a static device array of
+ * QSA_NOALLOC_SCRATCH_BYTES per device, held from the library's first use on
+ * that device until the process ends; the call allocates nothing.
+ *
+ *  - Returns QSA_ERR_UNSUPPORTED, enqueuing nothing, when the call needs more
+ *    scratch than that (qsa_select_paged_tokens_workspace_size(...) bytes;
+ *    every benchmark configuration of this library fits).
+ *  - Every call on one device shares that device's array.  Calls that may
+ *    overlap on one device (other streams, other threads, unordered graph
+ *    nodes) race on it and give undefined results; calls ordered on one
+ *    stream are safe.  The array's contents carry over between calls and are
+ *    never relied on: each call writes what it reads.
+ */
+#define QSA_NOALLOC_SCRATCH_BYTES (96ull << 20)
+qsa_status qsa_select_paged_tokens_noalloc(const void* q, const void* kcache, const int32_t* page_table,
+                                           int64_t pt_stride, int32_t num_pages, int32_t num_reqs,
+                                           const int32_t* row_req, const int32_t* pos, int32_t rows,
+                                           int32_t heads, int32_t head_dim, int32_t page_size,
+                                           int32_t compress_ratio, int32_t max_visible, int32_t k,
+                                           uint32_t flags, int32_t* out, void* stream);
+
+/*
  * qsa_sparse_attention -- the consumer of the selection ([spec] op survey:
  * plain GQA, 24 query heads over 2 KV heads, head_dim 256; [spec] "The
  * component deep-dives, and two corrections to the above": the consumer

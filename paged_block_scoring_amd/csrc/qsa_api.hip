@@ -415,50 +415,65 @@ QSA_EXPORT size_t qsa_select_paged_tokens_workspace_size(int32_t rows, int32_t n
     return two_pass_bytes(rows, max_visible);
 }
 
-QSA_EXPORT qsa_status qsa_select_paged_tokens(const void* q, const void* kcache, const int32_t* page_table,
-                                              int64_t pt_stride, int32_t num_pages, int32_t num_reqs,
-                                              const int32_t* row_req, const int32_t* pos, int32_t rows,
-                                              int32_t heads, int32_t head_dim, int32_t page_size,
-                                              int32_t compress_ratio, int32_t max_visible, int32_t k,
-                                              uint32_t flags, int32_t* out, void* workspace,
-                                              size_t workspace_bytes, void* stream) {
-    g_err[0] = 0;
-    g_recorded = 0;
-    qsa_status st = check_paged(q, kcache, page_table, pt_stride, num_pages, num_reqs, pos, rows, heads,
-                                head_dim, page_size, compress_ratio, max_visible);
+// Scratch of qsa_select_paged_tokens_noalloc: one array per device, held
+// from the library's load on that device until the process ends.  Host code
+// never uses the array's name as an address (it names a host-side stand-in);
+// the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[QSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Everything qsa_select_paged_tokens receives except its workspace.
+struct SelectCall {
+    const void* q;
+    const void* kcache;
+    const int32_t* page_table;
+    int64_t pt_stride;
+    int32_t num_pages, num_reqs;
+    const int32_t* row_req;
+    const int32_t* pos;
+    int32_t rows, heads, head_dim, page_size, compress_ratio, max_visible, k;
+    uint32_t flags;
+    int32_t* out;
+};
+
+// Host checks of a select call (all but the workspace); *need receives the
+// workspace bytes the call takes.
+qsa_status check_select(const SelectCall& c, size_t* need) {
+    qsa_status st = check_paged(c.q, c.kcache, c.page_table, c.pt_stride, c.num_pages, c.num_reqs, c.pos, c.rows,
+                                c.heads, c.head_dim, c.page_size, c.compress_ratio, c.max_visible);
     if (st != QSA_OK) return st;
-    REQUIRE((flags & ~(QSA_SCORE_RELU | QSA_OUT_KEYS)) == 0, QSA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x",
-            flags);
-    REQUIRE(k >= 1, QSA_ERR_INVALID_ARGUMENT, "k must be >= 1 (got %d)", k);
-    const bool out_keys = (flags & QSA_OUT_KEYS) != 0;
-    REQUIRE(out_keys || k % compress_ratio == 0, QSA_ERR_INVALID_ARGUMENT,
-            "k (%d) must be a multiple of compress_ratio (%d) unless QSA_OUT_KEYS is set", k, compress_ratio);
-    const int32_t kb = out_keys ? k : k / compress_ratio;
+    REQUIRE((c.flags & ~(QSA_SCORE_RELU | QSA_OUT_KEYS)) == 0, QSA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x",
+            c.flags);
+    REQUIRE(c.k >= 1, QSA_ERR_INVALID_ARGUMENT, "k must be >= 1 (got %d)", c.k);
+    const bool out_keys = (c.flags & QSA_OUT_KEYS) != 0;
+    REQUIRE(out_keys || c.k % c.compress_ratio == 0, QSA_ERR_INVALID_ARGUMENT,
+            "k (%d) must be a multiple of compress_ratio (%d) unless QSA_OUT_KEYS is set", c.k, c.compress_ratio);
+    const int32_t kb = out_keys ? c.k : c.k / c.compress_ratio;
     REQUIRE(kb <= QSA_MAX_SELECT, QSA_ERR_UNSUPPORTED, "%d selected entries per row exceed the limit %d", kb,
             QSA_MAX_SELECT);
-    const size_t need = qsa_select_paged_tokens_workspace_size(rows, num_reqs, max_visible, compress_ratio, k,
-                                                               flags);
-    REQUIRE(workspace_bytes >= need, QSA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < required %zu",
-            workspace_bytes, need);
-    if (rows == 0) return QSA_OK;
-    REQUIRE(out != nullptr, QSA_ERR_INVALID_ARGUMENT, "null pointer: out");
-    REQUIRE(need == 0 || workspace != nullptr, QSA_ERR_INVALID_ARGUMENT, "null pointer: workspace");
-    const DeviceInfo* dev = nullptr;
-    if ((st = check_device(&dev)) != QSA_OK) return st;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    *need = qsa_select_paged_tokens_workspace_size(c.rows, c.num_reqs, c.max_visible, c.compress_ratio, c.k,
+                                                   c.flags);
+    return QSA_OK;
+}
 
-    qsa::PagedArgs a = make_paged(q, kcache, page_table, pt_stride, num_pages, num_reqs, row_req, pos, rows,
-                                  page_size, compress_ratio, max_visible, flags);
+// The launches of a checked select call with rows > 0 on `workspace` (at
+// least the bytes check_select asked for).
+qsa_status run_select(const SelectCall& c, void* workspace, const DeviceInfo* dev, hipStream_t s) {
+    const bool out_keys = (c.flags & QSA_OUT_KEYS) != 0;
+    const int32_t kb = out_keys ? c.k : c.k / c.compress_ratio;
+    qsa::PagedArgs a = make_paged(c.q, c.kcache, c.page_table, c.pt_stride, c.num_pages, c.num_reqs, c.row_req,
+                                  c.pos, c.rows, c.page_size, c.compress_ratio, c.max_visible, c.flags);
     qsa::VisibleSource vs;
     vs.visible = nullptr;
-    vs.pos = pos;
-    vs.row_req = row_req;
-    vs.num_reqs = num_reqs;
-    vs.cr = compress_ratio;
-    vs.max_visible = max_visible;
-    const int32_t expand = out_keys ? 1 : compress_ratio;
-    if (choose_path(rows, num_reqs, max_visible) == Path::Fused) {
-        const FusedLayout L = fused_layout(rows, max_visible, kb);
+    vs.pos = c.pos;
+    vs.row_req = c.row_req;
+    vs.num_reqs = c.num_reqs;
+    vs.cr = c.compress_ratio;
+    vs.max_visible = c.max_visible;
+    const int32_t expand = out_keys ? 1 : c.compress_ratio;
+    if (choose_path(c.rows, c.num_reqs, c.max_visible) == Path::Fused) {
+        const FusedLayout L = fused_layout(c.rows, c.max_visible, kb);
         unsigned char* w = static_cast<unsigned char*>(workspace);
         float* samp = reinterpret_cast<float*>(w + L.off_samp);
         uint64_t* thresh = reinterpret_cast<uint64_t*>(w + L.off_thresh);
@@ -471,27 +486,107 @@ QSA_EXPORT qsa_status qsa_select_paged_tokens(const void* q, const void* kcache,
         HIP_CHECK(mark(s));
         HIP_CHECK(qsa::launch_score_store(a, qsum, L.plan.stride, false, samp, L.plan.ld_s, cus, s));
         HIP_CHECK(mark(s));
-        HIP_CHECK(qsa::launch_sample_threshold(samp, L.plan.ld_s, vs, L.plan, force_fallback(), thresh, count, rows, s));
+        HIP_CHECK(qsa::launch_sample_threshold(samp, L.plan.ld_s, vs, L.plan, force_fallback(), thresh, count,
+                                               c.rows, s));
         HIP_CHECK(mark(s));
         HIP_CHECK(qsa::launch_score_filter(a, qsum, thresh, cand, count, L.plan.cand_cap, cus, s));
         HIP_CHECK(mark(s));
-        HIP_CHECK(qsa::launch_fused_final(a, vs, L.plan, thresh, cand, count, kb, expand, k, out, s));
+        HIP_CHECK(qsa::launch_fused_final(a, vs, L.plan, thresh, cand, count, kb, expand, c.k, c.out, s));
         HIP_CHECK(mark(s));
         g_events = nullptr;
         g_path = "fused";
         return QSA_OK;
     }
     float* scores = static_cast<float*>(workspace);
-    const int64_t ld = two_pass_ld(max_visible);
+    const int64_t ld = two_pass_ld(c.max_visible);
     HIP_CHECK(mark(s));
     _Float16* qsum = a.relu ? nullptr
                             : reinterpret_cast<_Float16*>(static_cast<unsigned char*>(workspace) +
-                                                          two_pass_scores_bytes(rows, max_visible));
-    if (max_visible > 0) HIP_CHECK(qsa::launch_score_paged(a, qsum, scores, ld, dev->cus, scorer_choice(), s));
+                                                          two_pass_scores_bytes(c.rows, c.max_visible));
+    if (c.max_visible > 0) HIP_CHECK(qsa::launch_score_paged(a, qsum, scores, ld, dev->cus, scorer_choice(), s));
     HIP_CHECK(mark(s));
-    HIP_CHECK(qsa::launch_topk_rows(scores, ld, vs, rows, kb, expand, k, out, s));
+    HIP_CHECK(qsa::launch_topk_rows(scores, ld, vs, c.rows, kb, expand, c.k, c.out, s));
     HIP_CHECK(mark(s));
     g_events = nullptr;
     g_path = "two_pass";
     return QSA_OK;
+}
+
+struct ScratchSlot {
+    std::atomic<void*> ptr{nullptr};
+};
+ScratchSlot g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (looked up on its first use
+// there, with that device current).
+qsa_status device_scratch(void** out) {
+    int dev = -1;
+    HIP_CHECK(hipGetDevice(&dev));
+    REQUIRE(dev >= 0 && dev < kMaxDevices, QSA_ERR_UNSUPPORTED, "device index %d out of range", dev);
+    void* p = g_scratch[dev].ptr.load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].ptr.load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            void* found = nullptr;
+            HIP_CHECK(hipGetSymbolAddress(&found, HIP_SYMBOL(scratch)));
+            REQUIRE(found != nullptr, QSA_ERR_DEVICE, "hipGetSymbolAddress returned no address for the scratch");
+            g_scratch[dev].ptr.store(found, std::memory_order_release);
+            p = found;
+        }
+    }
+    *out = p;
+    return QSA_OK;
+}
+
+}  // namespace
+
+QSA_EXPORT qsa_status qsa_select_paged_tokens(const void* q, const void* kcache, const int32_t* page_table,
+                                              int64_t pt_stride, int32_t num_pages, int32_t num_reqs,
+                                              const int32_t* row_req, const int32_t* pos, int32_t rows,
+                                              int32_t heads, int32_t head_dim, int32_t page_size,
+                                              int32_t compress_ratio, int32_t max_visible, int32_t k,
+                                              uint32_t flags, int32_t* out, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+    g_err[0] = 0;
+    g_recorded = 0;
+    const SelectCall c{q, kcache, page_table, pt_stride, num_pages, num_reqs, row_req, pos, rows, heads, head_dim,
+                       page_size, compress_ratio, max_visible, k, flags, out};
+    size_t need = 0;
+    qsa_status st = check_select(c, &need);
+    if (st != QSA_OK) return st;
+    REQUIRE(workspace_bytes >= need, QSA_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes < required %zu",
+            workspace_bytes, need);
+    if (rows == 0) return QSA_OK;
+    REQUIRE(out != nullptr, QSA_ERR_INVALID_ARGUMENT, "null pointer: out");
+    REQUIRE(need == 0 || workspace != nullptr, QSA_ERR_INVALID_ARGUMENT, "null pointer: workspace");
+    const DeviceInfo* dev = nullptr;
+    if ((st = check_device(&dev)) != QSA_OK) return st;
+    return run_select(c, workspace, dev, static_cast<hipStream_t>(stream));
+}
+
+QSA_EXPORT qsa_status qsa_select_paged_tokens_noalloc(const void* q, const void* kcache, const int32_t* page_table,
+                                                      int64_t pt_stride, int32_t num_pages, int32_t num_reqs,
+                                                      const int32_t* row_req, const int32_t* pos, int32_t rows,
+                                                      int32_t heads, int32_t head_dim, int32_t page_size,
+                                                      int32_t compress_ratio, int32_t max_visible, int32_t k,
+                                                      uint32_t flags, int32_t* out, void* stream) {
+    g_err[0] = 0;
+    g_recorded = 0;
+    const SelectCall c{q, kcache, page_table, pt_stride, num_pages, num_reqs, row_req, pos, rows, heads, head_dim,
+                       page_size, compress_ratio, max_visible, k, flags, out};
+    size_t need = 0;
+    qsa_status st = check_select(c, &need);
+    if (st != QSA_OK) return st;
+    REQUIRE(need <= (size_t)QSA_NOALLOC_SCRATCH_BYTES, QSA_ERR_UNSUPPORTED,
+            "this call needs %zu bytes of scratch, more than the %llu the allocation-free entry point holds; "
+            "use qsa_select_paged_tokens with a workspace", need, (unsigned long long)QSA_NOALLOC_SCRATCH_BYTES);
+    if (rows == 0) return QSA_OK;
+    REQUIRE(out != nullptr, QSA_ERR_INVALID_ARGUMENT, "null pointer: out");
+    const DeviceInfo* dev = nullptr;
+    if ((st = check_device(&dev)) != QSA_OK) return st;
+    void* ws = nullptr;
+    if ((st = device_scratch(&ws)) != QSA_OK) return st;
+    return run_select(c, ws, dev, static_cast<hipStream_t>(stream));
 }

@@ -29,6 +29,8 @@ QSA_OUT_KEYS = 0x2
 QSA_ROPE_INTERLEAVED = 0x4
 QSA_MAX_SELECT = 4096
 
+QSA_NOALLOC_SCRATCH_BYTES = 96 << 20
+
 QSA_DEBUG_FORCE_TWO_PASS = 0x1
 QSA_DEBUG_FORCE_FUSED = 0x2
 QSA_DEBUG_FORCE_FALLBACK = 0x4
@@ -37,7 +39,8 @@ QSA_DEBUG_FORCE_GROUPS = 0x10
 
 EXPORTED = (
     "qsa_score_paged", "qsa_topk_rows", "qsa_topk_rows_workspace_size",
-    "qsa_select_paged_tokens", "qsa_select_paged_tokens_workspace_size", "qsa_sparse_attention",
+    "qsa_select_paged_tokens", "qsa_select_paged_tokens_workspace_size", "qsa_select_paged_tokens_noalloc",
+    "qsa_sparse_attention",
     "qsa_sparse_attention_workspace_size", "qsa_compress_keys", "qsa_last_error", "qsa_last_path", "qsa_version",
     "qsa_debug_record_events", "qsa_debug_events_recorded", "qsa_debug_force", "qsa_debug_forced",
 )
@@ -72,6 +75,9 @@ def lib():
     L.qsa_select_paged_tokens.argtypes = [P, P, P, i64, i32, i32, P, P, i32, i32, i32, i32, i32, i32, i32, u32,
                                           P, P, sz, P]
     L.qsa_select_paged_tokens.restype = ctypes.c_int
+    L.qsa_select_paged_tokens_noalloc.argtypes = [P, P, P, i64, i32, i32, P, P, i32, i32, i32, i32, i32, i32,
+                                                  i32, u32, P, P]
+    L.qsa_select_paged_tokens_noalloc.restype = ctypes.c_int
     L.qsa_select_paged_tokens_workspace_size.argtypes = [i32, i32, i32, i32, i32, u32]
     L.qsa_select_paged_tokens_workspace_size.restype = sz
     L.qsa_sparse_attention.argtypes = [P, P, P, P, i64, i32, i32, P, P, i32, i32, i32, i32, i32, i32,
@@ -378,4 +384,23 @@ def qsa_select_paged_tokens(q, kcache, page_table, pos, compress_ratio, k, *, ma
         _ptr(q), _ptr(kcache), _ptr(page_table), page_table.shape[1], kcache.shape[0], num_reqs,
         _ptr(row_req), _ptr(pos), rows, heads, head_dim, page_size, int(compress_ratio), int(max_visible),
         int(k), int(flags), _ptr(out), _ptr(workspace), wbytes, _stream(dev)))
+    return out
+
+
+def qsa_select_paged_tokens_noalloc(q, kcache, page_table, pos, compress_ratio, k, *, max_visible, out,
+                                    row_req=None, flags=0) -> torch.Tensor:
+    """qsa_select_paged_tokens without a workspace (the library's static
+    per-device scratch of QSA_NOALLOC_SCRATCH_BYTES); the caller passes
+    ``out`` int32 [rows, k], so nothing is allocated.  Calls that overlap on
+    one device race on the shared scratch."""
+    _paged_inputs(q, kcache, page_table, pos, row_req)
+    rows, heads, head_dim = q.shape
+    _want(out, "out", torch.int32, 2)
+    _want_shape(out, "out", (rows, k))
+    dev = _on_device(q=q, kcache=kcache, page_table=page_table, pos=pos, row_req=row_req, out=out)
+    page_size = kcache.shape[1] * int(compress_ratio)
+    _check(lib().qsa_select_paged_tokens_noalloc(
+        _ptr(q), _ptr(kcache), _ptr(page_table), page_table.shape[1], kcache.shape[0], page_table.shape[0],
+        _ptr(row_req), _ptr(pos), rows, heads, head_dim, page_size, int(compress_ratio), int(max_visible),
+        int(k), int(flags), _ptr(out), _stream(dev)))
     return out

@@ -347,3 +347,21 @@ def test_binding_refuses_host_tensors_and_bad_shapes_for_the_adjacent_steps():
     with pytest.raises(TypeError):
         Q.qsa_sparse_attention(torch.zeros((2, 24, 256)), f16(4, 64, 2, 256), f16(4, 64, 2, 256), i32(1, 4),
                                i32(2, 16))
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    """A call whose workspace would exceed the static scratch is refused on
+    the host, naming both sizes, before any device call."""
+    need = Q.qsa_select_paged_tokens_workspace_size(4096, 1, 200000, 4, 2048)
+    assert need > Q.QSA_NOALLOC_SCRATCH_BYTES
+    st = Q.lib().qsa_select_paged_tokens_noalloc(FAKE, FAKE, FAKE, 12500, 20000, 1, None, FAKE, 4096, 4, 128, 64,
+                                                 4, 200000, 2048, 0, FAKE, None)
+    assert st == Q.QSA_ERR_UNSUPPORTED
+    msg = Q.qsa_last_error()
+    assert str(need) in msg and str(Q.QSA_NOALLOC_SCRATCH_BYTES) in msg
+    # argument errors come first, as in the workspace entry point
+    st = Q.lib().qsa_select_paged_tokens_noalloc(FAKE, FAKE, FAKE, 12500, 20000, 1, None, FAKE, 4096, 5, 128, 64,
+                                                 4, 200000, 2048, 0, FAKE, None)
+    assert st == Q.QSA_ERR_UNSUPPORTED and "heads" in Q.qsa_last_error()
+    assert Q.lib().qsa_select_paged_tokens_noalloc(None, None, None, 1, 1, 1, None, None, 0, 4, 128, 64, 4, 0, 64,
+                                                   0, None, None) == Q.QSA_OK

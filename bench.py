@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--stats-dir", default=None)
     ap.add_argument("--fetch-dir", default=None)
     ap.add_argument("--write-dir", default=None)
+    ap.add_argument("--counters-dir", action="append", default=[],
+                    help="a `rocprofv3 --pmc ...` run of this script (repeatable: one per counter pass)")
     ap.add_argument("--kernel", default="filter_scorer")
     ap.add_argument("--command", default=None)
     return ap.parse_args()
@@ -121,6 +123,80 @@ def traffic_for(kernel_name, workload):
     if rec.get("source_digest") != source_digest(KERNEL_SOURCES[kernel_name][1]):
         return None
     return rec.get("bytes_per_launch")
+
+
+def counters_for(kernel_name, workload):
+    """Hardware-counter summary of a kernel from a committed rocprofv3 --pmc
+    record, only if it was taken on the kernel's current source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_name}_{workload}_counters.json")
+    if not os.path.exists(path) or kernel_name not in KERNEL_SOURCES:
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest(KERNEL_SOURCES[kernel_name][1]):
+        return None
+    return rec
+
+
+SIMDS = 1024  # 256 CUs x 4 SIMDs
+
+
+def summarize_counters(args, name):
+    """Per-launch means of every counter in the --counters-dir runs for the
+    chosen kernel, and the MFMA figures derived from them:
+      mfma_busy      = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1,024 SIMDs)
+                       (the share of SIMD cycles the matrix pipe was busy);
+      executed_flop  = SQ_INSTS_VALU_MFMA_MOPS_F16 x 512;
+      executed_frac  = executed_flop / launch duration / 2.5 PFLOP/s.
+    rocprofv3 reports each counter once per dispatch, summed over the
+    hardware instances; GRBM_GUI_ACTIVE is divided by its instance count (one
+    per XCD), which the duration check below confirms."""
+    import glob
+    kname = args.kernel
+    subs = KERNEL_SOURCES[kname][0]
+    sums, counts, durations, meta = {}, {}, [], {}
+    for d in args.counters_dir:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            seen = set()
+            for r in _read_csv(path):
+                if not all(sub in r["Kernel_Name"] for sub in subs):
+                    continue
+                c = r["Counter_Name"]
+                sums[c] = sums.get(c, 0.0) + float(r["Counter_Value"])
+                counts[c] = counts.get(c, 0) + 1
+                key = (path, r["Dispatch_Id"])
+                if key not in seen:
+                    seen.add(key)
+                    durations.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+                    for f in ("VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "LDS_Block_Size", "Workgroup_Size",
+                              "Grid_Size"):
+                        if f in r:
+                            meta[f] = r[f]
+    mean = {c: sums[c] / counts[c] for c in sums}
+    dur = sum(durations) / len(durations) if durations else None
+    rec = {"kernel": kname, "workload": name, "symbol_substrings": list(subs),
+           "source_digest": source_digest(KERNEL_SOURCES[kname][1]), "dispatches": counts,
+           "counters_per_launch": {c: round(v, 1) for c, v in sorted(mean.items())},
+           "mean_duration_us": round(dur * 1e6, 2) if dur else None, "launch": meta, "command": args.command}
+    gui = mean.get("GRBM_GUI_ACTIVE")
+    if dur and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+        # busy share of the launch's SIMD cycles at the 2.4 GHz peak clock
+        rec["mfma_busy"] = round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (dur * 2.4e9 * SIMDS), 4)
+        if gui:
+            # the same over GRBM_GUI_ACTIVE (one count per XCD and cycle): it also spans
+            # the dispatch around the kernel, so it reads lower on short launches
+            rec["mfma_busy_over_gui_cycles"] = round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui / 8 * SIMDS), 4)
+            rec["gui_cycles_per_xcd"] = round(gui / 8)
+    if "SQ_INSTS_VALU_MFMA_MOPS_F16" in mean and dur:
+        flop = mean["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512
+        rec["executed_flop"] = round(flop)
+        rec["executed_frac"] = round(flop / dur / (PEAK_MFMA_F16_TFLOPS * 1e12), 4)
+    if "SQ_LDS_BANK_CONFLICT" in mean and "SQ_LDS_IDX_ACTIVE" in mean and mean["SQ_LDS_IDX_ACTIVE"] > 0:
+        rec["lds_bank_conflict_share"] = round(mean["SQ_LDS_BANK_CONFLICT"] / mean["SQ_LDS_IDX_ACTIVE"], 4)
+    path = os.path.join(ROOT, "profiles", f"{kname}_{name}_counters.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    return path
 
 
 def _read_csv(path):
@@ -190,6 +266,8 @@ def summarize_profile(args):
         with open(path, "w") as f:
             json.dump(rec, f, indent=1)
         out["traffic"] = path
+    if args.counters_dir:
+        out["counters"] = summarize_counters(args, name)
     print(json.dumps(out))
     return 0
 

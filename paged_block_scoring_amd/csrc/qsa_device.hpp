@@ -129,13 +129,15 @@ __device__ __forceinline__ void head_sum_split(const half8& q0, const half8& q1,
     }
 }
 
+// relu of a finite fp32 as one integer max: a value with the sign bit set
+// (negative, or -0) is a negative int32 and becomes +0; any other value keeps
+// its bits.  (fmaxf would also quiet signalling NaNs first, one more VALU
+// operation per head; inputs are finite.)
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // The four head dots of one (row, key) -> score (relu form).
 __device__ __forceinline__ float combine_relu_heads(float h0, float h1, float h2, float h3) {
-    h0 = fmaxf(h0, 0.0f);
-    h1 = fmaxf(h1, 0.0f);
-    h2 = fmaxf(h2, 0.0f);
-    h3 = fmaxf(h3, 0.0f);
-    const float s = ((h0 + h1) + h2) + h3;
+    const float s = ((relu_bits(h0) + relu_bits(h1)) + relu_bits(h2)) + relu_bits(h3);
     return s * kRsqrtHeadDim;
 }
 

@@ -35,8 +35,9 @@
 //   Store  -- out[row*ld + i] = score with 16-byte stores (two-pass arm,
 //             sampling pass);
 //   Filter -- keep (score, key) if score >= the row's threshold score: one
-//             compare per score against a per-lane threshold; a prefix sum
-//             over the row's 4 lanes gives each kept entry its slot in the
+//             compare per score against a per-lane threshold, whose ballot is
+//             the exec mask of that score's append (no branch); a prefix sum
+//             over the row's 4 lanes gives each lane its first slot in the
 //             row's LDS staging list (score bits, key), which the lanes move
 //             to the row's global list -- one atomic per row -- when it would
 //             overflow and when the workgroup leaves the tile.
@@ -365,22 +366,32 @@ __global__ __launch_bounds__(ScoreShape::NT, ReluForm::WG_PER_CU) void score_til
                                 if (full || key0 + i < lim_r) dst[i] = v[i];
                         }
                     } else {
-                        bool kp[8];
-                        int n = 0;
+                        // the ballot of each compare is the exec mask of that
+                        // score's append (no branch); bounds only on a tile
+                        // that crosses a row's end
+                        uint64_t m[16];
+                        if (full) {
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            kp[i] = v[i] >= fT_r && (full || key0 + i < lim_r);
-                            n += kp[i] ? 1 : 0;
+                            for (int i = 0; i < 8; ++i) m[i] = __builtin_amdgcn_ballot_w64(v[i] >= fT_r);
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 8; ++i)
+                                m[i] = __builtin_amdgcn_ballot_w64(v[i] >= fT_r && key0 + i < lim_r);
                         }
+#pragma unroll
+                        for (int i = 8; i < 16; ++i) m[i] = 0ull;
+                        int n = 0;
+                        count_masks8(m, 0, n);
                         int tot;
                         const int excl = quad_exclusive_sum(n, &tot);
                         uint64_t* lb = s_lbuf + erow * kLCap;
                         if (__any(cnt_r + tot > kLCap))
                             flush_staged(A, lb, r0 + erow, cnt_r, g_leader, g_member, g_size);
-                        int slot = cnt_r + excl;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            if (kp[i]) lb[slot++] = cand_entry(v[i], key0 + i);
+                        // entries (key, score bits) from this lane's slot of the row's list on
+                        uint32_t ad = (uint32_t)reinterpret_cast<uintptr_t>(static_cast<void*>(lb + cnt_r + excl));
+                        const float16v sv = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7],
+                                             0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                        append_masks8(m, sv, 0, key0, ad);
                         cnt_r += tot;
                     }
                 }

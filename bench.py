@@ -62,7 +62,12 @@ def parse():
                          "instead of the plain head sum the workloads are defined with")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph (reported as graph_ms_per_step)")
-    ap.add_argument("--cpu-sample-rows", type=int, default=512)
+    ap.add_argument("--cpu-sample-rows", type=int, default=96,
+                    help="rows of the headline workload the CPU oracle is timed on")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time the headline workload only (no per-configuration table)")
+    ap.add_argument("--config-steps", type=int, default=10,
+                    help="timed steps of each configuration in the per-configuration table")
     ap.add_argument("--workload", default="kernel_shape",
                     choices=["tiny", "kernel_shape", "tie_stress", "mixed", "decode", "long_1", "long_8"])
     ap.add_argument("--path", choices=["two_pass", "fused"], default=None,
@@ -418,6 +423,206 @@ def bench_producer(args, w, torch, Q):
     return 0
 
 
+CONFIG_ORDER = ["tiny", "kernel_shape", "tie_stress", "mixed", "decode"]
+CONTEXT = {
+    "pages_kernel_shape_ms_per_call": {
+        "before": 505.38, "after": 10.86, "hardware": "Quadro RTX 8000 (Turing)",
+        "source": "[Perf][Qwen4Exp] Admit the cuBLAS QSA indexer and exact top-k on Turing: Test Result"},
+    "pages_paged_scorer_s_per_stage": {
+        "values": [20.0, 30.1], "what": "paged Triton scorer, total per pipeline stage of a 184k-token PP4 "
+                                        "prefill on two Quadro RTX 8000 stages (all chunks and layers)",
+        "source": "[Perf][Qwen4Exp] Admit the cuBLAS QSA indexer and exact top-k on Turing: Purpose"},
+    "vs_baseline_basis": "value / (1,616 rows / 10.86 ms): the pages' figure for this workload on another "
+                         "GPU generation; context, not a target",
+}
+
+
+class Run:
+    """One workload resident on the GPU and its timed indexer calls."""
+
+    def __init__(self, name, args, torch, Q, W, relu=False):
+        self.name, self.torch, self.Q = name, torch, Q
+        self.w = w = W.make(name)
+        dev = self.dev = torch.device("cuda:0")
+        self.q = torch.from_numpy(w.q).to(dev)
+        self.kc = torch.from_numpy(w.kcache).to(dev)
+        self.pt = torch.from_numpy(w.page_table).to(dev)
+        self.pos = torch.from_numpy(w.pos).to(dev)
+        self.row_req = torch.from_numpy(w.row_req).to(dev)
+        self.cr, self.k = w.compress_ratio, w.k
+        # work counts of the measurement (keys of each row: (pos + 1) // cr)
+        self.vis = (w.pos.astype(np.int64) + 1) // self.cr
+        self.sum_v, self.max_v, self.rows = int(self.vis.sum()), int(self.vis.max()), w.rows
+        self.flags = Q.QSA_SCORE_RELU if relu else 0
+        self.out = torch.empty((self.rows, self.k), dtype=torch.int32, device=dev)
+        need = Q.qsa_select_paged_tokens_workspace_size(self.rows, w.num_reqs, self.max_v, self.cr, self.k, self.flags)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def step(self):
+        self.Q.qsa_select_paged_tokens(self.q, self.kc, self.pt, self.pos, self.cr, self.k, row_req=self.row_req,
+                                       max_visible=self.max_v, out=self.out, workspace=self.ws, flags=self.flags)
+
+    def gpu_scores(self):
+        """Scores of every row by qsa_score_paged (for the parity check)."""
+        return self.Q.qsa_score_paged(self.q, self.kc, self.pt, self.pos, self.cr, row_req=self.row_req,
+                                      max_visible=self.max_v, flags=self.flags & self.Q.QSA_SCORE_RELU)
+
+    def measure(self, steps, warmup):
+        torch, Q = self.torch, self.Q
+        ms, wall = time_calls(self.step, steps, warmup, torch)
+        path = Q.qsa_last_path()
+        kms, ms_inst = kernel_times(self.step, steps, KERNELS[path], torch, Q)
+        w, rows, k = self.w, self.rows, self.k
+        flops_full = FLOPS_PER_ROW_KEY * self.sum_v
+        units = {}
+        if path == "fused":
+            stride = 16
+            while (self.max_v + stride - 1) // stride > 4096:
+                stride *= 2
+            sampled = int(((self.vis + stride - 1) // stride).sum())
+            units["filter_scorer"] = ("mfma", flops_full, PEAK_MFMA_F16_TFLOPS, "TFLOP/s")
+            units["sample_scorer"] = ("mfma", FLOPS_PER_ROW_KEY * sampled, PEAK_MFMA_F16_TFLOPS, "TFLOP/s")
+        elif rows < 32 * w.num_reqs:
+            # few rows per request: every key streams from HBM for one row (256 B per key)
+            units["scorer"] = ("hbm", 256 * self.sum_v + 1024 * rows, PEAK_HBM_GBS, "GB/s")
+            units["topk_rows"] = ("hbm", 4 * self.sum_v + 4 * rows * k, PEAK_HBM_GBS, "GB/s")
+        else:
+            units["scorer"] = ("mfma", flops_full, PEAK_MFMA_F16_TFLOPS, "TFLOP/s")
+            units["topk_rows"] = ("hbm", 4 * self.sum_v + 4 * rows * k, PEAK_HBM_GBS, "GB/s")
+        dom = max((n for n in kms if n in units), key=lambda n: kms[n])
+        bound, work, peak, unit = units[dom]
+        scale = 1e12 if unit == "TFLOP/s" else 1e9
+        achieved = work / (kms[dom] * 1e-3) / scale
+        relu = bool(self.flags & Q.QSA_SCORE_RELU)
+        roof = {"kernel": dom, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4),
+                # the counter profiles are of the default form's kernels
+                "traffic": None if relu else traffic_for(dom, self.name),
+                "ms_per_launch": round(kms[dom], 4)}
+        cnt = None if relu else counters_for(dom, self.name)
+        if bound == "mfma":
+            roof["algorithmic_flop_per_launch"] = work
+            if cnt and cnt.get("executed_flop"):
+                # executed MFMA flop (rocprofv3 SQ_INSTS_VALU_MFMA_MOPS_F16 x 512) over this run's launch time
+                roof["counter_executed_frac"] = round(
+                    cnt["executed_flop"] / (kms[dom] * 1e-3) / (PEAK_MFMA_F16_TFLOPS * 1e12), 4)
+                roof["counter_mfma_busy"] = cnt.get("mfma_busy")
+            else:
+                roof["counter_executed_frac"] = None
+            if path == "fused":
+                scoring = sum(kms.get(n, 0.0) for n in ("qsum_prep", "sample_scorer", "filter_scorer"))
+                # every scoring launch of the step against the full algorithmic work
+                roof["scoring_frac"] = round(flops_full / (scoring * 1e-3) / (peak * 1e12), 4)
+        return {"ms_per_step": round(ms, 4), "rows_per_s": round(rows / (ms * 1e-3), 1),
+                "gkeys_per_s": round(self.sum_v / (ms * 1e-3) / 1e9, 3), "path": path,
+                "rows": rows, "requests": w.num_reqs, "k": k, "sum_visible_keys": self.sum_v,
+                "max_visible_keys": self.max_v, "kernels_ms": {n: round(v, 4) for n, v in kms.items()},
+                "ms_per_step_instrumented": round(ms_inst, 4), "roofline": roof, "wall_s_timed": round(wall, 4)}
+
+    def sample_rows(self, n):
+        return np.unique(np.linspace(0, self.rows - 1, min(n, self.rows)).round().astype(np.int64))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def median3(fn):
+    """Median wall time of three runs (one run when it takes over 30 s)."""
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+        if ts[-1] > 30.0:
+            break
+    return sorted(ts)[len(ts) // 2], len(ts)
+
+
+def cpu_baseline_leg(runs, head, args):
+    """The CPU oracle (test infrastructure) on the host cores, in two parts:
+    timing -- its score and select phases on a bounded row sample of the
+    headline workload (median of 3, all cores), and on the tiny and tie-stress
+    workloads with one thread;
+    parity -- each workload's timed GPU output on sampled rows against it:
+    scores of qsa_score_paged within 1e-3 * max(|ref|, 1), the GPU selection
+    equal to the oracle's selector applied to the GPU's own scores, and, on
+    the integer-valued tie-stress workload, the whole output bit-exact."""
+    import oracle
+    cores = os.cpu_count() or 1
+    res = {"kind": "oracle", "cores": cores, "cpu_model": cpu_model()}
+
+    def phases(run, sample, threads):
+        w = run.w
+        kb = run.k // run.cr
+        V = run.vis[sample].astype(np.int32)
+        args_ = (w.q[sample], w.kcache, w.page_table, w.pos[sample], run.cr)
+        sc = {}
+        t_score, n_s = median3(lambda: sc.__setitem__(
+            "s", oracle.score_paged(*args_, row_req=w.row_req[sample], flags=run.flags & oracle.SCORE_RELU,
+                                    nthreads=threads)))
+        t_sel, _ = median3(lambda: oracle.select_rows(sc["s"], V, kb, nthreads=threads))
+        n = len(sample)
+        keys = int(V.sum())
+        return {"rows": n, "threads": threads, "runs": n_s, "score_s": round(t_score, 3), "select_s": round(t_sel, 3),
+                "rows_per_s": round(n / (t_score + t_sel), 3), "gkeys_per_s": round(keys / (t_score + t_sel) / 1e9, 5)}
+
+    hs = head.sample_rows(args.cpu_sample_rows)
+    hp = phases(head, hs, cores)
+    res.update({"value": hp["rows_per_s"], "unit": "rows/s", "gkeys_per_s": hp["gkeys_per_s"],
+                "sample": f"{hp['rows']} of the {head.rows} rows of {head.name} (evenly spaced), each over its "
+                          f"full visible context; score phase {hp['score_s']} s and select phase "
+                          f"{hp['select_s']} s, median of {hp['runs']}, {cores} threads",
+                "phases": {head.name: hp}})
+    for name, n in (("tiny", 64), ("tie_stress", 32)):
+        if name in runs:
+            res["phases"][name + "_1thread"] = phases(runs[name], runs[name].sample_rows(n), 1)
+
+    parity = {}
+    for name, run in runs.items():
+        w = run.w
+        sample = run.sample_rows(64 if name == "tiny" else 16)
+        gs = run.gpu_scores()
+        run.torch.cuda.synchronize()
+        gsc = gs[torch_index(run, sample)].cpu().numpy()
+        del gs
+        out = run.out[torch_index(run, sample)].cpu().numpy()
+        ref = oracle.score_paged(w.q[sample], w.kcache, w.page_table, w.pos[sample], run.cr,
+                                 row_req=w.row_req[sample], flags=run.flags & oracle.SCORE_RELU, nthreads=cores)
+        V = np.array([oracle.visible_keys(int(p), run.cr) for p in w.pos[sample]], np.int32)
+        worst = 0.0
+        for i in range(len(sample)):
+            a = gsc[i, :V[i]].astype(np.float64)
+            b = ref[i, :V[i]].astype(np.float64)
+            if len(a):
+                worst = max(worst, float((np.abs(a - b) / np.maximum(np.abs(b), 1.0)).max()))
+        kb = run.k // run.cr
+        blocks = oracle.select_rows(gsc, V, kb, nthreads=cores)
+        tok = np.where(blocks[:, :, None] >= 0, blocks[:, :, None] * run.cr + np.arange(run.cr), -1)
+        tok = tok.reshape(len(sample), run.k).astype(np.int32)
+        same_sel = int(np.all(tok == out, axis=1).sum())
+        entry = {"rows_checked": int(len(sample)), "max_rel_score_err": worst, "scores_ok": bool(worst <= 1e-3),
+                 "selection_equal_rows": same_sel, "selection_ok": same_sel == len(sample)}
+        if name == "tie_stress":
+            full = oracle.select_paged_tokens(w.q[sample], w.kcache, w.page_table, w.pos[sample], run.cr, run.k,
+                                              row_req=w.row_req[sample], flags=run.flags, nthreads=cores)
+            entry["bit_exact_rows"] = int(np.all(full == out, axis=1).sum())
+            entry["bit_exact"] = entry["bit_exact_rows"] == len(sample)
+        parity[name] = entry
+    return res, parity
+
+
+def torch_index(run, sample):
+    return run.torch.from_numpy(sample).to(run.dev)
+
+
 def main():
     args = parse()
     if args.summarize_profile:
@@ -432,36 +637,17 @@ def main():
     if args.path:
         Q.qsa_debug_force({"two_pass": Q.QSA_DEBUG_FORCE_TWO_PASS, "fused": Q.QSA_DEBUG_FORCE_FUSED}[args.path])
 
-    w = W.make(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.producer:
-        return bench_producer(args, w, torch, Q)
-    q = torch.from_numpy(w.q).to(dev)
-    kc = torch.from_numpy(w.kcache).to(dev)
-    pt = torch.from_numpy(w.page_table).to(dev)
-    pos = torch.from_numpy(w.pos).to(dev)
-    row_req = torch.from_numpy(w.row_req).to(dev)
-    cr, k = w.compress_ratio, w.k
-    vis = (w.pos.astype(np.int64) + 1) // cr
-    sum_v = int(vis.sum())
-    max_v = int(vis.max())
-    rows = w.rows
-    out = torch.empty((rows, k), dtype=torch.int32, device=dev)
-    flags = Q.QSA_SCORE_RELU if args.relu else 0
-    ws_bytes = Q.qsa_select_paged_tokens_workspace_size(rows, w.num_reqs, max_v, cr, k, flags)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-
-    def step():
-        Q.qsa_select_paged_tokens(q, kc, pt, pos, cr, k, row_req=row_req, max_visible=max_v, out=out,
-                                  workspace=ws, flags=flags)
-
+        return bench_producer(args, W.make(args.workload), torch, Q)
+    head = Run(args.workload, args, torch, Q, W, relu=args.relu)
     if args.consumer:
-        return bench_consumer(args, w, step, out, q, pt, row_req, rows, k, torch, Q)
+        return bench_consumer(args, head.w, head.step, head.out, head.q, head.pt, head.row_req, head.rows,
+                              head.k, torch, Q)
 
-    # the timed region: exactly `steps` whole steps
-    ms_step, wall = time_calls(step, args.steps, args.warmup, torch)
-    path = Q.qsa_last_path()
+    # the timed region of the headline: exactly `steps` whole steps
+    m = head.measure(args.steps, args.warmup)
     graph_ms = None
     if args.graph:
         # the same step captured once in a HIP graph and replayed: what a
@@ -469,86 +655,67 @@ def main():
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step()
+            head.step()
         torch.cuda.current_stream().wait_stream(side)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            step()
+            head.step()
         graph_ms, _ = time_calls(g.replay, args.steps, args.warmup, torch)
-    # per-kernel durations of the same launches (instrumented repeat)
-    kms, ms_instrumented = kernel_times(step, args.steps, KERNELS[path], torch, Q)
 
-    flops_full = FLOPS_PER_ROW_KEY * sum_v
-    units = {}
-    if path == "fused":
-        stride = 16
-        while (max_v + stride - 1) // stride > 4096:
-            stride *= 2
-        sampled = int(((vis + stride - 1) // stride).sum())
-        units["filter_scorer"] = ("mfma", flops_full, PEAK_MFMA_F16_TFLOPS, "TFLOP/s")
-        units["sample_scorer"] = ("mfma", FLOPS_PER_ROW_KEY * sampled, PEAK_MFMA_F16_TFLOPS, "TFLOP/s")
-    elif rows < 32 * w.num_reqs:
-        # few rows per request: every key streams from HBM for one row (256 B per key)
-        units["scorer"] = ("hbm", 256 * sum_v + 1024 * rows, PEAK_HBM_GBS, "GB/s")
-        units["topk_rows"] = ("hbm", 4 * sum_v + 4 * rows * k, PEAK_HBM_GBS, "GB/s")
-    else:
-        units["scorer"] = ("mfma", flops_full, PEAK_MFMA_F16_TFLOPS, "TFLOP/s")
-        units["topk_rows"] = ("hbm", 4 * sum_v + 4 * rows * k, PEAK_HBM_GBS, "GB/s")
-    dom_name = max((n for n in kms if n in units), key=lambda n: kms[n])
-    bound, work, peak, unit = units[dom_name]
-    scale = 1e12 if unit == "TFLOP/s" else 1e9
-    achieved = work / (kms[dom_name] * 1e-3) / scale
-    roofline = {"kernel": dom_name, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4),
-                # the counter profiles are of the default form's kernels
-                "traffic": None if args.relu else traffic_for(dom_name, args.workload),
-                "ms_per_launch": round(kms[dom_name], 4)}
-
-    rows_per_s = rows / (ms_step * 1e-3)
     is_headline = args.workload == "kernel_shape"
+    rows_per_s = m["rows_per_s"]
     result = {
         "metric": "indexer rows/s and Gkeys scored/s at 1616x184k; % MFMA/HBM roofline",
-        "value": round(rows_per_s, 1),
+        "value": rows_per_s,
         "unit": "rows/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(rows_per_s / (rows / (PAGES_MS_PER_CALL * 1e-3)), 3) if is_headline else None,
+        "vs_baseline": round(rows_per_s / (head.rows / (PAGES_MS_PER_CALL * 1e-3)), 3) if is_headline else None,
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT.get(args.workload, args.workload),
-                   "rows": rows, "requests": w.num_reqs, "k": k, "sum_visible_keys": sum_v,
-                   "max_visible_keys": max_v, "parallelism": "single-gpu",
+                   "rows": head.rows, "requests": head.w.num_reqs, "k": head.k, "sum_visible_keys": head.sum_v,
+                   "max_visible_keys": head.max_v, "parallelism": "single-gpu",
                    "score_form": "relu per head, times 1/sqrt(128)" if args.relu else "plain head sum"},
-        "gkeys_per_s": round(sum_v / (ms_step * 1e-3) / 1e9, 3),
-        "path": path,
-        "kernels_ms": {n: round(v, 4) for n, v in kms.items()},
-        "ms_per_step_instrumented": round(ms_instrumented, 4),
-        "roofline": roofline,
-        "wall_s_timed": round(wall, 4),
+        "gkeys_per_s": m["gkeys_per_s"],
+        "path": m["path"],
+        "kernels_ms": m["kernels_ms"],
+        "ms_per_step_instrumented": m["ms_per_step_instrumented"],
+        "roofline": m["roofline"],
+        "wall_s_timed": m["wall_s_timed"],
+        "context": CONTEXT if is_headline else None,
     }
     if graph_ms is not None:
         result["graph_ms_per_step"] = round(graph_ms, 4)
-
     copy_probe(args, torch, dev)
 
+    # every measured configuration, each timed the same way (fewer steps)
+    runs = {args.workload: head}
+    if not args.no_configs:
+        configs = {}
+        for name in CONFIG_ORDER:
+            run = runs.get(name) or Run(name, args, torch, Q, W, relu=args.relu)
+            runs[name] = run
+            r = m if name == args.workload else run.measure(args.config_steps, 2)
+            configs[name] = {k: r[k] for k in ("ms_per_step", "rows_per_s", "gkeys_per_s", "path", "rows",
+                                               "sum_visible_keys", "kernels_ms", "roofline")}
+            configs[name]["workload"] = WORKLOAD_TEXT[name]
+        result["configs"] = configs
+
     if not args.no_cpu_baseline:
-        import oracle
-        n = min(args.cpu_sample_rows, rows)
-        sample = np.unique(np.linspace(0, rows - 1, n).round().astype(np.int64))
-        cores = os.cpu_count() or 1
-        t0 = time.perf_counter()
-        oracle.select_paged_tokens(w.q[sample], w.kcache, w.page_table, w.pos[sample], cr, k,
-                                   row_req=w.row_req[sample], nthreads=cores)
-        dt = time.perf_counter() - t0
-        result["cpu_baseline"] = {
-            "value": round(len(sample) / dt, 3), "unit": "rows/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(sample)} of the {rows} rows (evenly spaced), each over its full visible context; "
-                      f"oracle score + exact select + expand took {dt:.1f} s",
-        }
+        cpu, parity = cpu_baseline_leg(runs, head, args)
+        result["cpu_baseline"] = cpu
+        result["parity"] = parity
+        result["parity_ok"] = all(p["scores_ok"] and p["selection_ok"] and p.get("bit_exact", True)
+                                  for p in parity.values())
+        if "configs" in result:
+            for name, p in parity.items():
+                if name in result["configs"]:
+                    result["configs"][name]["parity"] = p
     print(json.dumps(result), flush=True)
     return 0
 

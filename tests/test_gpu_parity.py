@@ -474,10 +474,21 @@ def sampled_parity(oracle_mod, w, flags, integer, sample_rows, paths=(None,)):
     return out
 
 
-def test_full_kernel_shape(oracle_mod):
+def _spread(n_rows, n, seed):
+    """n distinct rows spread over the batch (seeded), with both ends."""
+    rng = np.random.default_rng(seed)
+    return sorted(set([0, n_rows - 1] + list(rng.choice(n_rows, size=min(n, n_rows), replace=False))))
+
+
+@pytest.mark.parametrize("flags", [0, RELU])
+def test_full_kernel_shape(oracle_mod, flags):
+    """The benchmark's kernel shape in both score forms: 64 sampled rows
+    (with the tile edges) scored by the oracle; every row's selection checked
+    in the fused arm, the two-pass arm and the fused arm's exact recompute
+    path."""
     w = W.kernel_shape()
-    sampled_parity(oracle_mod, w, 0, False, [0, 1, 63, 64, 800, 1550, 1599, 1600, 1615],
-                   paths=(None, "two_pass"))
+    rows = sorted(set(_spread(w.rows, 56, 5) + [63, 64, 127, 128, 1535, 1536, 1599, 1600]))
+    sampled_parity(oracle_mod, w, flags, False, rows, paths=(None, "two_pass", "fused_fallback"))
 
 
 def test_full_tie_stress(oracle_mod):
@@ -490,11 +501,14 @@ def test_full_tie_stress(oracle_mod):
         assert np.array_equal(out, full), path
 
 
-def test_full_mixed(oracle_mod):
+@pytest.mark.parametrize("flags", [0, RELU])
+def test_full_mixed(oracle_mod, flags):
+    """Mixed batch in both score forms: each request's first and last row
+    and 32 more sampled rows; every row's selection in both arms."""
     w = W.mixed()
     starts = np.concatenate([[0], np.cumsum(np.bincount(w.row_req))])
-    sample = list(starts[:-1]) + list(starts[1:] - 1)
-    sampled_parity(oracle_mod, w, 0, False, sample, paths=(None, "two_pass"))
+    sample = sorted(set(list(starts[:-1]) + list(starts[1:] - 1) + _spread(w.rows, 32, 6)))
+    sampled_parity(oracle_mod, w, flags, False, sample, paths=(None, "two_pass", "fused"))
 
 
 @pytest.mark.parametrize("name", ["long_1", "long_8"])
@@ -505,6 +519,9 @@ def test_full_long_few(oracle_mod, name):
 
 
 @pytest.mark.slow
-def test_full_decode(oracle_mod):
+@pytest.mark.parametrize("flags", [0, RELU])
+def test_full_decode(oracle_mod, flags):
+    """Decode batch in both score forms: every row's scores against the
+    oracle, and every row's selection in both arms."""
     w = W.decode()
-    sampled_parity(oracle_mod, w, 0, False, list(range(0, 256, 17)))
+    sampled_parity(oracle_mod, w, flags, False, list(range(w.rows)), paths=(None, "fused"))

@@ -242,6 +242,29 @@ def test_large_query_scorers(oracle_mod, name):
         assert np.array_equal(gpu_select(d, w, 0), full)
 
 
+GEOMETRIES = [
+    # (compress_ratio, page_size): keys per page 16 (the benchmark), 24 (not a
+    # power of two), 8, 1 (a page per key) and 64 (a stage spans half a page)
+    (4, 64), (2, 48), (8, 64), (1, 4), (4, 256),
+]
+
+
+@pytest.mark.parametrize("cr,page_size", GEOMETRIES)
+def test_geometries(oracle_mod, cr, page_size):
+    """Other compress ratios and page sizes through every arm and both
+    scorers: integer inputs, so scores and selections are bit-exact with the
+    oracle; three requests of different lengths on a permuted page pool, k a
+    multiple of cr, one request with fewer visible keys than k / cr."""
+    rng = np.random.default_rng(60 + cr)
+    k = 64 * cr
+    w = W.build(f"geom_{cr}_{page_size}", rng, 60 + cr, [7000, 9 * cr, 3001], [40, 5, 37], permute_pages=True,
+                integer=True, k=k, compress_ratio=cr, page_size=page_size, extra_pages=2)
+    full_parity(oracle_mod, w, 0, True, paths=PATHS)
+    full_parity(oracle_mod, w, KEYS, True, paths=("two_pass",))
+    with force_scorer("groups"):
+        full_parity(oracle_mod, w, 0, True, paths=("two_pass",))
+
+
 def test_out_keys_reduced(oracle_mod):
     w = W.kernel_shape(rows=40, ctx=30_000)
     d = to_dev(w)

@@ -99,6 +99,13 @@ KERNEL_SOURCES = {
     "scorer": (("score_",),
                ["paged_block_scoring_amd/csrc/score_rows.hpp", "paged_block_scoring_amd/csrc/score_group.hip",
                 "paged_block_scoring_amd/csrc/score.hip", "paged_block_scoring_amd/csrc/qsa_device.hpp"]),
+    # the relu form's tiled scorer (score_core.hpp)
+    "filter_scorer_relu": (("score_tiles_kernel", "(qsa::Epi)1"),
+                           ["paged_block_scoring_amd/csrc/score_core.hpp", "paged_block_scoring_amd/csrc/score_rows.hpp",
+                            "paged_block_scoring_amd/csrc/score.hip", "paged_block_scoring_amd/csrc/qsa_device.hpp"]),
+    "sample_scorer_relu": (("score_tiles_kernel", "(qsa::Epi)0"),
+                           ["paged_block_scoring_amd/csrc/score_core.hpp", "paged_block_scoring_amd/csrc/score_rows.hpp",
+                            "paged_block_scoring_amd/csrc/score.hip", "paged_block_scoring_amd/csrc/qsa_device.hpp"]),
     "sample_threshold": (("sample_threshold_kernel",),
                          ["paged_block_scoring_amd/csrc/fused.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
     "final_select": (("fused_select_kernel",),
@@ -220,7 +227,8 @@ def summarize_profile(args):
     """
     import glob
     out = {}
-    name = args.workload + ("_consumer" if args.consumer else "") + ("_producer" if args.producer else "")
+    name = (args.workload + ("_consumer" if args.consumer else "") + ("_producer" if args.producer else "")
+            + ("_relu" if args.relu else ""))
     if args.stats_dir:
         stats = _read_csv(glob.glob(os.path.join(args.stats_dir, "*_kernel_stats.csv"))[0])
         lines = [f"# Kernel time, {name} (rocprofv3 --kernel-trace --stats)", "",
@@ -494,12 +502,13 @@ class Run:
         scale = 1e12 if unit == "TFLOP/s" else 1e9
         achieved = work / (kms[dom] * 1e-3) / scale
         relu = bool(self.flags & Q.QSA_SCORE_RELU)
+        # the relu form's scorers are other kernels with their own profiles
+        pname = dom + "_relu" if relu and dom in ("filter_scorer", "sample_scorer") else dom
         roof = {"kernel": dom, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4),
-                # the counter profiles are of the default form's kernels
-                "traffic": None if relu else traffic_for(dom, self.name),
+                "traffic": traffic_for(pname, self.name + ("_relu" if relu else "")),
                 "ms_per_launch": round(kms[dom], 4)}
-        cnt = None if relu else counters_for(dom, self.name)
+        cnt = counters_for(pname, self.name + ("_relu" if relu else ""))
         if bound == "mfma":
             roof["algorithmic_flop_per_launch"] = work
             if cnt and cnt.get("executed_flop"):

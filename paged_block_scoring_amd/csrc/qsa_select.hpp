@@ -376,14 +376,24 @@ __device__ __forceinline__ void select_from_bound(const uint32_t (&k)[EPT], IdxF
     for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
     if (lane == 0) hs.wmax[wave] = mx;
     for (int i = tid; i < kSelBins; i += NT) hs.hist[i] = 0u;
+    if (tid == 0) {  // (kept only if fewer than nsel keys were given: then nothing is emitted)
+        hs.bin = kSelBins - 1;
+        hs.above = 0;
+        hs.cnt = 0;
+    }
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) mx = max(mx, hs.wmax[w]);
     const uint32_t mn = min(lo, mx);
     const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
+    // a key's bin; an empty slot, and (outside the contract) a key below the
+    // bound, land in the guard bin kSelBins
+    auto bin_of = [&](uint32_t key) {
+        return key >= mn ? min((key - mn) >> shift1, (uint32_t)kSelBins) : (uint32_t)kSelBins;
+    };
 #pragma unroll
-    for (int e = 0; e < EPT; ++e)  // (an empty slot lands in the guard bin)
-        if (e * NT < nmax) atomicAdd(&hs.hist[k[e] ? (k[e] - mn) >> shift1 : (uint32_t)kSelBins], 1u);
+    for (int e = 0; e < EPT; ++e)
+        if (e * NT < nmax) atomicAdd(&hs.hist[k[e] ? bin_of(k[e]) : (uint32_t)kSelBins], 1u);
     __syncthreads();
     // thread t owns bins kSelBins-1-BPT*t .. (high to low)
     uint32_t cb[BPT];
@@ -417,14 +427,14 @@ __device__ __forceinline__ void select_from_bound(const uint32_t (&k)[EPT], IdxF
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             if (e * NT < nmax && k[e]) {
-                const uint32_t bn = (k[e] - mn) >> shift1;
-                if ((int)bn >= b) L.a[L.start[bn] + atomicAdd(&hs.hist[bn], 1u)] = compose(k[e], idx(e));
+                const uint32_t bn = bin_of(k[e]);
+                if (bn < (uint32_t)kSelBins && (int)bn >= b) L.a[L.start[bn] + atomicAdd(&hs.hist[bn], 1u)] = compose(k[e], idx(e));
             }
         }
         __syncthreads();
         for (int p = tid; p < above + cnt; p += NT) {
             const uint64_t me = L.a[p];
-            const uint32_t bn = ((uint32_t)(me >> 32) - mn) >> shift1;
+            const uint32_t bn = min(bin_of((uint32_t)(me >> 32)), (uint32_t)kSelBins - 1u);
             const int st = (int)L.start[bn], cn = (int)hs.hist[bn];
             if (cn > kMaxBucket) {
                 hs.flag = 1;  // a crowded bin above b: the sort below takes over
@@ -432,7 +442,8 @@ __device__ __forceinline__ void select_from_bound(const uint32_t (&k)[EPT], IdxF
             }
             int r = 0;
             for (int i = st; i < st + cn; ++i) r += L.a[i] > me ? 1 : 0;
-            if (st + r < nsel) emit(st + r, me);
+            // (unsigned: a rank is never negative, whatever the list held)
+            if ((unsigned)(st + r) < (unsigned)nsel) emit(st + r, me);
         }
         __syncthreads();
         slow = hs.flag != 0;

@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kThrNT) void sample_threshold_kernel(const float* _
     }
     if (threadIdx.x == 0) {
         thresh[row] = T;
-        cand_count[row] = 0;
+        cand_count[(int64_t)row * kCountStride] = 0;
     }
 }
 
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kFinNT) void fused_select_kernel(FinalArgs A) {
     uint64_t en[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) en[e] = c[min(e * kFinNT + tid, A.cand_cap - 1)];  // (score bits, key)
-    const int n = A.cand_count[row];
+    const int n = A.cand_count[(int64_t)row * kCountStride];
     const uint32_t tkey = (uint32_t)(A.thresh[row] >> 32);
     const int V = row_visible_count(A.vis, row);
     const int nsel = min(kb, V);

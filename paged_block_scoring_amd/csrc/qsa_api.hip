@@ -185,7 +185,7 @@ FusedLayout fused_layout(int32_t rows, int32_t max_visible, int32_t kb) {
     L.off_thresh = o;
     o = align256(o + (size_t)rows * sizeof(uint64_t));
     L.off_count = o;
-    o = align256(o + (size_t)rows * sizeof(int32_t));
+    o = align256(o + (size_t)rows * (size_t)qsa::kCountStride * sizeof(int32_t));
     L.off_cand = o;
     o = align256(o + (size_t)rows * (size_t)L.plan.cand_cap * sizeof(uint64_t));
     L.total = o;

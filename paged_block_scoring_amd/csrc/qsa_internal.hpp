@@ -37,6 +37,11 @@ const int32_t* qsum_tile_visible(const _Float16* qsum, int32_t rows);
 const float* qsum_row_factor(const _Float16* qsum, int32_t rows);
 hipError_t launch_qsum_prep(const PagedArgs& a, _Float16* qsum, hipStream_t stream);
 
+// Candidate counters of the fused arm: row r's count is cand_count[r *
+// kCountStride], one counter per 128-byte line, so that the atomics of
+// different rows do not queue on one line.
+constexpr int32_t kCountStride = 32;
+
 // Which materialising scorer runs: chosen from the rows per request, or forced.
 enum class ScorerChoice { Auto, Tiles, Groups };
 

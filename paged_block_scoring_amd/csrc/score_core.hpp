@@ -70,7 +70,7 @@ struct ScoreKernelArgs {
     // Filter
     const uint64_t* thresh;  // [rows] threshold composite; only its score is used
     uint64_t* cand;          // [rows][cand_cap] entries (score bits << 32 | key)
-    int32_t* cand_count;     // [rows]
+    int32_t* cand_count;     // [rows * kCountStride]
     int32_t cand_cap;
 };
 
@@ -118,7 +118,7 @@ __device__ __forceinline__ int quad_exclusive_sum(int x, int* total) {
 __device__ __forceinline__ void flush_staged(const ScoreKernelArgs& A, const uint64_t* lb, int row, int& cnt,
                                              int leader, int member, int gsize) {
     int base = 0;
-    if (member == 0 && cnt > 0) base = atomicAdd(&A.cand_count[row], cnt);
+    if (member == 0 && cnt > 0) base = atomicAdd(&A.cand_count[(int64_t)row * kCountStride], cnt);
     base = __shfl(base, leader, 64);
     uint64_t* dst = A.cand + (int64_t)row * A.cand_cap;
     for (int i = member; i < cnt; i += gsize)

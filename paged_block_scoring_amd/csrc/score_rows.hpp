@@ -81,7 +81,7 @@ struct RowsArgs {
     // Filter
     const uint64_t* thresh;  // [rows] threshold composite; only its score is used
     uint64_t* cand;          // [rows][cand_cap] entries (score bits << 32 | key)
-    int32_t* cand_count;     // [rows]
+    int32_t* cand_count;     // [rows * kCountStride]
     int32_t cand_cap;
 };
 
@@ -327,11 +327,15 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
         (uint32_t)reinterpret_cast<uintptr_t>(static_cast<void*>(&s_list[0])) + (uint32_t)(tid * kLaneCap * 8);
     int tile_r0 = -1;  // first row of the tile held in registers
 
-    // moves every lane's list to its row's global candidate list (one atomic
-    // per lane; the list is read from LDS 16 bytes at a time)
+    // moves every lane's list to its row's global candidate list: lanes l and
+    // l+32 hold the same row, lane l reserves room for both with one atomic
+    // and lane l+32's entries follow lane l's (the list is read from LDS 16
+    // bytes at a time).  Called by whole waves.
     auto flush = [&](int row) {
+        const int other = __shfl_xor(cnt, 32, 64);
         int base = 0;
-        if (cnt > 0) base = atomicAdd(&A.cand_count[row], cnt);
+        if (lane < 32 && cnt + other > 0) base = atomicAdd(&A.cand_count[(int64_t)row * kCountStride], cnt + other);
+        base = __shfl(base, lane & 31, 64) + (lane >= 32 ? other : 0);
         const int lim = min(cnt, A.cand_cap - base);
         uint64_t* dst = A.cand + (int64_t)row * A.cand_cap + base;
         const u32x4* src = reinterpret_cast<const u32x4*>(&s_list[tid * kLaneCap]);

@@ -18,7 +18,10 @@
 // XCD streams only its stripe of keys (which stays in its L2) and every
 // workgroup does the same amount of work.  A share is processed as pieces of
 // one tile and at most kRowsPiece keys; rows of different requests in one
-// tile are processed in successive passes over the piece.
+// tile are processed in successive passes over the piece (with a single
+// request there is one pass, set up before the piece's first barrier: the
+// page ids are loaded first and the slot table written as soon as they are
+// in, while the row and query loads are still on their way).
 //
 // A piece.  Each wave holds the head-sum query fragments (hi and lo halves,
 // qsa_device.hpp) of its 32 rows in registers: read from the prepared head
@@ -218,6 +221,7 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
     __shared__ int32_t s_req[TILE], s_lv[TILE], s_todo[TILE], s_lim[TILE];
     __shared__ float s_fT[FILTER ? TILE : 1];
     __shared__ int32_t s_act, s_vmax;
+    __shared__ int32_t s_wv[TILE / 64];  // one request: per wave of row threads, the longest active row
 
     const PagedArgs& a = A.a;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -399,8 +403,28 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
         const bool new_tile = r0 != tile_r0;
         if (FILTER && new_tile && tile_r0 >= 0) flush(tile_r0 + erow);
 
-        // the tile's rows (threads < 128): loads first, so that the query and
-        // page-table loads below overlap them
+        // (the stripe end c1 is padded to whole stages and may lie up to 31
+        // keys past the last visible key; the table stops at that key, so no
+        // page-table entry beyond the request's visible pages is read)
+        // (one request: the page ids first, in two halves -- loads now, the
+        // table once they, and only they, are in)
+        constexpr int U = kRowsPiece / NT;
+        const int sn = one_req ? min(c1, A.lmax) - c0 : 0;
+        int32_t pg1[U];
+        int sl1[U];
+        if (sn > 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (u * NT >= sn) break;
+                const int j = (c0 + min(tid + u * NT, sn - 1)) * A.stride;
+                const int lp = A.kpp_shift >= 0 ? (j >> A.kpp_shift) : j / a.kpp;
+                sl1[u] = j - lp * a.kpp;
+                pg1[u] = a.page_table[lp];
+            }
+        }
+        // the tile's rows (threads < 128), then the queries: the slot table
+        // below waits only for the page ids, the rows' bounds only for the
+        // rows, and the queries are first needed by the first MFMA
         int req = -1, ps = 0;
         uint64_t th = 0ull;
         const int rr = r0 + tid;
@@ -436,10 +460,12 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
                 head_sum_split(load(s, 0), load(s, 1), load(s, 2), load(s, 3), 1.0f / fac, qa[2 * s], qa[2 * s + 1]);
             if (!A.true_scores) fac = 1.0f;
         }
-        // (the stripe end c1 is padded to whole stages and may lie up to 31
-        // keys past the last visible key; the table stops at that key, so no
-        // page-table entry beyond the request's visible pages is read)
-        if (one_req) build_slots(0, c0, min(c1, A.lmax));
+        if (sn > 0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (tid + u * NT < sn)
+                    s_slot[tid + u * NT] = (uint32_t)min(max(pg1[u], 0), a.num_pages - 1) * (uint32_t)a.kpp + (uint32_t)sl1[u];
+        }
         if (tid < TILE) {
             int lv = 0;
             if (rr >= a.rows || req < 0 || req >= a.num_reqs) {
@@ -454,40 +480,61 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
             // the threshold composite's score (an all-ones composite decodes
             // to NaN, which no score reaches)
             if (FILTER && new_tile) s_fT[tid] = req >= 0 ? key_to_float((uint32_t)(th >> 32)) : 0.0f;
+            if (one_req) {
+                // a single pass over every active row: its bounds now, and the
+                // longest active row per wave (TILE row threads = whole waves)
+                const bool on = req >= 0 && lv > c0;
+                s_lim[tid] = on ? min(lv, c1) : 0;
+                int wv = on ? lv : 0;
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) wv = max(wv, __shfl_xor(wv, o, 64));
+                if (lane == 0) s_wv[wave] = wv;
+            }
         }
         __syncthreads();
         if (FILTER && new_tile) fT = s_fT[erow];
         tile_r0 = r0;
 
+        bool one_done = false;
         for (;;) {
-            // one pass per request present among the tile's pending rows
-            // (smallest request id first): wave 0 elects it and marks the rows
-            if (wave == 0) {
-                int best = 0x7FFFFFFF;
-                for (int t = lane; t < TILE; t += 64)
-                    if (s_todo[t]) best = min(best, s_req[t]);
+            int act = 0, vm = 0;
+            if (one_req) {
+                if (one_done) break;
+                one_done = true;
 #pragma unroll
-                for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o, 64));
-                int vmax = 0;
-                for (int t = lane; t < TILE; t += 64) {
-                    const bool on = s_todo[t] && s_req[t] == best;
-                    s_lim[t] = on ? min(s_lv[t], c1) : 0;
-                    if (on) {
-                        s_todo[t] = 0;
-                        vmax = max(vmax, s_lv[t]);
+                for (int w = 0; w < TILE / 64; ++w) vm = max(vm, s_wv[w]);
+                if (vm <= c0) break;
+            } else {
+                // one pass per request present among the tile's pending rows
+                // (smallest request id first): wave 0 elects it and marks the rows
+                if (wave == 0) {
+                    int best = 0x7FFFFFFF;
+                    for (int t = lane; t < TILE; t += 64)
+                        if (s_todo[t]) best = min(best, s_req[t]);
+#pragma unroll
+                    for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o, 64));
+                    int vmax = 0;
+                    for (int t = lane; t < TILE; t += 64) {
+                        const bool on = s_todo[t] && s_req[t] == best;
+                        s_lim[t] = on ? min(s_lv[t], c1) : 0;
+                        if (on) {
+                            s_todo[t] = 0;
+                            vmax = max(vmax, s_lv[t]);
+                        }
+                    }
+#pragma unroll
+                    for (int o = 32; o > 0; o >>= 1) vmax = max(vmax, __shfl_xor(vmax, o, 64));
+                    if (lane == 0) {
+                        s_act = best == 0x7FFFFFFF ? -1 : best;
+                        s_vmax = vmax;
                     }
                 }
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) vmax = max(vmax, __shfl_xor(vmax, o, 64));
-                if (lane == 0) {
-                    s_act = best == 0x7FFFFFFF ? -1 : best;
-                    s_vmax = vmax;
-                }
+                __syncthreads();
+                act = s_act;
+                if (act < 0) break;
+                vm = s_vmax;
             }
-            __syncthreads();
-            const int act = s_act;
-            if (act < 0) break;
-            const int cend = min(c1, s_vmax);
+            const int cend = min(c1, vm);
 
             if (!one_req) build_slots(act, c0, cend);
             // this lane's row bound, and the smallest over the wave's rows:
@@ -497,7 +544,8 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) wlim = min(wlim, __shfl_xor(wlim, o, 64));
             wlim = __builtin_amdgcn_readfirstlane(wlim);
-            __syncthreads();
+            // (with one request the slot table and bounds were in place at the first barrier)
+            if (!one_req) __syncthreads();
 
             const _Float16* kc = a.kcache;
             auto slots_of = [&](int stage) {

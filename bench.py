@@ -110,6 +110,9 @@ KERNEL_SOURCES = {
                          ["paged_block_scoring_amd/csrc/fused.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
     "final_select": (("fused_select_kernel",),
                      ["paged_block_scoring_amd/csrc/fused.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
+    # the two-pass arm's register top-k (rows up to 49,152 keys: the decode batch)
+    "topk_regs": (("topk_regs_kernel",),
+                  ["paged_block_scoring_amd/csrc/topk.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
     "topk_rows": (("topk_rows_kernel",), ["paged_block_scoring_amd/csrc/topk.hip"]),
     "attend": (("attend_kernel",), ["paged_block_scoring_amd/csrc/attend.hip"]),
     "compress_blocks": (("compress_blocks_kernel",), ["paged_block_scoring_amd/csrc/compress.hip"]),

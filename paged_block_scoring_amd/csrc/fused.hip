@@ -27,6 +27,7 @@
 //     scores itself with the same MFMA sequence and keeps an exact running
 //     top-kb in LDS.  Either way the result is exact; the sample only decides
 //     how fast.
+#include <algorithm>
 #include <cmath>
 
 #include "qsa.h"
@@ -58,7 +59,9 @@ __global__ __launch_bounds__(kThrNT) void sample_threshold_kernel(const float* _
                                                                   VisibleSource vis, int32_t stride, int32_t m,
                                                                   int32_t force_fallback,
                                                                   uint64_t* __restrict__ thresh,
-                                                                  int32_t* __restrict__ cand_count) {
+                                                                  int32_t* __restrict__ cand_count,
+                                                                  int32_t* __restrict__ redo_count) {
+    if (blockIdx.x == 0 && threadIdx.x == 0 && redo_count) *redo_count = 0;  // (for the split select)
     constexpr int EPT = kMaxSamples / kThrNT;
     __shared__ HistScratch hs;
     __shared__ float s_f[2 * (kThrNT / 64)];
@@ -154,9 +157,12 @@ struct FinalArgs {
     int32_t expand;
     int32_t out_len;
     int32_t* out;
+    int32_t* redo_count;  // split select: rows the candidate pass left to the full pass (count, then rows)
+    int32_t* redo_rows;
 };
 
 constexpr int kFinNT = 256;
+constexpr int kRedoGrid = 256;  // workgroups of the split select's second pass
 constexpr int kFinWaves = kFinNT / 64;
 
 // Exact top-kb of one row by recomputation: each wave scores 32 keys at a
@@ -280,9 +286,9 @@ union SelectLds {
     } r;
 };
 
-// One row per workgroup.  The row's visible count, candidate count,
-// threshold and first 2,048 candidate slots are loaded at once (slots past
-// the count are clamped into the list and masked).
+// The select of one row, by a whole workgroup.  The row's visible count,
+// candidate count, threshold and first 2,048 candidate slots are loaded at
+// once (slots past the count are clamped into the list and masked).
 // Candidate path: the candidates are held in registers as (order key,
 // index) and binned by order key between the threshold's key (no candidate
 // is below it) and their largest (kSelBins ordered bins); with start[bin] =
@@ -298,12 +304,19 @@ union SelectLds {
 // high; too long: it was too low or its score has many ties; or the
 // sampling pass left the row out) take the recompute path: exact top-kb by
 // recomputation (recompute_row_topk), then a sort in LDS.
-template <int KBMAX, int CAPC>
-__global__ __launch_bounds__(kFinNT) void fused_select_kernel(FinalArgs A) {
+// LEAN: the candidate path only, for lists of at most CAPC entries; any
+// other row is appended to the redo list for the full version (which then
+// writes the whole row), so that the common case runs without the recompute
+// path's registers.
+template <int KBMAX>
+__device__ __forceinline__ BoundSelectLds<KBMAX>& bound_lds(SelectLds<KBMAX>& L) { return L.f; }
+template <int KBMAX>
+__device__ __forceinline__ BoundSelectLds<KBMAX>& bound_lds(BoundSelectLds<KBMAX>& L) { return L; }
+
+template <int KBMAX, int CAPC, bool LEAN, class LdsT>
+__device__ __forceinline__ void select_row(const FinalArgs& A, const int row, LdsT& L) {
     constexpr int EPT = CAPC / kFinNT;
     static_assert(EPT % 4 == 0 && EPT >= 8, "slot groups of 4, two issued up front");
-    __shared__ SelectLds<KBMAX> L;
-    const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const int kb = A.kb;
     int32_t* orow = A.out + (int64_t)row * A.out_len;
@@ -311,24 +324,36 @@ __global__ __launch_bounds__(kFinNT) void fused_select_kernel(FinalArgs A) {
 
     // everything the row needs first, in one round of loads
     const uint64_t* c = A.cand + (int64_t)row * A.cand_cap;
+    // (the candidate pass loads 1,280 slots with the count, which covers
+    // about 85% of the rows at kb = 512, and the rest only where it is needed)
+    constexpr int U0 = LEAN ? 5 : 8;
     uint64_t en[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) en[e] = c[min(e * kFinNT + tid, A.cand_cap - 1)];  // (score bits, key)
+    for (int e = 0; e < U0; ++e) en[e] = c[min(e * kFinNT + tid, A.cand_cap - 1)];  // (score bits, key)
     const int n = A.cand_count[(int64_t)row * kCountStride];
     const uint32_t tkey = (uint32_t)(A.thresh[row] >> 32);
     const int V = row_visible_count(A.vis, row);
     const int nsel = min(kb, V);
 
-    if (n < nsel || n > A.cand_cap) {
-        const int have = recompute_row_topk<KBMAX + kRecChunk>(A, row, V, L.r.a, &L.r.ks, &L.r.pend, L.r.rs);
-        lds_sort_desc<kFinNT>(L.r.a, have);
-        for (int i = tid; i < A.out_len; i += kFinNT) {
-            const int rank = i / A.expand, t = i - rank * A.expand;
-            int v = -1;
-            if (rank < nsel) v = (int)composite_index(L.r.a[rank]) * A.expand + t;
-            orow[i] = v;
+    if constexpr (LEAN) {
+        if (n < nsel || n > A.cand_cap || n > CAPC) {
+            if (tid == 0) A.redo_rows[atomicAdd(A.redo_count, 1)] = row;
+            return;
         }
-        return;
+#pragma unroll
+        for (int e = U0; e < 8; ++e) en[e] = e * kFinNT < n ? c[min(e * kFinNT + tid, A.cand_cap - 1)] : 0ull;
+    } else {
+        if (n < nsel || n > A.cand_cap) {
+            const int have = recompute_row_topk<KBMAX + kRecChunk>(A, row, V, L.r.a, &L.r.ks, &L.r.pend, L.r.rs);
+            lds_sort_desc<kFinNT>(L.r.a, have);
+            for (int i = tid; i < A.out_len; i += kFinNT) {
+                const int rank = i / A.expand, t = i - rank * A.expand;
+                int v = -1;
+                if (rank < nsel) v = (int)composite_index(L.r.a[rank]) * A.expand + t;
+                orow[i] = v;
+            }
+            return;
+        }
     }
     if (nsel > 0) {
         uint32_t k[EPT], idx[EPT];
@@ -361,10 +386,36 @@ __global__ __launch_bounds__(kFinNT) void fused_select_kernel(FinalArgs A) {
         }
         // every candidate's key is >= the threshold's
         select_from_bound<kFinNT, EPT, KBMAX>(
-            k, [&](int e) { return idx[e]; }, n, nsel, tkey, L.f,
+            k, [&](int e) { return idx[e]; }, n, nsel, tkey, bound_lds(L),
             [&](int r, uint64_t c) { write_rank(orow, r, composite_index(c), A.expand, vec4); });
     }
     for (int i = nsel * A.expand + tid; i < A.out_len; i += kFinNT) orow[i] = -1;
+}
+
+// One row per workgroup (both paths).
+template <int KBMAX, int CAPC>
+__global__ __launch_bounds__(kFinNT) void fused_select_kernel(FinalArgs A) {
+    __shared__ SelectLds<KBMAX> L;
+    select_row<KBMAX, CAPC, false>(A, blockIdx.x, L);
+}
+
+// Split select, first pass: one row per workgroup, candidate path only.
+template <int KBMAX, int CAPC>
+__global__ __launch_bounds__(kFinNT) void fused_select_lean_kernel(FinalArgs A) {
+    __shared__ BoundSelectLds<KBMAX> L;
+    select_row<KBMAX, CAPC, true>(A, blockIdx.x, L);
+}
+
+// Split select, second pass: the rows the first pass left, spread over the
+// grid (every workgroup reads the same count, so the loop is uniform).
+template <int KBMAX, int CAPC>
+__global__ __launch_bounds__(kFinNT) void fused_select_redo_kernel(FinalArgs A) {
+    __shared__ SelectLds<KBMAX> L;
+    const int cnt = min(*A.redo_count, A.a.rows);
+    for (int i = blockIdx.x; i < cnt; i += gridDim.x) {
+        select_row<KBMAX, CAPC, false>(A, A.redo_rows[i], L);
+        __syncthreads();  // before the next row reuses the LDS
+    }
 }
 
 }  // namespace
@@ -384,17 +435,17 @@ FusedPlan plan_fused(int32_t max_visible, int32_t kb) {
 }
 
 hipError_t launch_sample_threshold(const float* samp, int64_t ld_s, const VisibleSource& vis, const FusedPlan& f,
-                                   bool force_fallback, uint64_t* thresh, int32_t* cand_count, int32_t rows,
-                                   hipStream_t stream) {
+                                   bool force_fallback, uint64_t* thresh, int32_t* cand_count, int32_t* redo,
+                                   int32_t rows, hipStream_t stream) {
     if (rows <= 0) return hipSuccess;
     sample_threshold_kernel<<<dim3((unsigned)rows), kThrNT, 0, stream>>>(
-        samp, ld_s, vis, f.stride, f.m, force_fallback ? 1 : 0, thresh, cand_count);
+        samp, ld_s, vis, f.stride, f.m, force_fallback ? 1 : 0, thresh, cand_count, redo);
     return hipGetLastError();
 }
 
 hipError_t launch_fused_final(const PagedArgs& a, const VisibleSource& vis, const FusedPlan& f, const uint64_t* thresh,
-                              const uint64_t* cand, const int32_t* cand_count, int32_t kb, int32_t expand,
-                              int32_t out_len, int32_t* out, hipStream_t stream) {
+                              const uint64_t* cand, const int32_t* cand_count, int32_t* redo, int32_t kb,
+                              int32_t expand, int32_t out_len, int32_t* out, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     FinalArgs A;
     A.a = a;
@@ -407,11 +458,19 @@ hipError_t launch_fused_final(const PagedArgs& a, const VisibleSource& vis, cons
     A.expand = expand;
     A.out_len = out_len;
     A.out = out;
+    A.redo_count = redo;
+    A.redo_rows = redo + kRedoHead;
     const dim3 grid((unsigned)a.rows);
-    if (f.capl == 4096)
-        fused_select_kernel<1024, 4096><<<grid, kFinNT, 0, stream>>>(A);
-    else
+    if (f.capl == 4096) {
+        // split: the candidate path for lists of up to 2,048 entries (the
+        // common case: about 16m, 1,100 at kb = 512), then every other row
+        fused_select_lean_kernel<1024, 2048><<<grid, kFinNT, 0, stream>>>(A);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        fused_select_redo_kernel<1024, 4096><<<dim3((unsigned)std::min(a.rows, kRedoGrid)), kFinNT, 0, stream>>>(A);
+    } else {
         fused_select_kernel<QSA_MAX_SELECT, 8192><<<grid, kFinNT, 0, stream>>>(A);
+    }
     return hipGetLastError();
 }
 

@@ -171,7 +171,7 @@ size_t two_pass_bytes(int32_t rows, int32_t max_visible) {
 // Fused arm: sample scores, per-row threshold and candidate count, candidate lists.
 struct FusedLayout {
     qsa::FusedPlan plan;
-    size_t off_qsum, off_samp, off_thresh, off_count, off_cand, total;
+    size_t off_qsum, off_samp, off_thresh, off_count, off_redo, off_cand, total;
 };
 
 FusedLayout fused_layout(int32_t rows, int32_t max_visible, int32_t kb) {
@@ -186,6 +186,8 @@ FusedLayout fused_layout(int32_t rows, int32_t max_visible, int32_t kb) {
     o = align256(o + (size_t)rows * sizeof(uint64_t));
     L.off_count = o;
     o = align256(o + (size_t)rows * (size_t)qsa::kCountStride * sizeof(int32_t));
+    L.off_redo = o;
+    o = align256(o + qsa::redo_bytes(rows));
     L.off_cand = o;
     o = align256(o + (size_t)rows * (size_t)L.plan.cand_cap * sizeof(uint64_t));
     L.total = o;
@@ -478,6 +480,7 @@ qsa_status run_select(const SelectCall& c, void* workspace, const DeviceInfo* de
         float* samp = reinterpret_cast<float*>(w + L.off_samp);
         uint64_t* thresh = reinterpret_cast<uint64_t*>(w + L.off_thresh);
         int32_t* count = reinterpret_cast<int32_t*>(w + L.off_count);
+        int32_t* redo = reinterpret_cast<int32_t*>(w + L.off_redo);
         uint64_t* cand = reinterpret_cast<uint64_t*>(w + L.off_cand);
         _Float16* qsum = a.relu ? nullptr : reinterpret_cast<_Float16*>(w + L.off_qsum);
         const int cus = dev->cus;
@@ -486,12 +489,12 @@ qsa_status run_select(const SelectCall& c, void* workspace, const DeviceInfo* de
         HIP_CHECK(mark(s));
         HIP_CHECK(qsa::launch_score_store(a, qsum, L.plan.stride, false, samp, L.plan.ld_s, cus, s));
         HIP_CHECK(mark(s));
-        HIP_CHECK(qsa::launch_sample_threshold(samp, L.plan.ld_s, vs, L.plan, force_fallback(), thresh, count,
+        HIP_CHECK(qsa::launch_sample_threshold(samp, L.plan.ld_s, vs, L.plan, force_fallback(), thresh, count, redo,
                                                c.rows, s));
         HIP_CHECK(mark(s));
         HIP_CHECK(qsa::launch_score_filter(a, qsum, thresh, cand, count, L.plan.cand_cap, cus, s));
         HIP_CHECK(mark(s));
-        HIP_CHECK(qsa::launch_fused_final(a, vs, L.plan, thresh, cand, count, kb, expand, c.k, c.out, s));
+        HIP_CHECK(qsa::launch_fused_final(a, vs, L.plan, thresh, cand, count, redo, kb, expand, c.k, c.out, s));
         HIP_CHECK(mark(s));
         g_events = nullptr;
         g_path = "fused";

@@ -96,12 +96,19 @@ struct FusedPlan {
 };
 FusedPlan plan_fused(int32_t max_visible, int32_t kb);
 
+// The fused arm's redo list (rows the final select's candidate pass leaves
+// to its full pass): kRedoHead int32 (the count, alone on a 256-byte
+// stretch), then one int32 per row.  The threshold kernel clears the count.
+constexpr int32_t kRedoHead = 64;
+inline size_t redo_bytes(int32_t rows) { return (size_t)(kRedoHead + rows) * sizeof(int32_t); }
+
 hipError_t launch_sample_threshold(const float* samp, int64_t ld_s, const VisibleSource& vis, const FusedPlan& f,
-                                   bool force_fallback, uint64_t* thresh, int32_t* cand_count, int32_t rows,
+                                   bool force_fallback, uint64_t* thresh, int32_t* cand_count, int32_t* redo,
+                                   int32_t rows,
                                    hipStream_t stream);
 
 hipError_t launch_fused_final(const PagedArgs& a, const VisibleSource& vis, const FusedPlan& f, const uint64_t* thresh,
-                              const uint64_t* cand, const int32_t* cand_count, int32_t kb, int32_t expand,
+                              const uint64_t* cand, const int32_t* cand_count, int32_t* redo, int32_t kb, int32_t expand,
                               int32_t out_len, int32_t* out, hipStream_t stream);
 
 // Sparse attention over selected tokens (attend.hip): head_dim 256, at most

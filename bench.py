@@ -108,8 +108,12 @@ KERNEL_SOURCES = {
                             "paged_block_scoring_amd/csrc/score.hip", "paged_block_scoring_amd/csrc/qsa_device.hpp"]),
     "sample_threshold": (("sample_threshold_kernel",),
                          ["paged_block_scoring_amd/csrc/fused.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
-    "final_select": (("fused_select_kernel",),
+    # the fused arm's final select: the candidate pass (every row), then the
+    # pass over the rows it leaves (usually none)
+    "final_select": (("fused_select_lean_kernel",),
                      ["paged_block_scoring_amd/csrc/fused.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
+    "final_select_redo": (("fused_select_redo_kernel",),
+                          ["paged_block_scoring_amd/csrc/fused.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
     # the two-pass arm's register top-k (rows up to 49,152 keys: the decode batch)
     "topk_regs": (("topk_regs_kernel",),
                   ["paged_block_scoring_amd/csrc/topk.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),

@@ -340,6 +340,7 @@ int32_t qsa_debug_events_recorded(void);
 #define QSA_DEBUG_FORCE_FALLBACK 0x4u   /* the fused arm, every row on its exact recompute path */
 #define QSA_DEBUG_FORCE_TILES    0x8u   /* materialising scorer: the row-tiled kernel */
 #define QSA_DEBUG_FORCE_GROUPS   0x10u  /* materialising scorer: the windowed kernel */
+#define QSA_DEBUG_FORCE_REDO     0x20u  /* the fused arm, every row's final select in its second pass */
 qsa_status qsa_debug_force(uint32_t mask);
 uint32_t qsa_debug_forced(void);
 

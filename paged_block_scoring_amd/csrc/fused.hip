@@ -159,6 +159,7 @@ struct FinalArgs {
     int32_t* out;
     int32_t* redo_count;  // split select: rows the candidate pass left to the full pass (count, then rows)
     int32_t* redo_rows;
+    int32_t force_redo;   // the candidate pass leaves every row to the full pass (debug override)
 };
 
 constexpr int kFinNT = 256;
@@ -336,7 +337,7 @@ __device__ __forceinline__ void select_row(const FinalArgs& A, const int row, Ld
     const int nsel = min(kb, V);
 
     if constexpr (LEAN) {
-        if (n < nsel || n > A.cand_cap || n > CAPC) {
+        if (n < nsel || n > A.cand_cap || n > CAPC || A.force_redo) {
             if (tid == 0) A.redo_rows[atomicAdd(A.redo_count, 1)] = row;
             return;
         }
@@ -444,8 +445,8 @@ hipError_t launch_sample_threshold(const float* samp, int64_t ld_s, const Visibl
 }
 
 hipError_t launch_fused_final(const PagedArgs& a, const VisibleSource& vis, const FusedPlan& f, const uint64_t* thresh,
-                              const uint64_t* cand, const int32_t* cand_count, int32_t* redo, int32_t kb,
-                              int32_t expand, int32_t out_len, int32_t* out, hipStream_t stream) {
+                              const uint64_t* cand, const int32_t* cand_count, int32_t* redo, bool force_redo,
+                              int32_t kb, int32_t expand, int32_t out_len, int32_t* out, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
     FinalArgs A;
     A.a = a;
@@ -460,6 +461,7 @@ hipError_t launch_fused_final(const PagedArgs& a, const VisibleSource& vis, cons
     A.out = out;
     A.redo_count = redo;
     A.redo_rows = redo + kRedoHead;
+    A.force_redo = force_redo ? 1 : 0;
     const dim3 grid((unsigned)a.rows);
     if (f.capl == 4096) {
         // split: the candidate path for lists of up to 2,048 entries (the

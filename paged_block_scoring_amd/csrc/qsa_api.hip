@@ -206,13 +206,14 @@ constexpr int64_t kFusedMinWork = 5000000;
 Path choose_path(int32_t rows, int32_t num_reqs, int32_t max_visible) {
     const uint32_t f = g_force.load(std::memory_order_relaxed);
     if (f & QSA_DEBUG_FORCE_TWO_PASS) return Path::TwoPass;
-    if (f & (QSA_DEBUG_FORCE_FUSED | QSA_DEBUG_FORCE_FALLBACK)) return Path::Fused;
+    if (f & (QSA_DEBUG_FORCE_FUSED | QSA_DEBUG_FORCE_FALLBACK | QSA_DEBUG_FORCE_REDO)) return Path::Fused;
     if (max_visible <= 0) return Path::TwoPass;
     if (rows / (num_reqs > 0 ? num_reqs : 1) < 32) return Path::TwoPass;
     return (int64_t)rows * max_visible >= kFusedMinWork ? Path::Fused : Path::TwoPass;
 }
 
 bool force_fallback() { return (g_force.load(std::memory_order_relaxed) & QSA_DEBUG_FORCE_FALLBACK) != 0; }
+bool force_redo() { return (g_force.load(std::memory_order_relaxed) & QSA_DEBUG_FORCE_REDO) != 0; }
 
 qsa::ScorerChoice scorer_choice() {
     const uint32_t f = g_force.load(std::memory_order_relaxed);
@@ -241,9 +242,10 @@ QSA_EXPORT int32_t qsa_debug_events_recorded(void) { return g_recorded; }
 QSA_EXPORT qsa_status qsa_debug_force(uint32_t mask) {
     g_err[0] = 0;
     constexpr uint32_t known = QSA_DEBUG_FORCE_TWO_PASS | QSA_DEBUG_FORCE_FUSED | QSA_DEBUG_FORCE_FALLBACK |
-                               QSA_DEBUG_FORCE_TILES | QSA_DEBUG_FORCE_GROUPS;
+                               QSA_DEBUG_FORCE_TILES | QSA_DEBUG_FORCE_GROUPS | QSA_DEBUG_FORCE_REDO;
     REQUIRE((mask & ~known) == 0, QSA_ERR_INVALID_ARGUMENT, "unknown debug bits 0x%x", mask & ~known);
-    REQUIRE(!((mask & QSA_DEBUG_FORCE_TWO_PASS) && (mask & (QSA_DEBUG_FORCE_FUSED | QSA_DEBUG_FORCE_FALLBACK))),
+    REQUIRE(!((mask & QSA_DEBUG_FORCE_TWO_PASS) &&
+              (mask & (QSA_DEBUG_FORCE_FUSED | QSA_DEBUG_FORCE_FALLBACK | QSA_DEBUG_FORCE_REDO))),
             QSA_ERR_INVALID_ARGUMENT, "the two-pass and the fused arm cannot both be forced (0x%x)", mask);
     REQUIRE(!((mask & QSA_DEBUG_FORCE_TILES) && (mask & QSA_DEBUG_FORCE_GROUPS)), QSA_ERR_INVALID_ARGUMENT,
             "the tiled and the windowed scorer cannot both be forced (0x%x)", mask);
@@ -494,7 +496,8 @@ qsa_status run_select(const SelectCall& c, void* workspace, const DeviceInfo* de
         HIP_CHECK(mark(s));
         HIP_CHECK(qsa::launch_score_filter(a, qsum, thresh, cand, count, L.plan.cand_cap, cus, s));
         HIP_CHECK(mark(s));
-        HIP_CHECK(qsa::launch_fused_final(a, vs, L.plan, thresh, cand, count, redo, kb, expand, c.k, c.out, s));
+        HIP_CHECK(qsa::launch_fused_final(a, vs, L.plan, thresh, cand, count, redo, force_redo(), kb, expand, c.k,
+                                          c.out, s));
         HIP_CHECK(mark(s));
         g_events = nullptr;
         g_path = "fused";

@@ -108,7 +108,8 @@ hipError_t launch_sample_threshold(const float* samp, int64_t ld_s, const Visibl
                                    hipStream_t stream);
 
 hipError_t launch_fused_final(const PagedArgs& a, const VisibleSource& vis, const FusedPlan& f, const uint64_t* thresh,
-                              const uint64_t* cand, const int32_t* cand_count, int32_t* redo, int32_t kb, int32_t expand,
+                              const uint64_t* cand, const int32_t* cand_count, int32_t* redo, bool force_redo,
+                              int32_t kb, int32_t expand,
                               int32_t out_len, int32_t* out, hipStream_t stream);
 
 // Sparse attention over selected tokens (attend.hip): head_dim 256, at most

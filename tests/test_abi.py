@@ -199,8 +199,9 @@ def test_binding_refuses_mis_shaped_tensors_before_any_call():
 
 def test_debug_force_rejects_bad_masks():
     assert Q.qsa_debug_forced() == 0
-    for bad in (0x20, Q.QSA_DEBUG_FORCE_TWO_PASS | Q.QSA_DEBUG_FORCE_FUSED,
+    for bad in (0x40, Q.QSA_DEBUG_FORCE_TWO_PASS | Q.QSA_DEBUG_FORCE_FUSED,
                 Q.QSA_DEBUG_FORCE_TWO_PASS | Q.QSA_DEBUG_FORCE_FALLBACK,
+                Q.QSA_DEBUG_FORCE_TWO_PASS | Q.QSA_DEBUG_FORCE_REDO,
                 Q.QSA_DEBUG_FORCE_TILES | Q.QSA_DEBUG_FORCE_GROUPS):
         with pytest.raises(Q.QSAError) as e:
             Q.qsa_debug_force(bad)
@@ -214,6 +215,11 @@ def test_debug_force_rejects_bad_masks():
     finally:
         Q.qsa_debug_force(0)
     assert 0 < fused < Q.qsa_select_paged_tokens_workspace_size(256, 256, 46000, 4, 2048)
+    Q.qsa_debug_force(Q.QSA_DEBUG_FORCE_REDO)
+    try:  # the redo override also drives the fused arm
+        assert Q.qsa_select_paged_tokens_workspace_size(256, 256, 46000, 4, 2048) == fused
+    finally:
+        Q.qsa_debug_force(0)
 
 
 def attend(**over):

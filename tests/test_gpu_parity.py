@@ -27,11 +27,11 @@ RELU = Q.QSA_SCORE_RELU
 KEYS = Q.QSA_OUT_KEYS
 
 
-PATHS = ["two_pass", "fused", "fused_fallback"]
+PATHS = ["two_pass", "fused", "fused_fallback", "fused_redo"]
 
 
 ARM_BITS = {"two_pass": Q.QSA_DEBUG_FORCE_TWO_PASS, "fused": Q.QSA_DEBUG_FORCE_FUSED,
-            "fused_fallback": Q.QSA_DEBUG_FORCE_FALLBACK}
+            "fused_fallback": Q.QSA_DEBUG_FORCE_FALLBACK, "fused_redo": Q.QSA_DEBUG_FORCE_REDO}
 SCORER_BITS = {"tiles": Q.QSA_DEBUG_FORCE_TILES, "groups": Q.QSA_DEBUG_FORCE_GROUPS}
 
 
@@ -48,8 +48,8 @@ def _forced(group, bit):
 
 def force_path(name):
     """Drive one execution arm deliberately; "fused_fallback" makes every row
-    of the fused arm take its exact recompute path; None leaves the choice to
-    the library."""
+    of the fused arm take its exact recompute path, "fused_redo" every row's
+    final select its second pass; None leaves the choice to the library."""
     return _forced(ARM_BITS, 0 if name is None else ARM_BITS[name])
 
 
@@ -511,7 +511,7 @@ def test_full_kernel_shape(oracle_mod, flags):
     path."""
     w = W.kernel_shape()
     rows = sorted(set(_spread(w.rows, 56, 5) + [63, 64, 127, 128, 1535, 1536, 1599, 1600]))
-    sampled_parity(oracle_mod, w, flags, False, rows, paths=(None, "two_pass", "fused_fallback"))
+    sampled_parity(oracle_mod, w, flags, False, rows, paths=(None, "two_pass", "fused_fallback", "fused_redo"))
 
 
 def test_full_tie_stress(oracle_mod):

@@ -189,14 +189,16 @@ __global__ __launch_bounds__(kNT) void topk_rows_kernel(TopkArgs A) {
 
 // Rows whose visible keys fit in registers (V <= NT * EPT, with NT threads
 // per workgroup).  Every score is loaded once, all loads issued before any
-// use, and kept as its order key (element e of thread t is key e*NT + t).  One histogram level
-// over the row (kSelBins bins of a power-of-two width between its smallest
-// and largest key) finds the bin holding the kk-th largest; the keys from that
-// bin's lower edge up -- usually a few more than kk -- are compacted into LDS,
-// and select_from_bound (qsa_select.hpp) ranks them exactly, usually with no
-// sort at all.  If more than kCompact keys survive (heavy ties or clustering
-// at the cut), the row is selected by select_exact_sorted instead, with keys
-// re-read from the score row at each level.
+// use, and kept as its order key (element e of thread t is key e*NT + t).  One
+// histogram level (kSelBins bins of a power-of-two width between the smallest
+// and largest key) finds the bin holding the kk-th largest -- for long rows
+// first over every 8th slot only, the bound then checked by an exact count --
+// and the keys from that bin's lower edge up (usually a few more than kk) are
+// compacted into LDS, where select_from_bound (qsa_select.hpp) ranks them
+// exactly, usually with no sort at all.  If more than kCompact keys survive
+// (heavy ties or clustering at the cut), the row is selected by
+// select_exact_sorted instead, with keys re-read from the score row at each
+// level.
 constexpr int kRegNT = 512;  // threads per workgroup for rows of 8,193 .. 49,152 keys
 
 // x, with the compiler unable to reuse an earlier expression built from it:
@@ -253,16 +255,14 @@ __global__ __launch_bounds__(NT) void topk_regs_kernel(TopkArgs A) {
                 k[e] = e * NT + tid < V ? ke : 0u;
         }
         const auto key = [&](int e) { return k[e]; };
-        uint32_t mn, mx;
-        block_minmax_u32<NT, EPT>(key, V, &mn, &mx, &L.s.hs);  // (slots wholly past V skipped)
-        const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
-        // A cheap bound first: the histogram of every 8th slot gives the bin of
-        // its m-th largest key (m covers nsel/8 with a margin); the keys at or
-        // above that bin's lower edge are then counted exactly.  With at least
-        // nsel of them they hold the row's top nsel; with too few or too many
-        // the histogram of every key decides instead.
+        // A cheap bound first: the range and histogram of every 8th slot give
+        // the bin of its m-th largest key (m covers nsel/8 with a margin); the
+        // keys at or above that bin's lower edge are then counted exactly, and
+        // the count's prefix sum gives every thread its survivors' places.
+        // With nsel .. kCompact of them they hold the row's top nsel; with too
+        // few or too many the range and histogram of every key decide instead.
         uint32_t lo = 0u;
-        int surv = -1;
+        int surv = -1, myoff = 0;
         if constexpr (EPT >= 64) {
             constexpr int S = EPT / 8;
             int sampled = 0;  // nonzero keys in slots 0, 8, 16, ...
@@ -271,51 +271,82 @@ __global__ __launch_bounds__(NT) void topk_regs_kernel(TopkArgs A) {
             const float q = (float)nsel / 8.0f;
             const int m = (int)(q + 3.0f * sqrtf(q) + 8.0f);
             if (m <= sampled) {
-                int sa, sc;
                 const auto skey = [&](int j) { return k[8 * j]; };
-                const uint32_t bs = hist_level32<NT, S>(skey, (V + 7) / 8, mn, shift1, 32, 0u, m, &L.s.hs,
+                uint32_t smn, smx;
+                block_minmax_u32<NT, S>(skey, (V + 7) / 8, &smn, &smx, &L.s.hs);
+                const int sshift = max(0, bit_length32(smx - smn) - kSelBits);
+                int sa, sc;
+                const uint32_t bs = hist_level32<NT, S>(skey, (V + 7) / 8, smn, sshift, 32, 0u, m, &L.s.hs,
                                                             nullptr, &sa, &sc);
-                lo = mn + (bs << shift1);
+                lo = smn + (bs << sshift);
                 int c = 0;
 #pragma unroll
                 for (int e = 0; e < EPT; ++e) c += k[e] >= lo ? 1 : 0;
                 int total;
-                (void)block_inclusive_scan<NT>(c, L.s.hs.wsum, &total);
+                myoff = block_inclusive_scan<NT>(c, L.s.hs.wsum, &total) - c;
                 surv = total;
             }
         }
-        if (surv < nsel || surv > kCompact) {
+        const bool placed = surv >= nsel && surv <= kCompact;
+        if (!placed) {
+            uint32_t mn, mx;
+            block_minmax_u32<NT, EPT>(key, V, &mn, &mx, &L.s.hs);  // (slots wholly past V skipped)
+            const int shift1 = max(0, bit_length32(mx - mn) - kSelBits);
             int above, cnt;
             const uint32_t b = hist_level32<NT, EPT>(key, V, mn, shift1, 32, 0u, nsel, &L.s.hs, nullptr, &above, &cnt);
             lo = mn + (b << shift1);
             surv = above + cnt;  // keys >= lo (lo >= the smallest key > 0)
         }
         if (surv <= kCompact) {
-            if (tid == 0) L.nc = 0;
-            __syncthreads();
-            // the survivors, eight slots at a time: one LDS atomic per wave and
-            // batch reserves the batch's places, ballots order the lanes
             const int lane = tid & 63;
-            const uint64_t below = (1ull << lane) - 1ull;
+            if (placed) {
+                // every thread stores its survivors from its own place on (no
+                // atomics); a key's store has its compare's ballot as exec
+                uint32_t ad =
+                    (uint32_t)reinterpret_cast<uintptr_t>(static_cast<void*>(&L.c[0])) + 8u * (uint32_t)myoff;
 #pragma unroll
-            for (int g = 0; g < EPT; g += 8) {
-                uint64_t mk[8];
-                int tot = 0;
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    mk[u] = __ballot(g + u < EPT && k[g + u] >= lo);
-                    tot += __popcll(mk[u]);
+                for (int e = 0; e < EPT; ++e) {
+                    const bool p = k[e] >= lo;
+                    const uint64_t mk = __builtin_amdgcn_ballot_w64(p);
+                    const uint64_t cv = compose(k[e], (uint32_t)(e * NT + fresh(tid)));
+                    asm volatile(
+                        "s_mov_b64 exec, %[m]\n\t"
+                        "ds_write_b64 %[ad], %[d]\n\t"
+                        "s_mov_b64 exec, -1"
+                        :
+                        : [m] "s"(mk), [ad] "v"(ad), [d] "v"(cv)
+                        : "memory");
+                    ad += p ? 8u : 0u;
                 }
-                if (tot) {  // (wave-uniform)
-                    int at = 0;
-                    if (lane == 0) at = atomicAdd(&L.nc, tot);
-                    at = __builtin_amdgcn_readfirstlane(at);
+                // (the compiler's wait counting does not see these stores: they
+                // must land before the barrier lets other waves read them)
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            } else {
+                if (tid == 0) L.nc = 0;
+                __syncthreads();
+                // the survivors, eight slots at a time: one LDS atomic per wave
+                // and batch reserves the batch's places, ballots order the lanes
+                const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+                for (int g = 0; g < EPT; g += 8) {
+                    uint64_t mk[8];
+                    int tot = 0;
 #pragma unroll
                     for (int u = 0; u < 8; ++u) {
-                        if (g + u < EPT && ((mk[u] >> lane) & 1ull))
-                            L.c[at + __popcll(mk[u] & below)] =
-                                compose(k[g + u], (uint32_t)((g + u) * NT + fresh(tid)));
-                        at += __popcll(mk[u]);
+                        mk[u] = __ballot(g + u < EPT && k[g + u] >= lo);
+                        tot += __popcll(mk[u]);
+                    }
+                    if (tot) {  // (wave-uniform)
+                        int at = 0;
+                        if (lane == 0) at = atomicAdd(&L.nc, tot);
+                        at = __builtin_amdgcn_readfirstlane(at);
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            if (g + u < EPT && ((mk[u] >> lane) & 1ull))
+                                L.c[at + __popcll(mk[u] & below)] =
+                                    compose(k[g + u], (uint32_t)((g + u) * NT + fresh(tid)));
+                            at += __popcll(mk[u]);
+                        }
                     }
                 }
             }

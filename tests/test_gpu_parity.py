@@ -466,6 +466,25 @@ def test_topk_rows_few_long(oracle_mod, kind):
         assert np.array_equal(out, oracle_mod.select_rows(sc, V, k)), (kind, k)
 
 
+def test_topk_rows_repeated_calls(oracle_mod):
+    """Rows of 16k..40k scores (the sampled-bound path, whose survivors are
+    stored at per-thread places and read by other waves after a barrier),
+    256 rows so that every compute unit holds one: twenty calls in a row, each
+    equal to the oracle's selection."""
+    rng = np.random.default_rng(54)
+    rows, ld, k = 256, 40_000, 2048
+    sc = rng.standard_normal((rows, ld)).astype(np.float32)
+    sc[:, rng.integers(0, ld, 300)] = 2.25          # ties near the cut of most rows
+    V = rng.integers(16_000, ld + 1, size=rows).astype(np.int32)
+    exp = oracle_mod.select_rows(sc, V, k)
+    s = torch.from_numpy(sc).to(DEV)
+    vis = torch.from_numpy(V).to(DEV)
+    for it in range(20):
+        out = Q.qsa_topk_rows(s, k, visible=vis, max_visible=ld)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), exp), f"call {it}"
+
+
 def test_topk_rows_visible_none(oracle_mod):
     rng = np.random.default_rng(53)
     sc = rng.standard_normal((7, 6000)).astype(np.float32)

@@ -50,7 +50,11 @@
 //             rows' global candidate lists (one atomic per lane), as does
 //             leaving a tile.  The appends themselves run without branches:
 //             exec is set to the score's ballot around one LDS store; they
-//             are issued in the gaps of the next stage's MFMA chain.
+//             are issued in the gaps of the next stage's MFMA chain.  A row
+//             with no key in a pass (another request's, or a padding row)
+//             compares against NaN, so only the pass's own rows bound the
+//             column tiles that need a per-key mask, and a wave none of whose
+//             rows is in the pass skips its MFMA chain.
 #pragma once
 
 #include "qsa_device.hpp"
@@ -540,10 +544,17 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
             // this lane's row bound, and the smallest over the wave's rows:
             // column tiles entirely below it need no per-row mask
             const int lim_r = s_lim[erow];
-            int wlim = lim_r;
+            // (Filter: a row with no key in this pass -- another request's, one
+            // that ends before the piece, or a padding row -- takes a NaN
+            // threshold, which no score reaches, and does not bound the
+            // wave's unmasked column tiles)
+            const bool row_on = lim_r > c0;
+            int wlim = FILTER && !row_on ? 0x7FFFFFFF : lim_r;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) wlim = min(wlim, __shfl_xor(wlim, o, 64));
             wlim = __builtin_amdgcn_readfirstlane(wlim);
+            const float fTp = row_on ? fT : __builtin_nanf("");
+            const bool wave_on = wlim != 0x7FFFFFFF;
             // (with one request the slot table and bounds were in place at the first barrier)
             if (!one_req) __syncthreads();
 
@@ -646,17 +657,20 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
                 issue(sl_next, pf_issue);
                 sl_next = slots_of(si + 3);
                 __builtin_amdgcn_sched_barrier(0);
-                half8 kf[kSlices];
+                // (a wave with no row in this pass has nothing to score or append)
+                if (wave_on) {
+                    half8 kf[kSlices];
 #pragma unroll
-                for (int s = 0; s < kSlices; ++s)
-                    kf[s] = *reinterpret_cast<const half8*>(sk + lds_key_chunk(lane & 31, 2 * s + (lane >> 5)));
-                __builtin_amdgcn_sched_barrier(0);
-                __builtin_amdgcn_s_setprio(1);
-                mfma_quarter_appends<0>(acc, kf, kf[0], kf[1], qa, pm, pacc, pkb, pad);
-                mfma_quarter_appends<1>(acc, kf, kf[2], kf[3], qa, pm, pacc, pkb, pad);
-                mfma_quarter_appends<2>(acc, kf, kf[4], kf[5], qa, pm, pacc, pkb, pad);
-                mfma_quarter_appends<3>(acc, kf, kf[6], kf[7], qa, pm, pacc, pkb, pad);
-                __builtin_amdgcn_s_setprio(0);
+                    for (int s = 0; s < kSlices; ++s)
+                        kf[s] = *reinterpret_cast<const half8*>(sk + lds_key_chunk(lane & 31, 2 * s + (lane >> 5)));
+                    __builtin_amdgcn_sched_barrier(0);
+                    __builtin_amdgcn_s_setprio(1);
+                    mfma_quarter_appends<0>(acc, kf, kf[0], kf[1], qa, pm, pacc, pkb, pad);
+                    mfma_quarter_appends<1>(acc, kf, kf[2], kf[3], qa, pm, pacc, pkb, pad);
+                    mfma_quarter_appends<2>(acc, kf, kf[4], kf[5], qa, pm, pacc, pkb, pad);
+                    mfma_quarter_appends<3>(acc, kf, kf[6], kf[7], qa, pm, pacc, pkb, pad);
+                    __builtin_amdgcn_s_setprio(0);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 stage_in(buf ^ 1, pf_wait);
 
@@ -670,7 +684,7 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
                         if (v >= nv) acc[v] = -__builtin_huge_valf();
                 }
 #pragma unroll
-                for (int v = 0; v < 16; ++v) m[v] = __builtin_amdgcn_ballot_w64(acc[v] >= fT);
+                for (int v = 0; v < 16; ++v) m[v] = __builtin_amdgcn_ballot_w64(acc[v] >= fTp);
                 int n = 0;
                 count_masks8(m, 0, n);
                 count_masks8(m, 8, n);

@@ -70,7 +70,7 @@ def parse():
                     help="timed steps of each configuration in the per-configuration table")
     ap.add_argument("--workload", default="kernel_shape",
                     choices=["tiny", "kernel_shape", "tie_stress", "mixed", "decode", "long_1", "long_8"])
-    ap.add_argument("--path", choices=["two_pass", "fused"], default=None,
+    ap.add_argument("--path", choices=["two_pass", "fused", "stream"], default=None,
                     help="force one execution arm (default: the library's choice)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="after timing, copy this many MiB device to device (counter scale probe)")
@@ -118,6 +118,13 @@ KERNEL_SOURCES = {
     "topk_regs": (("topk_regs_kernel",),
                   ["paged_block_scoring_amd/csrc/topk.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
     "topk_rows": (("topk_rows_kernel",), ["paged_block_scoring_amd/csrc/topk.hip"]),
+    # the streaming arm (one row per request): chunks scored and cut to their
+    # top-k on chip, then a merge per row
+    "stream_chunks": (("stream_chunk_kernel",),
+                      ["paged_block_scoring_amd/csrc/stream_select.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp",
+                       "paged_block_scoring_amd/csrc/qsa_device.hpp"]),
+    "stream_merge": (("stream_merge_kernel",),
+                     ["paged_block_scoring_amd/csrc/stream_select.hip", "paged_block_scoring_amd/csrc/qsa_select.hpp"]),
     "attend": (("attend_kernel",), ["paged_block_scoring_amd/csrc/attend.hip"]),
     "compress_blocks": (("compress_blocks_kernel",), ["paged_block_scoring_amd/csrc/compress.hip"]),
 }
@@ -311,6 +318,7 @@ def time_calls(fn, steps, warmup, torch):
 KERNELS = {
     "fused": ["qsum_prep", "sample_scorer", "sample_threshold", "filter_scorer", "final_select"],
     "two_pass": ["scorer", "topk_rows"],
+    "stream": ["stream_chunks", "stream_merge"],
 }
 
 
@@ -497,6 +505,9 @@ class Run:
             sampled = int(((self.vis + stride - 1) // stride).sum())
             units["filter_scorer"] = ("mfma", flops_full, PEAK_MFMA_F16_TFLOPS, "TFLOP/s")
             units["sample_scorer"] = ("mfma", FLOPS_PER_ROW_KEY * sampled, PEAK_MFMA_F16_TFLOPS, "TFLOP/s")
+        elif path == "stream":
+            # every key streams from HBM once (256 B); only the chunks' top-k lists are written
+            units["stream_chunks"] = ("hbm", 256 * self.sum_v + 1024 * rows, PEAK_HBM_GBS, "GB/s")
         elif rows < 32 * w.num_reqs:
             # few rows per request: every key streams from HBM for one row (256 B per key)
             units["scorer"] = ("hbm", 256 * self.sum_v + 1024 * rows, PEAK_HBM_GBS, "GB/s")
@@ -651,7 +662,8 @@ def main():
     import workloads as W
     from paged_block_scoring_amd import qsa as Q
     if args.path:
-        Q.qsa_debug_force({"two_pass": Q.QSA_DEBUG_FORCE_TWO_PASS, "fused": Q.QSA_DEBUG_FORCE_FUSED}[args.path])
+        Q.qsa_debug_force({"two_pass": Q.QSA_DEBUG_FORCE_TWO_PASS, "fused": Q.QSA_DEBUG_FORCE_FUSED,
+                           "stream": Q.QSA_DEBUG_FORCE_STREAM}[args.path])
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -172,7 +172,9 @@ size_t qsa_topk_rows_workspace_size(int32_t rows, int32_t max_visible, int32_t k
  *               tokens cr*j .. cr*j+cr-1 ascending (or key j with
  *               QSA_OUT_KEYS); -1 after the min(k/cr, V_r) selected blocks.
  *  workspace    device scratch of at least
- *               qsa_select_paged_tokens_workspace_size(...) bytes.
+ *               qsa_select_paged_tokens_workspace_size(...) bytes, queried
+ *               under the same debug-force mask as the call (the arms'
+ *               workspaces differ in size).
  */
 qsa_status qsa_select_paged_tokens(const void* q, const void* kcache, const int32_t* page_table,
                                    int64_t pt_stride, int32_t num_pages, int32_t num_reqs,
@@ -310,7 +312,8 @@ qsa_status qsa_compress_keys(const void* k_tok, const int32_t* tok_req, const in
 const char* qsa_last_error(void);
 
 /* Name of the execution arm the calling thread's last successful
- * qsa_select_paged_tokens call used (e.g. "two_pass"); "" before any call. */
+ * qsa_select_paged_tokens call used ("two_pass", "fused" or "stream"); ""
+ * before any call. */
 const char* qsa_last_path(void);
 
 /* Library version string. */
@@ -324,8 +327,9 @@ const char* qsa_version(void);
  * disarms the hook; qsa_debug_events_recorded() then returns how many events
  * it recorded.  Kernel order: two-pass arm = scorer, selector; fused arm =
  * head-sum preparation (default form; nothing in the relu form), sampling
- * scorer, threshold, filtering scorer, final select; producer = block
- * compression, staging of open blocks (none when compress_ratio is 1). */
+ * scorer, threshold, filtering scorer, final select; streaming arm = chunk
+ * top-k, merge; producer = block compression, staging of open
+ * blocks (none when compress_ratio is 1). */
 qsa_status qsa_debug_record_events(void* const* events, int32_t n);
 int32_t qsa_debug_events_recorded(void);
 
@@ -341,6 +345,7 @@ int32_t qsa_debug_events_recorded(void);
 #define QSA_DEBUG_FORCE_TILES    0x8u   /* materialising scorer: the row-tiled kernel */
 #define QSA_DEBUG_FORCE_GROUPS   0x10u  /* materialising scorer: the windowed kernel */
 #define QSA_DEBUG_FORCE_REDO     0x20u  /* the fused arm, every row's final select in its second pass */
+#define QSA_DEBUG_FORCE_STREAM   0x40u  /* qsa_select_paged_tokens: the streaming arm */
 qsa_status qsa_debug_force(uint32_t mask);
 uint32_t qsa_debug_forced(void);
 

@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqsa.so")
 
-SOURCES = ["qsa_api.hip", "score.hip", "score_group.hip", "topk.hip", "fused.hip", "attend.hip", "compress.hip"]
+SOURCES = ["qsa_api.hip", "score.hip", "score_group.hip", "stream_select.hip", "topk.hip", "fused.hip", "attend.hip",
+           "compress.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

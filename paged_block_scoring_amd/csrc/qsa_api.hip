@@ -194,19 +194,24 @@ FusedLayout fused_layout(int32_t rows, int32_t max_visible, int32_t kb) {
     return L;
 }
 
-enum class Path { TwoPass, Fused };
+enum class Path { TwoPass, Fused, Stream };
 
 // The fused arm scores every key twice over a 1/16 sample but never writes
 // the score matrix; it pays off when many rows share each request's keys and
 // there is enough work to cover its five launches (measured crossover: rows x
 // longest row between 4.2 M and 6.6 M keys).  Few rows per request (decode),
-// and small batches, take the two-pass arm.
+// and small batches, take the two-pass arm.  The streaming arm (chunk top-k
+// on chip, then a merge) is taken only when forced: on decode batches it
+// measured level with the two-pass arm at 256 rows of 16 k..46 k keys and
+// slower with fewer rows or shorter rows, where its coarser chunks leave a
+// longer tail.
 constexpr int64_t kFusedMinWork = 5000000;
 
 Path choose_path(int32_t rows, int32_t num_reqs, int32_t max_visible) {
     const uint32_t f = g_force.load(std::memory_order_relaxed);
     if (f & QSA_DEBUG_FORCE_TWO_PASS) return Path::TwoPass;
     if (f & (QSA_DEBUG_FORCE_FUSED | QSA_DEBUG_FORCE_FALLBACK | QSA_DEBUG_FORCE_REDO)) return Path::Fused;
+    if (f & QSA_DEBUG_FORCE_STREAM) return Path::Stream;
     if (max_visible <= 0) return Path::TwoPass;
     if (rows / (num_reqs > 0 ? num_reqs : 1) < 32) return Path::TwoPass;
     return (int64_t)rows * max_visible >= kFusedMinWork ? Path::Fused : Path::TwoPass;
@@ -242,11 +247,14 @@ QSA_EXPORT int32_t qsa_debug_events_recorded(void) { return g_recorded; }
 QSA_EXPORT qsa_status qsa_debug_force(uint32_t mask) {
     g_err[0] = 0;
     constexpr uint32_t known = QSA_DEBUG_FORCE_TWO_PASS | QSA_DEBUG_FORCE_FUSED | QSA_DEBUG_FORCE_FALLBACK |
-                               QSA_DEBUG_FORCE_TILES | QSA_DEBUG_FORCE_GROUPS | QSA_DEBUG_FORCE_REDO;
+                               QSA_DEBUG_FORCE_TILES | QSA_DEBUG_FORCE_GROUPS | QSA_DEBUG_FORCE_REDO |
+                               QSA_DEBUG_FORCE_STREAM;
+    constexpr uint32_t fused = QSA_DEBUG_FORCE_FUSED | QSA_DEBUG_FORCE_FALLBACK | QSA_DEBUG_FORCE_REDO;
     REQUIRE((mask & ~known) == 0, QSA_ERR_INVALID_ARGUMENT, "unknown debug bits 0x%x", mask & ~known);
-    REQUIRE(!((mask & QSA_DEBUG_FORCE_TWO_PASS) &&
-              (mask & (QSA_DEBUG_FORCE_FUSED | QSA_DEBUG_FORCE_FALLBACK | QSA_DEBUG_FORCE_REDO))),
-            QSA_ERR_INVALID_ARGUMENT, "the two-pass and the fused arm cannot both be forced (0x%x)", mask);
+    REQUIRE(((mask & QSA_DEBUG_FORCE_TWO_PASS) ? 1 : 0) + ((mask & fused) ? 1 : 0) +
+                    ((mask & QSA_DEBUG_FORCE_STREAM) ? 1 : 0) <= 1,
+            QSA_ERR_INVALID_ARGUMENT, "at most one of the two-pass, fused and streaming arms can be forced (0x%x)",
+            mask);
     REQUIRE(!((mask & QSA_DEBUG_FORCE_TILES) && (mask & QSA_DEBUG_FORCE_GROUPS)), QSA_ERR_INVALID_ARGUMENT,
             "the tiled and the windowed scorer cannot both be forced (0x%x)", mask);
     g_force.store(mask, std::memory_order_relaxed);
@@ -415,7 +423,9 @@ QSA_EXPORT size_t qsa_select_paged_tokens_workspace_size(int32_t rows, int32_t n
     if (rows <= 0 || max_visible <= 0 || k < 1 || compress_ratio < 1) return 0;
     const int32_t kb = (flags & QSA_OUT_KEYS) ? k : k / compress_ratio;
     if (kb < 1) return 0;
-    if (choose_path(rows, num_reqs, max_visible) == Path::Fused) return fused_layout(rows, max_visible, kb).total;
+    const Path p = choose_path(rows, num_reqs, max_visible);
+    if (p == Path::Stream) return qsa::stream_bytes(rows, max_visible, kb);
+    if (p == Path::Fused) return fused_layout(rows, max_visible, kb).total;
     return two_pass_bytes(rows, max_visible);
 }
 
@@ -476,7 +486,16 @@ qsa_status run_select(const SelectCall& c, void* workspace, const DeviceInfo* de
     vs.cr = c.compress_ratio;
     vs.max_visible = c.max_visible;
     const int32_t expand = out_keys ? 1 : c.compress_ratio;
-    if (choose_path(c.rows, c.num_reqs, c.max_visible) == Path::Fused) {
+    const Path path = choose_path(c.rows, c.num_reqs, c.max_visible);
+    if (path == Path::Stream) {
+        HIP_CHECK(mark(s));
+        HIP_CHECK(qsa::launch_stream_select(a, kb, expand, c.k, c.out, workspace, s, mark));
+        HIP_CHECK(mark(s));
+        g_events = nullptr;
+        g_path = "stream";
+        return QSA_OK;
+    }
+    if (path == Path::Fused) {
         const FusedLayout L = fused_layout(c.rows, c.max_visible, kb);
         unsigned char* w = static_cast<unsigned char*>(workspace);
         float* samp = reinterpret_cast<float*>(w + L.off_samp);

@@ -58,6 +58,14 @@ int32_t group_rows_for(int32_t rows, int32_t num_reqs, bool relu);
 // Few-rows-per-request scorer (score_group.hip): same scores as the tiled one.
 hipError_t launch_score_group(const PagedArgs& a, float* out, int64_t ld, int32_t cus, hipStream_t stream);
 
+// Streaming arm (stream_select.hip): chunks of each row are scored and cut
+// to their exact top-kb on chip (workspace: stream_bytes), then one
+// workgroup per row merges them; out as qsa_select_paged_tokens.  `mark` is
+// called between the two kernels.
+size_t stream_bytes(int32_t rows, int32_t max_visible, int32_t kb);
+hipError_t launch_stream_select(const PagedArgs& a, int32_t kb, int32_t expand, int32_t out_len, int32_t* out,
+                                void* workspace, hipStream_t stream, hipError_t (*mark)(hipStream_t));
+
 // Scorer over logical keys i (key stride*i): out[r*ld + i] for i < ceil(V_r/stride).
 // With true_scores false the default form stores chain results (score / f of
 // the row's head-sum factor f), the unit the filtering pass compares in.

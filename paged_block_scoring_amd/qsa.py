@@ -37,6 +37,7 @@ QSA_DEBUG_FORCE_FALLBACK = 0x4
 QSA_DEBUG_FORCE_TILES = 0x8
 QSA_DEBUG_FORCE_GROUPS = 0x10
 QSA_DEBUG_FORCE_REDO = 0x20
+QSA_DEBUG_FORCE_STREAM = 0x40
 
 EXPORTED = (
     "qsa_score_paged", "qsa_topk_rows", "qsa_topk_rows_workspace_size",

@@ -225,7 +225,9 @@ static void abi_checks() {
     expect(qsa_topk_rows(scores, 99, nullptr, 4, 100, 8, out, nullptr, 0, nullptr), QSA_ERR_INVALID_ARGUMENT,
            "topk ld");
     expect(qsa_topk_rows(scores, 100, nullptr, 0, 100, 8, nullptr, nullptr, 0, nullptr), QSA_OK, "topk zero rows");
-    expect(qsa_debug_force(0x40), QSA_ERR_INVALID_ARGUMENT, "unknown debug bits");
+    expect(qsa_debug_force(0x80), QSA_ERR_INVALID_ARGUMENT, "unknown debug bits");
+    expect(qsa_debug_force(QSA_DEBUG_FORCE_STREAM | QSA_DEBUG_FORCE_TWO_PASS), QSA_ERR_INVALID_ARGUMENT,
+           "conflicting arms (streaming)");
     expect(qsa_debug_force(QSA_DEBUG_FORCE_TWO_PASS | QSA_DEBUG_FORCE_FUSED), QSA_ERR_INVALID_ARGUMENT,
            "conflicting arms");
     CHECK(qsa_debug_forced() == 0, "a refused mask changes nothing");

@@ -199,9 +199,12 @@ def test_binding_refuses_mis_shaped_tensors_before_any_call():
 
 def test_debug_force_rejects_bad_masks():
     assert Q.qsa_debug_forced() == 0
-    for bad in (0x40, Q.QSA_DEBUG_FORCE_TWO_PASS | Q.QSA_DEBUG_FORCE_FUSED,
+    for bad in (0x80, Q.QSA_DEBUG_FORCE_TWO_PASS | Q.QSA_DEBUG_FORCE_FUSED,
                 Q.QSA_DEBUG_FORCE_TWO_PASS | Q.QSA_DEBUG_FORCE_FALLBACK,
                 Q.QSA_DEBUG_FORCE_TWO_PASS | Q.QSA_DEBUG_FORCE_REDO,
+                Q.QSA_DEBUG_FORCE_STREAM | Q.QSA_DEBUG_FORCE_TWO_PASS,
+                Q.QSA_DEBUG_FORCE_STREAM | Q.QSA_DEBUG_FORCE_FUSED,
+                Q.QSA_DEBUG_FORCE_STREAM | Q.QSA_DEBUG_FORCE_REDO,
                 Q.QSA_DEBUG_FORCE_TILES | Q.QSA_DEBUG_FORCE_GROUPS):
         with pytest.raises(Q.QSAError) as e:
             Q.qsa_debug_force(bad)
@@ -220,6 +223,12 @@ def test_debug_force_rejects_bad_masks():
         assert Q.qsa_select_paged_tokens_workspace_size(256, 256, 46000, 4, 2048) == fused
     finally:
         Q.qsa_debug_force(0)
+    Q.qsa_debug_force(Q.QSA_DEBUG_FORCE_STREAM)
+    try:  # streaming arm: 6 chunk lists of 512 composites (8 bytes) per row, then 6 counts
+        stream = Q.qsa_select_paged_tokens_workspace_size(256, 256, 46000, 4, 2048)
+    finally:
+        Q.qsa_debug_force(0)
+    assert stream == 256 * 6 * 512 * 8 + 256 * 6 * 4
 
 
 def attend(**over):

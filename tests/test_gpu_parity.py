@@ -27,11 +27,12 @@ RELU = Q.QSA_SCORE_RELU
 KEYS = Q.QSA_OUT_KEYS
 
 
-PATHS = ["two_pass", "fused", "fused_fallback", "fused_redo"]
+PATHS = ["two_pass", "fused", "fused_fallback", "fused_redo", "stream"]
 
 
 ARM_BITS = {"two_pass": Q.QSA_DEBUG_FORCE_TWO_PASS, "fused": Q.QSA_DEBUG_FORCE_FUSED,
-            "fused_fallback": Q.QSA_DEBUG_FORCE_FALLBACK, "fused_redo": Q.QSA_DEBUG_FORCE_REDO}
+            "fused_fallback": Q.QSA_DEBUG_FORCE_FALLBACK, "fused_redo": Q.QSA_DEBUG_FORCE_REDO,
+            "stream": Q.QSA_DEBUG_FORCE_STREAM}
 SCORER_BITS = {"tiles": Q.QSA_DEBUG_FORCE_TILES, "groups": Q.QSA_DEBUG_FORCE_GROUPS}
 
 
@@ -323,7 +324,7 @@ def test_tiles_without_keys(oracle_mod):
 
 
 @pytest.mark.parametrize("name,path", [("kernel_shape_80", "fused"), ("decode_small", "two_pass"),
-                                       ("mixed_small", "fused_fallback")])
+                                       ("mixed_small", "fused_fallback"), ("decode_small", "stream")])
 def test_graph_capture(oracle_mod, name, path):
     """The whole call captured in a HIP graph (the pages name graph capture as a
     failure site of their cooperative selector): every replay, with eager work
@@ -331,8 +332,8 @@ def test_graph_capture(oracle_mod, name, path):
     w = REDUCED[name](False)
     d = to_dev(w)
     mv = int(visible(oracle_mod, w).max())
-    need = Q.qsa_select_paged_tokens_workspace_size(w.rows, w.num_reqs, mv, w.compress_ratio, w.k)
-    with force_path(path):
+    with force_path(path):  # the workspace query follows the forced arm
+        need = Q.qsa_select_paged_tokens_workspace_size(w.rows, w.num_reqs, mv, w.compress_ratio, w.k)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)
         call = lambda out: Q.qsa_select_paged_tokens(d["q"], d["kcache"], d["page_table"], d["pos"],  # noqa: E731
                                                      w.compress_ratio, w.k, row_req=d["row_req"],

@@ -22,7 +22,7 @@ ROCM = "/opt/rocm"
 HIPCC = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
 CLANG = os.path.join(ROCM, "llvm", "bin", "clang")
 CLANGXX = os.path.join(ROCM, "llvm", "bin", "clang++")
-HIP_SOURCES = ["qsa_api.hip", "score.hip", "score_group.hip", "topk.hip", "fused.hip", "attend.hip", "compress.hip"]
+from paged_block_scoring_amd.build import SOURCES as HIP_SOURCES  # the library's own source list
 HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
 

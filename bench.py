@@ -242,7 +242,7 @@ def summarize_profile(args):
     import glob
     out = {}
     name = (args.workload + ("_consumer" if args.consumer else "") + ("_producer" if args.producer else "")
-            + ("_relu" if args.relu else ""))
+            + ("_relu" if args.relu else "") + (f"_{args.path}" if args.path else ""))
     if args.stats_dir:
         stats = _read_csv(glob.glob(os.path.join(args.stats_dir, "*_kernel_stats.csv"))[0])
         lines = [f"# Kernel time, {name} (rocprofv3 --kernel-trace --stats)", "",

@@ -531,14 +531,14 @@ def test_full_kernel_shape(oracle_mod, flags):
     path."""
     w = W.kernel_shape()
     rows = sorted(set(_spread(w.rows, 56, 5) + [63, 64, 127, 128, 1535, 1536, 1599, 1600]))
-    sampled_parity(oracle_mod, w, flags, False, rows, paths=(None, "two_pass", "fused_fallback", "fused_redo"))
+    sampled_parity(oracle_mod, w, flags, False, rows, paths=(None, "two_pass", "fused_fallback", "fused_redo", "stream"))
 
 
 def test_full_tie_stress(oracle_mod):
     w = W.tie_stress()
     d = to_dev(w)
     full = oracle_mod.select_paged_tokens(w.q, w.kcache, w.page_table, w.pos, 4, w.k)
-    for path in (None, "two_pass", "fused"):
+    for path in (None, "two_pass", "fused", "stream"):
         with force_path(path):
             out = gpu_select(d, w, 0)
         assert np.array_equal(out, full), path
@@ -551,14 +551,14 @@ def test_full_mixed(oracle_mod, flags):
     w = W.mixed()
     starts = np.concatenate([[0], np.cumsum(np.bincount(w.row_req))])
     sample = sorted(set(list(starts[:-1]) + list(starts[1:] - 1) + _spread(w.rows, 32, 6)))
-    sampled_parity(oracle_mod, w, flags, False, sample, paths=(None, "two_pass", "fused"))
+    sampled_parity(oracle_mod, w, flags, False, sample, paths=(None, "two_pass", "fused", "stream"))
 
 
 @pytest.mark.parametrize("name", ["long_1", "long_8"])
 def test_full_long_few(oracle_mod, name):
     """One and eight 184k-token requests with one row each."""
     w = W.make(name)
-    sampled_parity(oracle_mod, w, 0, False, [0, w.rows - 1], paths=(None, "fused"))
+    sampled_parity(oracle_mod, w, 0, False, [0, w.rows - 1], paths=(None, "fused", "stream"))
 
 
 @pytest.mark.slow
@@ -567,4 +567,4 @@ def test_full_decode(oracle_mod, flags):
     """Decode batch in both score forms: every row's scores against the
     oracle, and every row's selection in both arms."""
     w = W.decode()
-    sampled_parity(oracle_mod, w, flags, False, list(range(w.rows)), paths=(None, "fused"))
+    sampled_parity(oracle_mod, w, flags, False, list(range(w.rows)), paths=(None, "fused", "stream"))

@@ -326,7 +326,8 @@ const char* qsa_version(void);
  * passed as void*; they must stay valid until that call returns).  The call
  * disarms the hook; qsa_debug_events_recorded() then returns how many events
  * it recorded.  Kernel order: two-pass arm = scorer, selector; fused arm =
- * head-sum preparation (default form; nothing in the relu form), sampling
+ * head-sum preparation (default form; in the relu form the tile counts of
+ * calls with several requests, else nothing), sampling
  * scorer, threshold, filtering scorer, final select; streaming arm = chunk
  * top-k, merge; producer = block compression, staging of open
  * blocks (none when compress_ratio is 1). */

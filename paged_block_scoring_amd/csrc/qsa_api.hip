@@ -503,10 +503,11 @@ qsa_status run_select(const SelectCall& c, void* workspace, const DeviceInfo* de
         int32_t* count = reinterpret_cast<int32_t*>(w + L.off_count);
         int32_t* redo = reinterpret_cast<int32_t*>(w + L.off_redo);
         uint64_t* cand = reinterpret_cast<uint64_t*>(w + L.off_cand);
-        _Float16* qsum = a.relu ? nullptr : reinterpret_cast<_Float16*>(w + L.off_qsum);
+        // (the relu form uses the head-sum buffer for its tile counts only)
+        _Float16* qsum = reinterpret_cast<_Float16*>(w + L.off_qsum);
         const int cus = dev->cus;
         HIP_CHECK(mark(s));
-        if (qsum) HIP_CHECK(qsa::launch_qsum_prep(a, qsum, s));
+        HIP_CHECK(qsa::launch_qsum_prep(a, qsum, s));
         HIP_CHECK(mark(s));
         HIP_CHECK(qsa::launch_score_store(a, qsum, L.plan.stride, false, samp, L.plan.ld_s, cus, s));
         HIP_CHECK(mark(s));

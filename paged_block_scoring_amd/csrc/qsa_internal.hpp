@@ -32,6 +32,9 @@ struct PagedArgs {
 // count of its rows (qsum_tile_visible); then one float per row slot of every
 // tile, the row's head-sum factor f (qsa_device.hpp head_sum_factor; 1 for
 // slots past the last row): a chain over the fragments gives score / f.
+// The relu form computes no head sums: launch_qsum_prep then writes only, for
+// calls with several requests, the largest visible-key count of each 64-row
+// relu tile at the start of the buffer (and nothing for one request).
 size_t qsum_bytes(int32_t rows);
 const int32_t* qsum_tile_visible(const _Float16* qsum, int32_t rows);
 const float* qsum_row_factor(const _Float16* qsum, int32_t rows);

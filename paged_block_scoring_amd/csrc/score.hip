@@ -8,9 +8,16 @@
 namespace qsa {
 namespace {
 
+// The relu form scores q itself and leaves the head-sum buffer unused; with
+// several requests its first bytes hold the visible-key count of each relu
+// tile's longest row (relu_tile_visible_kernel).
+int32_t* relu_tile_visible(const _Float16* qsum) { return reinterpret_cast<int32_t*>(const_cast<_Float16*>(qsum)); }
+
 // Relu form: the tiled scorer of score_core.hpp.  Even shares of each XCD's
 // (tile, key) positions, in whole stages: about the form's resident
-// workgroups per compute unit, but no share below `min_seg` positions.
+// workgroups per compute unit, but no share below `min_seg` positions.  With
+// several requests and the tile counts in the head-sum buffer, the kernel
+// shares only the keys each tile can see (the grid stays the same).
 template <Epi EPI>
 hipError_t launch_relu(ScoreKernelArgs A, int32_t cus, int64_t min_seg, hipStream_t stream) {
     constexpr int64_t g = ReluForm::STEP;
@@ -18,6 +25,10 @@ hipError_t launch_relu(ScoreKernelArgs A, int32_t cus, int64_t min_seg, hipStrea
     const int64_t stripe = ((int64_t)(A.lmax + kXcds - 1) / kXcds + g - 1) / g * g;
     A.xcd_keys = (int32_t)stripe;
     const int64_t positions = (int64_t)A.tiles * stripe;
+    // (positions are counted in 32 bits, as in the default form's kernel)
+    A.tile_v = A.qsum && A.a.num_reqs > 1 && positions + (int64_t)A.tiles * g < (1ll << 31)
+                   ? relu_tile_visible(A.qsum)
+                   : nullptr;
     int64_t per_xcd = (int64_t)(cus / kXcds > 0 ? cus / kXcds : 1) * ReluForm::WG_PER_CU;
     int64_t seg = ((positions + per_xcd - 1) / per_xcd + g - 1) / g * g;
     if (seg < min_seg) seg = (min_seg + g - 1) / g * g;
@@ -214,8 +225,30 @@ const float* qsum_row_factor(const _Float16* qsum, int32_t rows) {
                 : nullptr;
 }
 
+// Relu form, several requests: the visible-key count of each relu tile's
+// longest row (0 for rows past the end or of an unknown request), one wave
+// per tile.
+__global__ __launch_bounds__(64) void relu_tile_visible_kernel(PagedArgs a, int32_t* __restrict__ tile_v) {
+    static_assert(ReluForm::TILE == 64, "one row per lane");
+    const int row = blockIdx.x * ReluForm::TILE + threadIdx.x;
+    int v = 0;
+    if (row < a.rows) {
+        const int req = a.row_req ? a.row_req[row] : 0;
+        if (req >= 0 && req < a.num_reqs) v = visible_keys(a.pos[row], a.cr, a.max_visible);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    if (threadIdx.x == 0) tile_v[blockIdx.x] = v;
+}
+
 hipError_t launch_qsum_prep(const PagedArgs& a, _Float16* qsum, hipStream_t stream) {
     if (a.rows <= 0) return hipSuccess;
+    if (a.relu) {
+        if (a.num_reqs <= 1) return hipSuccess;
+        const int64_t tiles = (a.rows + ReluForm::TILE - 1) / ReluForm::TILE;
+        relu_tile_visible_kernel<<<dim3((unsigned)tiles), 64, 0, stream>>>(a, relu_tile_visible(qsum));
+        return hipGetLastError();
+    }
     const int64_t tiles = (a.rows + RowsShape::TILE - 1) / RowsShape::TILE;
     int32_t* tile_v = const_cast<int32_t*>(qsum_tile_visible(qsum, a.rows));
     float* row_f = const_cast<float*>(qsum_row_factor(qsum, a.rows));

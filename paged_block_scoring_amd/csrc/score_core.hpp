@@ -16,8 +16,11 @@
 // Workgroup w runs on XCD w % 8 (the hardware's round-robin dispatch) and
 // owns a contiguous, equal share of that XCD's (tile, key) positions, so every
 // XCD streams only its stripe of keys (which stays in its L2) and every
-// workgroup does the same amount of work.  A share is processed as pieces of
-// one tile and at most kMaxPiece keys.
+// workgroup does the same amount of work.  With several requests and the
+// tiles' visible-key counts, each tile's own keys are striped instead and the
+// stripes shared evenly (TileShares, score_rows.hpp), so that tiles of short
+// rows cost nothing.  A share is processed as pieces of one tile and at most
+// kMaxPiece keys.
 //
 // A piece.  Each of the 4 waves holds the fp16 query fragments of its rows
 // in registers (loaded once per tile): MFMA row m = 4*row + head, 8 rows x 4
@@ -60,6 +63,7 @@ struct ScoreKernelArgs {
     int32_t stride;    // logical key i is key stride*i
     int32_t lmax;      // logical keys of the longest row: ceil(max_visible / stride)
     int32_t tiles;     // ceil(rows / rows per tile)
+    const int32_t* tile_v;  // relu form: [tiles] visible keys of each tile's longest row, or null (see below)
     int32_t xcd_keys;  // logical keys per XCD stripe (a multiple of the stage size)
     int64_t seg_len;   // (tile, key) positions per workgroup (a multiple of the stage size)
     // Store
@@ -150,14 +154,24 @@ __global__ __launch_bounds__(ScoreShape::NT, ReluForm::WG_PER_CU) void score_til
     const PagedArgs& a = A.a;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int xcd = blockIdx.x % kXcds, loc = blockIdx.x / kXcds;
+    // Work positions of this XCD: without tile counts, keys xk0 .. xk0+span of
+    // the XCD's stripe of the longest row for every tile, padded to whole
+    // stages so that every piece starts on a stage boundary (keys past the end
+    // are invisible to every row); with them (tile_v, several requests), each
+    // tile's own stripes laid end to end and shared evenly (TileShares).
+    const bool bal = A.tile_v != nullptr;
     const int xk0 = xcd * A.xcd_keys;
-    // keys of this XCD's stripe, padded to whole stages so that every piece
-    // starts on a stage boundary (keys past the end are invisible to every row)
     const int span = min(A.xcd_keys, (A.lmax - xk0 + kStepKeys - 1) / kStepKeys * kStepKeys);
-    if (span <= 0) return;
-    const int64_t total = (int64_t)A.tiles * span;
-    int64_t p = (int64_t)loc * A.seg_len;
-    const int64_t pend = min(p + A.seg_len, total);
+    if (!bal && span <= 0) return;
+    TileShares<NT, kStepKeys> ts{A.tile_v, A.tiles, A.stride, xcd};
+    int64_t p, pend;
+    if (bal) {
+        ts.begin(loc, gridDim.x / kXcds, &p, &pend);
+    } else {
+        const int64_t total = (int64_t)A.tiles * span;
+        p = (int64_t)loc * A.seg_len;
+        pend = min(p + A.seg_len, total);
+    }
 
     // staging: this thread's NLOAD consecutive keys of a stage and its chunk
     const int pk = NLOAD * (tid >> 4), pc = tid & 15;
@@ -176,10 +190,16 @@ __global__ __launch_bounds__(ScoreShape::NT, ReluForm::WG_PER_CU) void score_til
     int tile_r0 = -1;   // first row of the tile held in registers
 
     while (p < pend) {
-        const int tile = (int)(p / span);
-        const int off = (int)(p - (int64_t)tile * span);
-        const int len = (int)min<int64_t>(min<int64_t>((int64_t)(span - off), pend - p), (int64_t)kMaxPiece);
-        const int c0 = xk0 + off, c1 = c0 + len;
+        int tile, len, c0;
+        if (bal) {
+            ts.piece(p, pend, kMaxPiece, &tile, &c0, &len);
+        } else {
+            tile = (int)(p / span);
+            const int off = (int)(p - (int64_t)tile * span);
+            len = (int)min<int64_t>(min<int64_t>((int64_t)(span - off), pend - p), (int64_t)kMaxPiece);
+            c0 = xk0 + off;
+        }
+        const int c1 = c0 + len;
         p += len;
         const int r0 = tile * TILE;
         const bool new_tile = r0 != tile_r0;

@@ -212,6 +212,110 @@ __device__ __forceinline__ void mfma_quarter_appends(float16v& acc, const half8 
 #undef QSA_APP
 }
 
+// Balanced (tile, key) positions of the tiled scorers, for calls with several
+// requests.  tile_v[t] is the visible-key count of tile t's longest row; its
+// logical keys (logical key i is key stride*i) are cut into kXcds stripes
+// padded to whole stages of STEP keys, and this XCD's stripe of every tile is
+// laid end to end.  The XCD's workgroups share that total evenly, in whole
+// stages, so that tiles of short rows cost nothing.  A cursor follows the
+// tile that holds the current position.
+template <int NT, int STEP>
+struct TileShares {
+    const int32_t* tile_v;
+    int tiles, stride, xcd;
+    int tcur = 0, ucur = 0, stcur = 0;  // the tile holding the cursor, its share and its stripe
+    int64_t pbase = 0;                  // the position where that share starts
+
+    // this XCD's stage-padded share of tile t's keys; *st = the tile's stripe
+    __device__ __forceinline__ int share(int t, int* st) const {
+        const int lv = (tile_v[t] + stride - 1) / stride;
+        *st = ((lv + kXcds - 1) / kXcds + STEP - 1) / STEP * STEP;
+        const int u = min(max(lv - xcd * *st, 0), *st);
+        return (u + STEP - 1) / STEP * STEP;
+    }
+
+    // Positions [*p, *pend) of workgroup `loc` of the XCD's `per`, and the
+    // cursor on the tile that holds *p.  Called by the whole workgroup (one
+    // block scan of the shares); contains barriers.
+    __device__ __forceinline__ void begin(int loc, int64_t per, int64_t* p, int64_t* pend) {
+        __shared__ int32_t s_ws[NT / 64];
+        __shared__ int64_t s_found;
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        // an inclusive block scan of the shares of tiles t0 .. t0+NT-1
+        auto scan = [&](int t0, int& u, int& incl, int& chunk) {
+            int st;
+            u = t0 + tid < tiles ? share(t0 + tid, &st) : 0;
+            incl = u;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int nb = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += nb;
+            }
+            if (lane == 63) s_ws[wave] = incl;
+            __syncthreads();
+            chunk = 0;
+#pragma unroll
+            for (int w = 0; w < NT / 64; ++w) {
+                incl += w < wave ? s_ws[w] : 0;
+                chunk += s_ws[w];
+            }
+            __syncthreads();
+        };
+        int64_t total = 0;
+        int u0 = 0, incl0 = 0;  // the first chunk's scan, kept for the search below
+        for (int t0 = 0; t0 < tiles; t0 += NT) {
+            int u, incl, chunk;
+            scan(t0, u, incl, chunk);
+            if (t0 == 0) {
+                u0 = u;
+                incl0 = incl;
+            }
+            total += chunk;
+        }
+        const int64_t seg = max<int64_t>(STEP, ((total + per - 1) / per + STEP - 1) / STEP * STEP);
+        *p = (int64_t)loc * seg;
+        *pend = min(*p + seg, total);
+        if (*p < *pend) {
+            const int64_t q = *p;
+            // the tile whose share holds q (exactly one thread finds it); with
+            // at most NT tiles the first scan already holds every prefix
+            if (tid == 0) s_found = -1;
+            __syncthreads();
+            if (tiles <= NT) {
+                if (u0 > 0 && incl0 - u0 <= q && q < incl0)
+                    s_found = ((int64_t)tid << 32) | (uint64_t)(uint32_t)(incl0 - u0);
+            } else {
+                int64_t base = 0;
+                for (int t0 = 0; t0 < tiles; t0 += NT) {
+                    int u, incl, chunk;
+                    scan(t0, u, incl, chunk);
+                    if (u > 0 && base + incl - u <= q && q < base + incl)
+                        s_found = ((int64_t)(t0 + tid) << 32) | (uint64_t)(uint32_t)(base + incl - u);
+                    base += chunk;
+                }
+            }
+            __syncthreads();
+            tcur = (int)(s_found >> 32);
+            pbase = (int64_t)(uint32_t)(s_found & 0xFFFFFFFFll);
+            ucur = share(tcur, &stcur);
+        }
+    }
+
+    // The piece at position p (< pend): its tile, its first logical key and
+    // its length, at most maxlen keys and not past pend.
+    __device__ __forceinline__ void piece(int64_t p, int64_t pend, int maxlen, int* tile, int* c0, int* len) {
+        while (p >= pbase + ucur) {  // on to the next tile with keys on this XCD
+            pbase += ucur;
+            ++tcur;
+            ucur = share(tcur, &stcur);
+        }
+        *tile = tcur;
+        const int off = (int)(p - pbase);
+        *len = (int)min<int64_t>(min<int64_t>((int64_t)(ucur - off), pend - p), (int64_t)maxlen);
+        *c0 = xcd * stcur + off;
+    }
+};
+
 template <Epi EPI>
 __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A) {
     using S = RowsShape;
@@ -241,77 +345,10 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
     const int xk0 = xcd * A.xcd_keys;
     const int span = min(A.xcd_keys, (A.lmax - xk0 + STEP - 1) / STEP * STEP);
     if (!bal && span <= 0) return;
-    // this XCD's stage-padded share of tile t's keys; *st = the tile's stripe
-    auto share = [&](int t, int* st) {
-        const int lv = (A.tile_v[t] + A.stride - 1) / A.stride;
-        *st = ((lv + kXcds - 1) / kXcds + STEP - 1) / STEP * STEP;
-        const int u = min(max(lv - xcd * *st, 0), *st);
-        return (u + STEP - 1) / STEP * STEP;
-    };
+    TileShares<NT, STEP> ts{A.tile_v, A.tiles, A.stride, xcd};
     int64_t p, pend;
-    int tcur = 0, ucur = 0, stcur = 0;  // balanced mapping: the tile holding p, its share and stripe
-    int64_t pbase = 0;                  // ... and the position where its share starts
     if (bal) {
-        __shared__ int32_t s_ws[NT / 64];
-        __shared__ int64_t s_found;
-        // an inclusive block scan of the shares of tiles t0 .. t0+NT-1
-        auto scan = [&](int t0, int& u, int& incl, int& chunk) {
-            int st;
-            u = t0 + tid < A.tiles ? share(t0 + tid, &st) : 0;
-            incl = u;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int nb = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += nb;
-            }
-            if (lane == 63) s_ws[wave] = incl;
-            __syncthreads();
-            chunk = 0;
-#pragma unroll
-            for (int w = 0; w < NT / 64; ++w) {
-                incl += w < wave ? s_ws[w] : 0;
-                chunk += s_ws[w];
-            }
-            __syncthreads();
-        };
-        int64_t total = 0;
-        int u0 = 0, incl0 = 0;  // the first chunk's scan, kept for the search below
-        for (int t0 = 0; t0 < A.tiles; t0 += NT) {
-            int u, incl, chunk;
-            scan(t0, u, incl, chunk);
-            if (t0 == 0) {
-                u0 = u;
-                incl0 = incl;
-            }
-            total += chunk;
-        }
-        const int64_t per = gridDim.x / kXcds;
-        const int64_t seg = max<int64_t>(STEP, ((total + per - 1) / per + STEP - 1) / STEP * STEP);
-        p = (int64_t)loc * seg;
-        pend = min(p + seg, total);
-        if (p < pend) {
-            // the tile whose share holds p (exactly one thread finds it); with
-            // at most NT tiles the first scan already holds every prefix
-            if (tid == 0) s_found = -1;
-            __syncthreads();
-            if (A.tiles <= NT) {
-                if (u0 > 0 && incl0 - u0 <= p && p < incl0)
-                    s_found = ((int64_t)tid << 32) | (uint64_t)(uint32_t)(incl0 - u0);
-            } else {
-                int64_t base = 0;
-                for (int t0 = 0; t0 < A.tiles; t0 += NT) {
-                    int u, incl, chunk;
-                    scan(t0, u, incl, chunk);
-                    if (u > 0 && base + incl - u <= p && p < base + incl)
-                        s_found = ((int64_t)(t0 + tid) << 32) | (uint64_t)(uint32_t)(base + incl - u);
-                    base += chunk;
-                }
-            }
-            __syncthreads();
-            tcur = (int)(s_found >> 32);
-            pbase = (int64_t)(uint32_t)(s_found & 0xFFFFFFFFll);
-            ucur = share(tcur, &stcur);
-        }
+        ts.begin(loc, gridDim.x / kXcds, &p, &pend);
     } else {
         const int64_t total = (int64_t)A.tiles * span;
         p = (int64_t)loc * A.seg_len;
@@ -386,15 +423,7 @@ __global__ __launch_bounds__(RowsShape::NT, 2) void score_rows_kernel(RowsArgs A
     while (p < pend) {
         int tile, len, c0;
         if (bal) {
-            while (p >= pbase + ucur) {  // on to the next tile with keys on this XCD
-                pbase += ucur;
-                ++tcur;
-                ucur = share(tcur, &stcur);
-            }
-            tile = tcur;
-            const int off = (int)(p - pbase);
-            len = (int)min<int64_t>(min<int64_t>((int64_t)(ucur - off), pend - p), (int64_t)kRowsPiece);
-            c0 = xcd * stcur + off;
+            ts.piece(p, pend, kRowsPiece, &tile, &c0, &len);
         } else {
             tile = (int)(p / span);
             const int off = (int)(p - (int64_t)tile * span);

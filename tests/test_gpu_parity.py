@@ -278,14 +278,16 @@ def test_out_keys_reduced(oracle_mod):
             assert np.array_equal(out, expected_from_scores(oracle_mod, gs, V, k, 4, KEYS)), (path, k)
 
 
-def test_interleaved_requests(oracle_mod):
-    """Rows of different requests in any order (not grouped by request)."""
+@pytest.mark.parametrize("flags", [0, RELU])
+def test_interleaved_requests(oracle_mod, flags):
+    """Rows of different requests in any order (not grouped by request), both
+    score forms."""
     rng = np.random.default_rng(41)
     w = W.build("interleaved", rng, 41, [3000, 7000, 500, 12000], [30, 20, 5, 25], permute_pages=True,
                 integer=True, k=256)
     perm = rng.permutation(w.rows)
     w.q, w.pos, w.row_req = np.ascontiguousarray(w.q[perm]), w.pos[perm].copy(), w.row_req[perm].copy()
-    full_parity(oracle_mod, w, 0, True, paths=PATHS)
+    full_parity(oracle_mod, w, flags, True, paths=PATHS)
 
 
 def test_edges(oracle_mod):
@@ -310,17 +312,19 @@ def test_edges(oracle_mod):
     full_parity(oracle_mod, one, 0, True, paths=PATHS)
 
 
-def test_tiles_without_keys(oracle_mod):
+@pytest.mark.parametrize("flags", [0, RELU])
+def test_tiles_without_keys(oracle_mod, flags):
     """Several requests (the scorer then shares each tile's own visible keys
     among its workgroups): a whole 128-row tile whose rows see no key at all,
     a tile mixing such rows with rows of a long context, and a short and a long
-    request side by side; every arm, integer inputs, end to end."""
+    request side by side; every arm, both score forms, integer inputs, end to
+    end."""
     rng = np.random.default_rng(44)
     w = W.build("tiles", rng, 44, [20000, 300, 9000, 40], [128, 200, 70, 30], permute_pages=True, integer=True,
                 k=2048)
     w.pos = w.pos.copy()
     w.pos[128:328] = np.arange(200) % 3          # request 1: positions 0..2, no visible key
-    full_parity(oracle_mod, w, 0, True, paths=PATHS)
+    full_parity(oracle_mod, w, flags, True, paths=PATHS)
 
 
 @pytest.mark.parametrize("name,path", [("kernel_shape_80", "fused"), ("decode_small", "two_pass"),

@@ -87,3 +87,97 @@ def test_model_sees_the_unclamped_stage_padding():
     keys, the last one padded): the model is sharp enough to catch that."""
     assert largest_page_read(1616, 46000, 1, 16, clamp=False) >= ceil_div(46000, 16)
     assert largest_page_read(1616, 46000, 16, 16, clamp=False) >= ceil_div(46000, 16)
+
+
+# ---------------------------------------------------------------------------
+# The balanced split used with several requests (TileShares in
+# score_rows.hpp): each tile's own visible keys cut into 8 stripes padded to
+# whole stages, this XCD's stripe of every tile laid end to end, the XCD's
+# workgroups sharing that total evenly.  The default-form kernel uses it with
+# 128-row tiles, 32-key stages and 2,048-key pieces; the relu-form kernel with
+# 64-row tiles, 64-key stages and 1,024-key pieces.
+
+def tile_counts(w, tile):
+    """Largest visible-key count of each tile's rows (0 for rows past the end)."""
+    import oracle
+    v = np.array([oracle.visible_keys(int(p), w.compress_ratio) for p in w.pos], dtype=np.int64)
+    tiles = ceil_div(w.rows, tile)
+    pad = np.zeros(tiles * tile, dtype=np.int64)
+    pad[:w.rows] = v
+    return pad.reshape(tiles, tile).max(axis=1)
+
+
+def balanced_pieces(tile_v, stride, step, piece, per):
+    """Every piece (xcd, workgroup, tile, first key, length) of the balanced
+    split, following the kernel's begin/piece steps."""
+    def share(t, xcd):
+        lv = ceil_div(int(tile_v[t]), stride)
+        st = ceil_div(ceil_div(lv, XCDS), step) * step
+        u = min(max(lv - xcd * st, 0), st)
+        return ceil_div(u, step) * step, st
+
+    out = []
+    tiles = len(tile_v)
+    for xcd in range(XCDS):
+        shares = [share(t, xcd) for t in range(tiles)]
+        total = sum(u for u, _ in shares)
+        seg = max(step, ceil_div(ceil_div(total, per), step) * step)
+        starts = np.concatenate([[0], np.cumsum([u for u, _ in shares])])
+        for loc in range(per):
+            p, pend = loc * seg, min(loc * seg + seg, total)
+            if p >= pend:
+                continue
+            # the tile whose share holds p: exactly one tile with u > 0 qualifies
+            hits = [t for t in range(tiles) if shares[t][0] > 0 and starts[t] <= p < starts[t] + shares[t][0]]
+            assert len(hits) == 1
+            t = hits[0]
+            pbase, (ucur, st) = starts[t], shares[t]
+            while p < pend:
+                while p >= pbase + ucur:
+                    pbase += ucur
+                    t += 1
+                    ucur, st = shares[t]
+                off = p - pbase
+                n = min(ucur - off, pend - p, piece)
+                out.append((xcd, loc, t, xcd * st + off, n))
+                p += n
+    return out
+
+
+@pytest.mark.parametrize("tile,step,piece", [(128, 32, 2048), (64, 64, 1024)])
+@pytest.mark.parametrize("name", ["mixed", "three_reqs", "empty_tiles"])
+def test_balanced_split_covers_every_visible_key_once(name, tile, step, piece):
+    """Every visible logical key of every tile lies in exactly one piece, pieces
+    start on stage boundaries and stay within their tile's stage-padded stripe,
+    and no workgroup gets more than one stage above an even share."""
+    rng = np.random.default_rng(7)
+    if name == "mixed":
+        w = W.mixed()
+    elif name == "three_reqs":
+        w = W.build("three", rng, 7, [5000, 300, 70000], [100, 150, 90], permute_pages=True, k=256)
+    else:  # whole tiles of rows that see no key, between long ones
+        w = W.build("empty", rng, 7, [20000, 300, 9000], [200, 260, 70], permute_pages=True, k=256)
+        w.pos = w.pos.copy()
+        w.pos[200:460] = np.arange(260) % 3
+    tv = tile_counts(w, tile)
+    per = (256 // XCDS) * 2
+    for stride in (1, 16):
+        pieces = balanced_pieces(tv, stride, step, piece, per)
+        covered = {}
+        work = {}
+        for xcd, loc, t, c0, n in pieces:
+            assert c0 % step == 0 and 0 < n <= piece, (xcd, loc, t, c0, n)
+            lv = ceil_div(int(tv[t]), stride)
+            st = ceil_div(ceil_div(lv, XCDS), step) * step
+            assert xcd * st <= c0 and c0 + n <= (xcd + 1) * st, (xcd, t, c0, n, st)
+            for j in range(c0, min(c0 + n, lv)):
+                covered[(t, j)] = covered.get((t, j), 0) + 1
+            work[(xcd, loc)] = work.get((xcd, loc), 0) + n
+        for t in range(len(tv)):
+            lv = ceil_div(int(tv[t]), stride)
+            assert all(covered.get((t, j), 0) == 1 for j in range(lv)), (name, stride, t)
+        for xcd in range(XCDS):
+            loads = [n for (x, _), n in work.items() if x == xcd]
+            if loads:
+                mean = sum(loads) / per
+                assert max(loads) <= mean + 2 * step, (name, stride, xcd, max(loads), mean)

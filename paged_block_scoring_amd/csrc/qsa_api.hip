@@ -526,9 +526,9 @@ qsa_status run_select(const SelectCall& c, void* workspace, const DeviceInfo* de
     float* scores = static_cast<float*>(workspace);
     const int64_t ld = two_pass_ld(c.max_visible);
     HIP_CHECK(mark(s));
-    _Float16* qsum = a.relu ? nullptr
-                            : reinterpret_cast<_Float16*>(static_cast<unsigned char*>(workspace) +
-                                                          two_pass_scores_bytes(c.rows, c.max_visible));
+    // (head sums in the default form, tile counts in the relu form)
+    _Float16* qsum = reinterpret_cast<_Float16*>(static_cast<unsigned char*>(workspace) +
+                                                 two_pass_scores_bytes(c.rows, c.max_visible));
     if (c.max_visible > 0) HIP_CHECK(qsa::launch_score_paged(a, qsum, scores, ld, dev->cus, scorer_choice(), s));
     HIP_CHECK(mark(s));
     HIP_CHECK(qsa::launch_topk_rows(scores, ld, vs, c.rows, kb, expand, c.k, c.out, s));

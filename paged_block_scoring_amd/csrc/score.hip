@@ -113,7 +113,7 @@ static bool use_group_scorer(const PagedArgs& a, ScorerChoice choice) {
 hipError_t launch_score_paged(const PagedArgs& a, const _Float16* qsum, float* scores, int64_t ld, int32_t cus,
                               ScorerChoice choice, hipStream_t stream) {
     if (use_group_scorer(a, choice)) return launch_score_group(a, scores, ld, cus, stream);
-    if (qsum && !a.relu) {
+    if (qsum) {
         const hipError_t e = launch_qsum_prep(a, const_cast<_Float16*>(qsum), stream);
         if (e != hipSuccess) return e;
     }

@@ -201,9 +201,11 @@ def test_scorers_bit_identical(oracle_mod, name, flags):
         b = gpu_scores(d, w, flags)
     for r in range(w.rows):
         assert np.array_equal(a[r, :V[r]].view(np.uint32), b[r, :V[r]].view(np.uint32)), f"row {r}"
-    with force_scorer("groups"), force_path("two_pass"):
-        out = gpu_select(d, w, flags)
-    assert np.array_equal(out, expected_from_scores(oracle_mod, a, V, w.k, w.compress_ratio, flags))
+    exp = expected_from_scores(oracle_mod, a, V, w.k, w.compress_ratio, flags)
+    for scorer in ("groups", "tiles"):  # (the tiled scorer shares out each tile's own keys here)
+        with force_scorer(scorer), force_path("two_pass"):
+            out = gpu_select(d, w, flags)
+        assert np.array_equal(out, exp), scorer
 
 
 LARGE_Q = ["kernel_shape_80", "mixed_small", "decode_small", "three_reqs_40"]

@@ -329,6 +329,30 @@ def test_tiles_without_keys(oracle_mod, flags):
     full_parity(oracle_mod, w, flags, True, paths=PATHS)
 
 
+def test_stream_merge_beyond_registers(oracle_mod):
+    """Streaming arm: rows whose chunk lists exceed the merge's registers
+    (kb = 4,096 with QSA_OUT_KEYS and more than six 8,192-key chunks, so the
+    merge cuts the lists down in LDS), beside a row whose last chunk is
+    shorter than kb; integer inputs (many ties), compared with the oracle's
+    selector on the GPU's own scores, and end to end for one case."""
+    rng = np.random.default_rng(91)
+    # 100,000, 60,000 (two rows) and 8,250 visible keys
+    w = W.build("stream_long", rng, 91, [400_000, 240_000, 33_000], [1, 2, 1], permute_pages=True, integer=True,
+                k=4096)
+    d = to_dev(w)
+    V = visible(oracle_mod, w)
+    gs = gpu_scores(d, w, 0)
+    for flags, k in ((KEYS, 4096), (0, 4096), (KEYS, 1000)):
+        with force_path("stream"):
+            out = gpu_select(d, w, flags, k=k)
+        assert Q.qsa_last_path() == "stream"
+        assert np.array_equal(out, expected_from_scores(oracle_mod, gs, V, k, w.compress_ratio, flags)), (flags, k)
+    full = oracle_mod.select_paged_tokens(w.q, w.kcache, w.page_table, w.pos, w.compress_ratio, 4096,
+                                          row_req=w.row_req, flags=KEYS)
+    with force_path("stream"):
+        assert np.array_equal(gpu_select(d, w, KEYS, k=4096), full)
+
+
 @pytest.mark.parametrize("name,path", [("kernel_shape_80", "fused"), ("decode_small", "two_pass"),
                                        ("mixed_small", "fused_fallback"), ("decode_small", "stream")])
 def test_graph_capture(oracle_mod, name, path):

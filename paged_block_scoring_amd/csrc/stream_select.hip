@@ -68,16 +68,9 @@ struct ChunkArgs {
     int32_t* count;     // [rows][nchunk] entries of each list
 };
 
-// Exact top-nsel of register-resident keys: thread t holds k[e], element
-// e*NT + t with index idx(e); 0 marks an empty slot, slots e*NT >= nmax are
-// skipped, 1 <= nsel <= the nonempty keys.  One histogram level over the keys
-// (kSelBins bins between the smallest and largest) bounds the nsel-th
-// largest (and, if that bin is crowded, a second level inside it); the keys at
-// or above the bound are compacted into LDS and ranked by select_from_bound
-// (qsa_select.hpp), or, if more than kTopCompact survive (ties), the keys are
-// selected by select_exact_sorted.  emit(r, c) is
-// called once for each rank r < nsel.  Contains barriers.
-constexpr int kTopCompact = 4096;  // > the largest kb, so a cut at kb usually fits
+// Keys a register select compacts at most: twice the usual kb, so that a cut
+// at kb fits unless the keys crowd around it.
+constexpr int kTopCompact = 4096;
 
 template <int KBMAX>
 struct TopLds {
@@ -86,6 +79,15 @@ struct TopLds {
     int nc;
 };
 
+// Exact top-nsel of register-resident keys: thread t holds k[e], element
+// e*NT + t with index idx(e); 0 marks an empty slot, slots e*NT >= nmax are
+// skipped, 1 <= nsel <= the nonempty keys.  One histogram level over the keys
+// (kSelBins bins between the smallest and largest) bounds the nsel-th
+// largest (and, if that bin is crowded, a second level inside it); the keys at
+// or above the bound are compacted into LDS and ranked by select_from_bound
+// (qsa_select.hpp), or, if more than kTopCompact survive (ties), the keys are
+// selected by select_exact_sorted.  emit(r, c) is called once for each rank
+// r < nsel.  Contains barriers.
 template <int NT, int EPT, int KBMAX, class IdxF, class EmitF>
 __device__ __forceinline__ void select_top(const uint32_t (&k)[EPT], IdxF idx, int nmax, int nsel, TopLds<KBMAX>& L,
                                            EmitF emit) {

@@ -68,9 +68,9 @@ struct ChunkArgs {
     int32_t* count;     // [rows][nchunk] entries of each list
 };
 
-// Keys a register select compacts at most: twice the usual kb, so that a cut
-// at kb fits unless the keys crowd around it.
-constexpr int kTopCompact = 4096;
+// Keys a register select compacts at most: the largest kb (QSA_MAX_SELECT),
+// so that a cut at a smaller kb fits unless many keys crowd around it.
+constexpr int kTopCompact = QSA_MAX_SELECT;
 
 template <int KBMAX>
 struct TopLds {

@@ -522,11 +522,13 @@ class Run:
         relu = bool(self.flags & Q.QSA_SCORE_RELU)
         # the relu form's scorers are other kernels with their own profiles
         pname = dom + "_relu" if relu and dom in ("filter_scorer", "sample_scorer") else dom
+        # (summaries of a forced arm carry its name)
+        wname = self.name + ("_relu" if relu else "") + ("_stream" if path == "stream" else "")
         roof = {"kernel": dom, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4),
-                "traffic": traffic_for(pname, self.name + ("_relu" if relu else "")),
+                "traffic": traffic_for(pname, wname),
                 "ms_per_launch": round(kms[dom], 4)}
-        cnt = counters_for(pname, self.name + ("_relu" if relu else ""))
+        cnt = counters_for(pname, wname)
         if bound == "mfma":
             roof["algorithmic_flop_per_launch"] = work
             if cnt and cnt.get("executed_flop"):
@@ -732,6 +734,23 @@ def main():
             configs[name] = {k: r[k] for k in ("ms_per_step", "rows_per_s", "gkeys_per_s", "path", "rows",
                                                "sum_visible_keys", "kernels_ms", "roofline")}
             configs[name]["workload"] = WORKLOAD_TEXT[name]
+        # the decode batch through the streaming arm too (the dispatcher keeps
+        # the two-pass arm there; this arm keeps the scores on chip)
+        if "decode" in configs and not args.path:
+            run = runs["decode"]
+            ws_default = run.ws
+            Q.qsa_debug_force(Q.QSA_DEBUG_FORCE_STREAM)
+            try:
+                need = Q.qsa_select_paged_tokens_workspace_size(run.rows, run.w.num_reqs, run.max_v, run.cr, run.k,
+                                                                run.flags)
+                run.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=run.dev)
+                r = run.measure(args.config_steps, 2)
+            finally:
+                Q.qsa_debug_force(0)
+                run.ws = ws_default
+            run.step()  # (the parity check below reads the default arm's output)
+            torch.cuda.synchronize()
+            configs["decode"]["stream_arm"] = {k: r[k] for k in ("ms_per_step", "kernels_ms", "roofline", "path")}
         result["configs"] = configs
 
     if not args.no_cpu_baseline:

@@ -91,6 +91,11 @@ typedef enum qsa_status {
 #define QSA_SCORE_RELU 0x1u  /* [spec] form: sum_h relu(q_h . k) times the fp32 value nearest 1/sqrt(head_dim);
                                 default is the plain sum_h q_h . k */
 #define QSA_OUT_KEYS   0x2u  /* k counts keys and the output holds key indices (no expansion to tokens) */
+#define QSA_STREAM_SELECT 0x8u /* qsa_select_paged_tokens: take the streaming arm -- each range of 8,192 keys
+                                  reduced to its top-k on chip, then a merge per row -- in place of the
+                                  library's choice.  Measured faster for batches of one row per request whose
+                                  rows are all long (64k+ tokens, 256+ rows); slower with short or few rows.
+                                  The workspace query must be given the same flag. */
 
 /* Largest number of selected entries per row (blocks, or keys with
  * QSA_OUT_KEYS) that the selector supports. */
@@ -167,14 +172,14 @@ size_t qsa_topk_rows_workspace_size(int32_t rows, int32_t max_visible, int32_t k
  *               multiple of compress_ratio and k/cr blocks are selected
  *               (1 <= k/cr <= QSA_MAX_SELECT).  With QSA_OUT_KEYS: keys,
  *               1 <= k <= QSA_MAX_SELECT.
- *  flags        QSA_SCORE_RELU and/or QSA_OUT_KEYS.
+ *  flags        QSA_SCORE_RELU, QSA_OUT_KEYS and/or QSA_STREAM_SELECT.
  *  out          device int32 [rows][k]: rank-ordered blocks, each expanded to
  *               tokens cr*j .. cr*j+cr-1 ascending (or key j with
  *               QSA_OUT_KEYS); -1 after the min(k/cr, V_r) selected blocks.
  *  workspace    device scratch of at least
  *               qsa_select_paged_tokens_workspace_size(...) bytes, queried
- *               under the same debug-force mask as the call (the arms'
- *               workspaces differ in size).
+ *               with the same flags and under the same debug-force mask as
+ *               the call (the arms' workspaces differ in size).
  */
 qsa_status qsa_select_paged_tokens(const void* q, const void* kcache, const int32_t* page_table,
                                    int64_t pt_stride, int32_t num_pages, int32_t num_reqs,

@@ -201,17 +201,17 @@ enum class Path { TwoPass, Fused, Stream };
 // there is enough work to cover its five launches (measured crossover: rows x
 // longest row between 4.2 M and 6.6 M keys).  Few rows per request (decode),
 // and small batches, take the two-pass arm.  The streaming arm (chunk top-k
-// on chip, then a merge) is taken only when forced: on decode batches it
-// measured level with the two-pass arm at 256 rows of 16 k..46 k keys and
-// slower with fewer rows or shorter rows, where its coarser chunks leave a
-// longer tail.
+// on chip, then a merge) is taken when the caller asks for it
+// (QSA_STREAM_SELECT) or a test forces it: it measured faster on decode
+// batches whose rows are all long and slower once short rows join, which the
+// row count and the longest row do not tell apart.
 constexpr int64_t kFusedMinWork = 5000000;
 
-Path choose_path(int32_t rows, int32_t num_reqs, int32_t max_visible) {
+Path choose_path(int32_t rows, int32_t num_reqs, int32_t max_visible, uint32_t flags) {
     const uint32_t f = g_force.load(std::memory_order_relaxed);
     if (f & QSA_DEBUG_FORCE_TWO_PASS) return Path::TwoPass;
     if (f & (QSA_DEBUG_FORCE_FUSED | QSA_DEBUG_FORCE_FALLBACK | QSA_DEBUG_FORCE_REDO)) return Path::Fused;
-    if (f & QSA_DEBUG_FORCE_STREAM) return Path::Stream;
+    if ((f & QSA_DEBUG_FORCE_STREAM) || (flags & QSA_STREAM_SELECT)) return Path::Stream;
     if (max_visible <= 0) return Path::TwoPass;
     if (rows / (num_reqs > 0 ? num_reqs : 1) < 32) return Path::TwoPass;
     return (int64_t)rows * max_visible >= kFusedMinWork ? Path::Fused : Path::TwoPass;
@@ -423,7 +423,7 @@ QSA_EXPORT size_t qsa_select_paged_tokens_workspace_size(int32_t rows, int32_t n
     if (rows <= 0 || max_visible <= 0 || k < 1 || compress_ratio < 1) return 0;
     const int32_t kb = (flags & QSA_OUT_KEYS) ? k : k / compress_ratio;
     if (kb < 1) return 0;
-    const Path p = choose_path(rows, num_reqs, max_visible);
+    const Path p = choose_path(rows, num_reqs, max_visible, flags);
     if (p == Path::Stream) return qsa::stream_bytes(rows, max_visible, kb);
     if (p == Path::Fused) return fused_layout(rows, max_visible, kb).total;
     return two_pass_bytes(rows, max_visible);
@@ -457,8 +457,8 @@ qsa_status check_select(const SelectCall& c, size_t* need) {
     qsa_status st = check_paged(c.q, c.kcache, c.page_table, c.pt_stride, c.num_pages, c.num_reqs, c.pos, c.rows,
                                 c.heads, c.head_dim, c.page_size, c.compress_ratio, c.max_visible);
     if (st != QSA_OK) return st;
-    REQUIRE((c.flags & ~(QSA_SCORE_RELU | QSA_OUT_KEYS)) == 0, QSA_ERR_INVALID_ARGUMENT, "unknown flags 0x%x",
-            c.flags);
+    REQUIRE((c.flags & ~(QSA_SCORE_RELU | QSA_OUT_KEYS | QSA_STREAM_SELECT)) == 0, QSA_ERR_INVALID_ARGUMENT,
+            "unknown flags 0x%x", c.flags);
     REQUIRE(c.k >= 1, QSA_ERR_INVALID_ARGUMENT, "k must be >= 1 (got %d)", c.k);
     const bool out_keys = (c.flags & QSA_OUT_KEYS) != 0;
     REQUIRE(out_keys || c.k % c.compress_ratio == 0, QSA_ERR_INVALID_ARGUMENT,
@@ -486,7 +486,7 @@ qsa_status run_select(const SelectCall& c, void* workspace, const DeviceInfo* de
     vs.cr = c.compress_ratio;
     vs.max_visible = c.max_visible;
     const int32_t expand = out_keys ? 1 : c.compress_ratio;
-    const Path path = choose_path(c.rows, c.num_reqs, c.max_visible);
+    const Path path = choose_path(c.rows, c.num_reqs, c.max_visible, c.flags);
     if (path == Path::Stream) {
         HIP_CHECK(mark(s));
         HIP_CHECK(qsa::launch_stream_select(a, kb, expand, c.k, c.out, workspace, s, mark));

@@ -26,6 +26,7 @@ QSA_ERR_DEVICE = 4
 
 QSA_SCORE_RELU = 0x1
 QSA_OUT_KEYS = 0x2
+QSA_STREAM_SELECT = 0x8
 QSA_ROPE_INTERLEAVED = 0x4
 QSA_MAX_SELECT = 4096
 

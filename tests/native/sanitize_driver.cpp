@@ -182,7 +182,7 @@ static void abi_checks() {
         {"num_reqs", [](Sel& s) { s.num_reqs = 0; }, QSA_ERR_INVALID_ARGUMENT},
         {"rows", [](Sel& s) { s.rows = -1; }, QSA_ERR_INVALID_ARGUMENT},
         {"max_visible", [](Sel& s) { s.max_visible = -1; }, QSA_ERR_INVALID_ARGUMENT},
-        {"flags", [](Sel& s) { s.flags = 0x8; }, QSA_ERR_INVALID_ARGUMENT},
+        {"flags", [](Sel& s) { s.flags = 0x10; }, QSA_ERR_INVALID_ARGUMENT},
         {"misaligned q", [](Sel& s) { s.q = fp(4); }, QSA_ERR_INVALID_ARGUMENT},
     };
     for (const Case& c : cases) {

@@ -111,7 +111,7 @@ def topk(**over):
     (dict(num_reqs=0), Q.QSA_ERR_INVALID_ARGUMENT),
     (dict(rows=-1), Q.QSA_ERR_INVALID_ARGUMENT),
     (dict(max_visible=-1), Q.QSA_ERR_INVALID_ARGUMENT),
-    (dict(flags=0x8), Q.QSA_ERR_INVALID_ARGUMENT),
+    (dict(flags=0x10), Q.QSA_ERR_INVALID_ARGUMENT),
     (dict(q=FAKE + 4), Q.QSA_ERR_INVALID_ARGUMENT),           # misaligned
 ])
 def test_select_rejects_before_device(over, code):
@@ -229,6 +229,14 @@ def test_debug_force_rejects_bad_masks():
     finally:
         Q.qsa_debug_force(0)
     assert stream == 256 * 6 * 512 * 8 + 256 * 6 * 4
+    # the caller's flag asks for the same arm, and the workspace follows it
+    assert Q.qsa_select_paged_tokens_workspace_size(256, 256, 46000, 4, 2048, Q.QSA_STREAM_SELECT) == stream
+    Q.qsa_debug_force(Q.QSA_DEBUG_FORCE_TWO_PASS)
+    try:  # a forced arm overrides the flag
+        assert (Q.qsa_select_paged_tokens_workspace_size(256, 256, 46000, 4, 2048, Q.QSA_STREAM_SELECT)
+                == Q.qsa_select_paged_tokens_workspace_size(256, 256, 46000, 4, 2048))
+    finally:
+        Q.qsa_debug_force(0)
 
 
 def attend(**over):

@@ -329,6 +329,23 @@ def test_tiles_without_keys(oracle_mod, flags):
     full_parity(oracle_mod, w, flags, True, paths=PATHS)
 
 
+@pytest.mark.parametrize("flags", [0, RELU, KEYS])
+@pytest.mark.parametrize("name", ["decode_small", "kernel_shape_80", "mixed_small"])
+def test_stream_select_flag(oracle_mod, name, flags):
+    """QSA_STREAM_SELECT (the caller's request for the streaming arm) takes
+    that arm and returns the default arm's selection; a forced arm still wins."""
+    w = REDUCED[name](False)
+    d = to_dev(w)
+    base = gpu_select(d, w, flags)
+    out = gpu_select(d, w, flags | Q.QSA_STREAM_SELECT)
+    assert Q.qsa_last_path() == "stream"
+    assert np.array_equal(out, base)
+    with force_path("two_pass"):
+        again = gpu_select(d, w, flags | Q.QSA_STREAM_SELECT)
+        assert Q.qsa_last_path() == "two_pass"
+    assert np.array_equal(again, base)
+
+
 def test_stream_merge_beyond_registers(oracle_mod):
     """Streaming arm: rows whose chunk lists exceed the merge's registers
     (kb = 4,096 with QSA_OUT_KEYS and more than six 8,192-key chunks, so the

@@ -94,8 +94,9 @@ typedef enum qsa_status {
 #define QSA_STREAM_SELECT 0x8u /* qsa_select_paged_tokens: take the streaming arm -- each range of 8,192 keys
                                   reduced to its top-k on chip, then a merge per row -- in place of the
                                   library's choice.  Measured faster for batches of one row per request whose
-                                  rows are all long (64k+ tokens, 256+ rows); slower with short or few rows.
-                                  The workspace query must be given the same flag. */
+                                  rows are all long (64k+ tokens) and number 320 or more (about level at
+                                  256); slower with short or few rows.  The workspace query must be given the
+                                  same flag. */
 
 /* Largest number of selected entries per row (blocks, or keys with
  * QSA_OUT_KEYS) that the selector supports. */

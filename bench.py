@@ -524,6 +524,10 @@ class Run:
         pname = dom + "_relu" if relu and dom in ("filter_scorer", "sample_scorer") else dom
         # (summaries of a forced arm carry its name)
         wname = self.name + ("_relu" if relu else "") + ("_stream" if path == "stream" else "")
+        # (the two-pass arm's top-k interval holds the register kernel for rows
+        # of up to 49,152 keys, whose summaries carry that kernel's name)
+        if dom == "topk_rows" and traffic_for(pname, wname) is None:
+            pname = "topk_regs"
         roof = {"kernel": dom, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4),
                 "traffic": traffic_for(pname, wname),

@@ -233,35 +233,41 @@ __global__ __launch_bounds__(kGroupNT, 2) void score_group_kernel(GroupArgs A) {
                 wbase += kbuf;
             }
         };
-        // Tile t+1 is in flight while tile t is scored; a tile's scores are
-        // buffered (and possibly flushed) before the next loads are issued,
+        // Tile t+1 (and t+2 in the relu form) is in flight while tile t is
+        // scored; a tile's scores are buffered (and possibly flushed) before
+        // the next loads are issued,
         // so that no wait for a tile can drain the loads behind it.  The loop
         // has a single exit so that the waits are the same on every path.
         // Tiles past the segment load its last key.
-        half8 b0[kSlices], b1[kSlices];
-        load_tile(k0, b0);
-        __builtin_amdgcn_sched_barrier(0);
-        load_tile(k0 + 32, b1);
-        __builtin_amdgcn_sched_barrier(0);
-        int j0 = k0;
-        for (; j0 + 32 < k1; j0 += 64) {
-            float16v acc = chain(b0);
-            __builtin_amdgcn_sched_barrier(0);
-            store(j0, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            load_tile(j0 + 64, b0);
-            __builtin_amdgcn_sched_barrier(0);
-            acc = chain(b1);
-            __builtin_amdgcn_sched_barrier(0);
-            store(j0 + 32, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            load_tile(j0 + 96, b1);
+        // (the relu form keeps two tiles in flight: it runs at two waves per
+        // SIMD with three buffers as at three with two, and streams faster)
+        constexpr int NB = RELU ? 3 : 2;
+        half8 b[NB][kSlices];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            load_tile(k0 + 32 * i, b[i]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (j0 < k1) {
-            const float16v acc = chain(b0);
-            store(j0, acc);
-            j0 += 32;
+        int j0 = k0;
+        for (; j0 + 32 * (NB - 1) < k1; j0 += 32 * NB) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const float16v acc = chain(b[i]);
+                __builtin_amdgcn_sched_barrier(0);
+                store(j0 + 32 * i, acc);
+                __builtin_amdgcn_sched_barrier(0);
+                load_tile(j0 + 32 * (NB + i), b[i]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // the last tiles (fewer than NB), already loaded in order
+#pragma unroll
+        for (int i = 0; i < NB - 1; ++i) {
+            if (j0 < k1) {
+                const float16v acc = chain(b[i]);
+                store(j0, acc);
+                j0 += 32;
+            }
         }
         if (j0 != wbase) flush(wbase);
     }

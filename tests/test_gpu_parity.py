@@ -455,8 +455,10 @@ def run_topk(scores_np, V, k, max_visible=None):
 
 def test_topk_rows_random_with_ties(oracle_mod):
     rng = np.random.default_rng(51)
+    # (also 512-key rows with k above V, one-key rows, and k = 1)
     for trial, (rows, ld, k) in enumerate([(37, 300, 17), (16, 5000, 512), (9, 20_000, 2048),
-                                           (5, 9000, Q.QSA_MAX_SELECT), (64, 70, 64)]):
+                                           (5, 9000, Q.QSA_MAX_SELECT), (64, 70, 64), (48, 512, 600),
+                                           (7, 1, 3), (40, 512, 1)]):
         kind = trial % 3
         if kind == 0:
             sc = rng.integers(-3, 4, size=(rows, ld)).astype(np.float32)
